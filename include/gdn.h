@@ -1,0 +1,125 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) chunked gated delta rule prefill scan.
+ *
+ * The operation ("flashinfer.gdn_prefill": chunk_gated_delta_rule is the
+ * chunked GDN scan that builds the recurrent state from a whole prompt before
+ * decoding takes over; "flashinfer.cudnn.cudnn_chunk_gated_delta_rule" gives
+ * its arguments).  Per token t of a sequence and per value head h:
+ *
+ *     S_t = a_t * S_{t-1} * (I - b_t k_t k_t^T) + b_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * S is the [V = 128, K = 128] state, stored V-major (S[v][k]) as on the
+ * "flashinfer.cudnn" page, section "Linear attention".  a_t is the forget
+ * gate in linear space (Parameters: g), b_t the post-sigmoid update gate
+ * (Parameters: beta).  Value head h reads query/key head h / (Hv / Hqk).
+ *
+ * Everything here is plain C: device pointers, element sizes and element
+ * strides.  No caller pointer is kept after a call returns.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of a gdn_tensor. */
+enum gdn_dtype {
+    GDN_F32 = 0,
+    GDN_BF16 = 1,
+    GDN_F16 = 2,
+    GDN_I32 = 3,
+    GDN_I64 = 4
+};
+
+/* Return codes.  A non-zero code means nothing was enqueued and nothing was
+ * written; gdn_last_error() then describes the reason. */
+enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1, /* NULL required tensor, bad ndim/shape/stride/dtype */
+    GDN_ERR_UNSUPPORTED = 2,      /* head_dim != 128, head relation, dtype combination */
+    GDN_ERR_ALIAS = 3,            /* output_state->data == initial_state->data */
+    GDN_ERR_NO_DEVICE = 4,        /* no HIP device visible */
+    GDN_ERR_ARCH = 5,             /* current device is not gfx950 */
+    GDN_ERR_HIP = 6               /* a HIP runtime call failed (launch, allocation) */
+};
+
+/* A strided view of device memory.  sizes/strides are in elements; entries
+ * beyond ndim are ignored.  The innermost dimension must have stride 1. */
+typedef struct gdn_tensor {
+    void *data;
+    int32_t dtype;      /* enum gdn_dtype */
+    int32_t ndim;
+    int64_t sizes[4];
+    int64_t strides[4];
+} gdn_tensor;
+
+/*
+ * gdn_chunk_prefill - runs the scan over a packed varlen batch.
+ *
+ * Argument meanings follow "flashinfer.cudnn.cudnn_chunk_gated_delta_rule",
+ * Parameters (T = total tokens, N = sequences, d = 128):
+ *   q, k            [T, Hqk, 128], F32 or BF16 (both the same); any
+ *                   non-negative token/head strides, innermost contiguous.
+ *   v               [T, Hv, 128], q's dtype, same stride rule; Hv % Hqk == 0.
+ *   g               NULL (all ones) or [T, Hv] forget gate in linear space,
+ *                   F32, BF16 or F16, innermost stride 1 not required.
+ *                   Values in [0, 1]; a zero gate resets the state (the
+ *                   kernels clamp ln(a) at -80).
+ *   beta            NULL (all ones) or [T, Hv] post-sigmoid gate, F32 or q's
+ *                   dtype.
+ *   scale           query scale; exactly 0.0 means 1/sqrt(128); must be finite.
+ *   cu_seqlens      [N + 1] I32 or I64 in device memory, contiguous; required.
+ *                   cu[0] = 0, non-decreasing, cu[N] = T.  These contents are
+ *                   an unchecked precondition (they are never read on the
+ *                   host); empty sequences are allowed.
+ *   initial_state   NULL (zero state) or [N, Hv, 128, 128] F32 or BF16,
+ *                   V-major, innermost (K) stride 1, other strides free.
+ *   output_state    NULL (no state written at all) or the same shape, F32 or
+ *                   BF16 (each state buffer carries its own dtype; the scan
+ *                   accumulates in fp32).  Must not overlap initial_state:
+ *                   equal data pointers are rejected with GDN_ERR_ALIAS;
+ *                   partial overlap is an unchecked precondition.  An empty
+ *                   sequence copies its initial state (or zeros) here.
+ *   use_qk_l2norm   non-zero: q and k rows are scaled by 1/sqrt(sum x^2 + 1e-6)
+ *                   inside the kernel before use.
+ *   batch_invariant non-zero: every sequence is scanned by one work item per
+ *                   head in a fixed order, so its output and final state are
+ *                   bitwise independent of the rest of the batch.  Zero
+ *                   allows splitting one long sequence across work items
+ *                   (segment scan, then a state fix-up), which may change the
+ *                   last bits.
+ *   out             [T, Hv, 128], q's dtype, written in place (the library
+ *                   allocates no output).
+ *   stream          a hipStream_t (NULL = the default stream).  The call is
+ *                   asynchronous: it validates on the host, enqueues on
+ *                   `stream` and returns without synchronising.
+ *
+ * Ownership: every tensor is caller-owned device memory; the library writes
+ * only `out`, `output_state` and its own workspace (cached per device and
+ * stream, grown on demand; see gdn_release_workspace).
+ * Errors: validation happens before any enqueue; an invalid call writes
+ * nothing and returns a gdn_status (no fallback path exists).
+ */
+int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                      const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                      const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                      const gdn_tensor *output_state, int use_qk_l2norm,
+                      int batch_invariant, const gdn_tensor *out, void *stream);
+
+/* Message for the last non-zero return of a gdn_* call on this thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char *gdn_last_error(void);
+
+/* Frees every cached workspace (all devices and streams).  The caller must
+ * ensure no enqueued gdn work is still running. */
+void gdn_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gdn.h declares, and rejects bad arguments before touching a device
+(descriptors carry fake, never-dereferenced pointers)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import chunked_gated_delta_prefill_amd as lib
+from chunked_gated_delta_prefill_amd import (GDN_BF16, GDN_F16, GDN_F32, GDN_I32, GDN_I64,
+                                             make_tensor)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced
+OK, INVALID, UNSUPPORTED, ALIAS, NO_DEVICE, ARCH, HIPERR = range(7)
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = _declared_functions()
+    assert names == ["gdn_chunk_prefill", "gdn_last_error", "gdn_release_workspace"]
+    L = lib.load()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _contig(sizes):
+    st, acc = [], 1
+    for s in reversed(sizes):
+        st.append(acc)
+        acc *= s
+    return list(reversed(st))
+
+
+def _t(sizes, dt=GDN_BF16, ptr=FAKE, strides=None):
+    return make_tensor(ptr, dt, sizes, strides or _contig(sizes))
+
+
+def _args(T=100, N=2, Hqk=2, Hv=4, dt=GDN_BF16, **over):
+    a = dict(q=_t([T, Hqk, 128], dt), k=_t([T, Hqk, 128], dt), v=_t([T, Hv, 128], dt),
+             g=_t([T, Hv], GDN_F32), beta=_t([T, Hv], GDN_F32), scale=0.0,
+             cu=_t([N + 1], GDN_I32), s0=_t([N, Hv, 128, 128], GDN_F32, FAKE + (1 << 30)),
+             s1=_t([N, Hv, 128, 128], GDN_F32, FAKE + (1 << 31)), l2=1, bi=1,
+             out=_t([T, Hv, 128], dt, FAKE + (1 << 32)))
+    a.update(over)
+    return a
+
+
+def _call(a):
+    return lib.call_raw(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["cu"], a["s0"],
+                        a["s1"], a["l2"], a["bi"], a["out"], None)
+
+
+CASES = {
+    "q_missing": (dict(q=None), INVALID),
+    "out_missing": (dict(out=None), INVALID),
+    "cu_missing": (dict(cu=None), INVALID),
+    "q_ndim": (dict(q=_t([100, 256], GDN_BF16)), INVALID),
+    "head_dim_64": (dict(q=_t([100, 2, 64]), k=_t([100, 2, 64])), UNSUPPORTED),
+    "head_ratio": (dict(v=_t([100, 3, 128]), out=_t([100, 3, 128]), g=_t([100, 3], GDN_F32),
+                        beta=_t([100, 3], GDN_F32), s0=None, s1=None), UNSUPPORTED),
+    "f16_inputs": (dict(q=_t([100, 2, 128], GDN_F16), k=_t([100, 2, 128], GDN_F16),
+                        v=_t([100, 4, 128], GDN_F16), out=_t([100, 4, 128], GDN_F16)), UNSUPPORTED),
+    "k_dtype": (dict(k=_t([100, 2, 128], GDN_F32)), INVALID),
+    "k_shape": (dict(k=_t([99, 2, 128])), INVALID),
+    "inner_stride": (dict(q=_t([100, 2, 128], strides=[512, 256, 2])), INVALID),
+    "negative_stride": (dict(v=_t([100, 4, 128], strides=[-512, 128, 1])), INVALID),
+    "alias": (dict(s1=_t([2, 4, 128, 128], GDN_F32, FAKE + (1 << 30))), ALIAS),
+    "g_shape": (dict(g=_t([100, 2], GDN_F32)), INVALID),
+    "g_dtype": (dict(g=_t([100, 4], GDN_I32)), INVALID),
+    "beta_dtype": (dict(beta=_t([100, 4], GDN_F16)), INVALID),
+    "cu_dtype": (dict(cu=_t([3], GDN_F32)), INVALID),
+    "cu_strided": (dict(cu=_t([3], GDN_I64, strides=[2])), INVALID),
+    "state_shape": (dict(s0=_t([3, 4, 128, 128], GDN_F32)), INVALID),
+    "state_dtype": (dict(s1=_t([2, 4, 128, 128], GDN_F16, FAKE + (1 << 31))), INVALID),
+    "scale_nan": (dict(scale=math.nan), INVALID),
+    "misaligned_q": (dict(q=_t([100, 2, 128], ptr=FAKE + 2)), UNSUPPORTED),
+    "misaligned_stride": (dict(q=_t([100, 2, 128], strides=[260, 130, 1]),
+                               k=_t([100, 2, 128], strides=[260, 130, 1])), UNSUPPORTED),
+    "null_data": (dict(v=_t([100, 4, 128], ptr=None)), INVALID),
+    "out_dtype": (dict(out=_t([100, 4, 128], GDN_F32)), INVALID),
+    "bad_dtype_code": (dict(g=_t([100, 4], 17)), INVALID),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_rejected_before_any_device_access(name):
+    over, code = CASES[name]
+    rc, msg = _call(_args(**over))
+    assert rc == code, (rc, msg)
+    assert msg, "a failed call must leave a message"
+
+
+def test_fp32_inputs_and_bf16_state_validate():
+    a = _args(dt=GDN_F32, beta=_t([100, 4], GDN_F32), s0=_t([2, 4, 128, 128], GDN_BF16, FAKE + (1 << 30)))
+    if _has_gpu():
+        pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
+    rc, msg = _call(a)
+    assert rc == NO_DEVICE, (rc, msg)
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    if _has_gpu():
+        pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
+    rc, msg = _call(_args())
+    assert rc == NO_DEVICE and "device" in msg
+
+
+def test_optional_arguments_may_be_null():
+    if _has_gpu():
+        pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
+    rc, _ = _call(_args(g=None, beta=None, s0=None, s1=None))
+    assert rc == NO_DEVICE
+
+
+def test_release_workspace_without_gpu():
+    lib.load().gdn_release_workspace()

@@ -1,0 +1,91 @@
+"""GPU parity: the HIP scan against the CPU oracle on seeded workloads.
+
+Tolerances (max normalised error over each tensor): 1e-4 for fp32 inputs,
+2e-2 for bf16 inputs; out and final state are checked separately.
+Full-size workloads are checked on sampled (sequence, head) items that the
+oracle computes one by one, from the same device-resident run.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_workloads as W
+from _harness import BF16_TOL, F32_TOL, check, nerr, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("variant", [None, "raw_l2"])
+@pytest.mark.parametrize("bi", [True, False])
+def test_tiny_fp32(gdn, variant, bi):
+    check(gdn, W.make(0, variant=variant), F32_TOL, bi)
+
+
+@pytest.mark.parametrize("variant", [None, "gates_bf16", "long_memory"])
+def test_varlen_bf16(gdn, variant):
+    check(gdn, W.make(1, variant=variant), BF16_TOL, True)
+
+
+def test_many_short_bf16_state(gdn):
+    w = W.make(3)
+    out, fin = check(gdn, w, BF16_TOL, True)
+    # empty sequences pass the (bf16) initial state through bitwise
+    for n in (0, 127, 255):
+        assert torch.equal(fin[n].cpu(), w.initial_state[n])
+
+
+def _sampled(gdn, w, items, bi):
+    say(f"[gpu] {w.name}: T={w.T} N={w.N} batch_invariant={bi} (sampled {items})")
+    out, fin = run_gpu(gdn, w, bi)
+    cu = w.cu_seqlens.cpu().to(torch.int64)
+    worst = 0.0
+    for n, heads in items:
+        sub = W.slice_item(w, n, heads)
+        ro, rf = run_oracle(sub)
+        bos, eos = int(cu[n]), int(cu[n + 1])
+        e1 = nerr(out[bos:eos][:, heads], ro)
+        e2 = nerr(fin[n][heads], rf[0])
+        say(f"      n={n} heads={heads}: out {e1:.3e} state {e2:.3e}")
+        worst = max(worst, e1, e2)
+    assert worst <= BF16_TOL
+
+
+@pytest.mark.parametrize("bi", [True, False])
+def test_long_single_sampled(gdn, bi):
+    w = W.make(2, device="cuda")
+    _sampled(gdn, w, [(0, [0, 1, 17, 31])], bi)
+
+
+@pytest.mark.parametrize("bi", [True, False])
+def test_large_batch_sampled(gdn, bi):
+    w = W.make(4, device="cuda")
+    _sampled(gdn, w, [(0, [0, 1]), (17, [12, 30]), (31, [31])], bi)
+
+
+@pytest.mark.parametrize("lengths", [[1], [63], [64], [65], [1, 127, 128, 129, 0, 200]])
+def test_ragged_lengths(gdn, lengths):
+    w = W.build(lengths, 2, 4, torch.bfloat16, seed=7, gate="long", name=f"ragged{lengths}")
+    check(gdn, w, BF16_TOL, True)
+
+
+def test_ragged_lengths_fp32(gdn):
+    w = W.build([1, 63, 64, 65, 130], 2, 2, torch.float32, seed=8, gate="long", name="ragged_fp32")
+    check(gdn, w, F32_TOL, True)
+
+
+@pytest.mark.parametrize("r", [1, 4])
+def test_head_ratios(gdn, r):
+    w = W.build([100, 37], 4, 4 * r, torch.bfloat16, seed=9, name=f"ratio{r}")
+    check(gdn, w, BF16_TOL, True)
+
+
+def test_no_states(gdn):
+    w = W.build([70, 5], 2, 4, torch.bfloat16, seed=10, state_in=None, state_out=None, name="nostate")
+    check(gdn, w, BF16_TOL, True)
+
+
+def test_all_empty_batch(gdn):
+    w = W.build([0, 0, 0], 2, 4, torch.bfloat16, seed=11, name="all_empty")
+    out, fin = run_gpu(gdn, w, True)
+    assert out.shape[0] == 0
+    assert torch.equal(fin.cpu(), w.initial_state)
