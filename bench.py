@@ -1,0 +1,265 @@
+"""Benchmark of the chunked gated delta rule prefill scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large_batch]
+
+One step = one gdn_chunk_prefill call over the whole synthetic batch (inputs
+already resident in HBM).  Prints one JSON line with the throughput
+(tokens/s), the roofline of the dominant kernel and the CPU oracle baseline.
+
+Default workload: 32 sequences x 8192 tokens, Hqk = 16, Hv = 32, d = 128, bf16
+q/k/v/out, fp32 gates and state, in-kernel L2 norm, batch_invariant off.
+
+Algorithmic work (chunk length 64, whatever the kernels use internally):
+  flop/token  = Hv (6 d^2 + 3 C d) + Hqk (2 C d)           (MFMA work)
+  bytes/token = q, k (2 Hqk d 2B) + v, out (2 Hv d 2B) + g, beta (2 Hv 4B)
+  bytes/seq   = initial + final state (2 Hv d^2 4B)
+
+Other modes (used to produce the committed rocprofv3 summaries):
+  --copy-calibration   a plain device copy of known size (for PMC scaling)
+  --summarize-pmc DIR  turn rocprofv3 --pmc outputs into profiles/*.txt
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+D, C = 128, 64
+KERNEL = "fused_scan_kernel"
+KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_prefill_amd", "csrc", "gdn_scan.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_scan_large_batch.txt")
+
+
+def algorithmic(w):
+    """(MFMA flops, HBM bytes) the method itself needs for workload w."""
+    import torch
+    T, N, Hqk, Hv = w.T, w.N, w.Hqk, w.Hv
+    io = w.q.element_size()
+    esz = lambda t: 0 if t is None else t.element_size()
+    flops = T * (Hv * (6 * D * D + 3 * C * D) + Hqk * (2 * C * D))
+    byts = T * (2 * Hqk * D * io + 2 * Hv * D * io + Hv * (esz(w.g) + esz(w.beta)))
+    s_out = 0 if w.state_dtype is None else torch.empty(0, dtype=w.state_dtype).element_size()
+    byts += N * Hv * D * D * (esz(w.initial_state) + s_out)
+    return flops, byts
+
+
+def kernel_source_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch measured by rocprofv3 PMC runs, if they were taken
+    on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, max_seqs):
+    """The oracle (fp64 C recurrence, all host cores) on the first sequences."""
+    import gdn_workloads as W
+    import oracle
+    import torch
+    lens = w.lengths()
+    take = min(max_seqs, w.N)
+    cu = w.cu_seqlens.cpu().to(torch.int64)
+    end = int(cu[take])
+    sub = W.Workload("sample", w.q[:end].cpu(), w.k[:end].cpu(), w.v[:end].cpu(),
+                     None if w.g is None else w.g[:end].cpu(),
+                     None if w.beta is None else w.beta[:end].cpu(), cu[:take + 1].clone(),
+                     None if w.initial_state is None else w.initial_state[:take].cpu(),
+                     w.state_dtype, w.use_qk_l2norm, w.scale)
+    threads = oracle.default_threads()
+    oracle.run(sub.q[:1], sub.k[:1], sub.v[:1], None, None, 0.0, [0, 1], None, False, nthreads=1)  # load
+    t = time.perf_counter()
+    oracle.run(sub.q, sub.k, sub.v, sub.g, sub.beta, sub.scale, sub.cu_seqlens, sub.initial_state,
+               sub.use_qk_l2norm, nthreads=threads)
+    dt = time.perf_counter() - t
+    return {"value": end / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {take} of {w.N} sequences ({end} tokens, all {w.Hv} v-heads), fp64 oracle, "
+                      f"{dt:.1f} s wall"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}))
+
+
+def _pmc_rows(d):
+    import csv
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, name_part, counter):
+    vals = {}
+    for r in rows:
+        if name_part in r.get("Kernel_Name", "") and r.get("Counter_Name") == counter:
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes):
+    """Reads four rocprofv3 --pmc output dirs (kernel FETCH_SIZE, WRITE_SIZE;
+    copy FETCH_SIZE, WRITE_SIZE) and writes the traffic summary file."""
+    kf = _per_dispatch(_pmc_rows(os.path.join(base, "pmc_fetch")), KERNEL, "FETCH_SIZE")
+    kw = _per_dispatch(_pmc_rows(os.path.join(base, "pmc_write")), KERNEL, "WRITE_SIZE")
+    cf = _per_dispatch(_pmc_rows(os.path.join(base, "pmc_copy_fetch")), "", "FETCH_SIZE")
+    cw = _per_dispatch(_pmc_rows(os.path.join(base, "pmc_copy_write")), "", "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    # counters are KiB per dispatch; the copy reads and writes copy_bytes once
+    f_fac = copy_bytes / (max(cf) * 1024.0)
+    w_fac = copy_bytes / (max(cw) * 1024.0)
+    fetch = statistics.median(kf) * 1024.0 * f_fac
+    write = statistics.median(kw) * 1024.0 * w_fac
+    lines = [
+        "# HBM traffic of fused_scan_kernel, large_batch workload (32 x 8192 tokens, Hqk 16, Hv 32, bf16)",
+        "# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by the same counters",
+        "# read for a plain 1 GiB device copy (bench.py --copy-calibration).",
+        f"# kernel FETCH_SIZE command: {cmd_fetch}",
+        f"# kernel WRITE_SIZE command: {cmd_write}",
+        f"# copy FETCH_SIZE command:   {cmd_cf}",
+        f"# copy WRITE_SIZE command:   {cmd_cw}",
+        f"kernel_source_sha = {kernel_source_sha()}",
+        f"dispatches_fetch = {len(kf)}",
+        f"dispatches_write = {len(kw)}",
+        f"raw_fetch_kib_median = {statistics.median(kf):.1f}",
+        f"raw_write_kib_median = {statistics.median(kw):.1f}",
+        f"copy_fetch_kib = {max(cf):.1f}",
+        f"copy_write_kib = {max(cw):.1f}",
+        f"fetch_scale = {f_fac:.4f}",
+        f"write_scale = {w_fac:.4f}",
+        f"fetch_bytes_per_launch = {fetch:.0f}",
+        f"write_bytes_per_launch = {write:.0f}",
+        f"hbm_bytes_per_launch = {fetch + write:.0f}",
+        f"algorithmic_bytes_per_launch = {launch_alg_bytes:.0f}",
+        f"traffic_over_algorithmic = {(fetch + write) / launch_alg_bytes:.3f}",
+    ]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    open(TRAFFIC_FILE, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large_batch")
+    ap.add_argument("--variant", default=None)
+    ap.add_argument("--batch-invariant", type=int, default=0)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", default=None)
+    ap.add_argument("--pmc-commands", default="{}")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the scan shards across GPUs by heads and sequences with no communication, "
+              "which is not built here", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    import chunked_gated_delta_prefill_amd as gdn
+    import gdn_workloads as W
+
+    gdn.load()
+    w = W.make(args.workload, device="cuda", variant=args.variant)
+    flops, byts = algorithmic(w)
+    if args.summarize_pmc:
+        cmds = json.loads(args.pmc_commands)
+        summarize_pmc(args.summarize_pmc, cmds.get("fetch", "?"), cmds.get("write", "?"),
+                      cmds.get("copy_fetch", "?"), cmds.get("copy_write", "?"), byts)
+        return
+
+    out = torch.empty(w.T, w.Hv, D, dtype=w.q.dtype, device="cuda")
+    fin = None if w.state_dtype is None else torch.empty(w.N, w.Hv, D, D, dtype=w.state_dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin,
+                              w.use_qk_l2norm, bool(args.batch_invariant), out, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch durations with events on the launch stream (one kernel per call)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = statistics.mean(launch_ms)
+    value = w.T / (ms_step / 1e3)
+    achieved = byts / (kern_ms / 1e3) / 1e9
+    traffic = read_traffic()
+    res = {
+        "metric": "GDN prefill tokens/s and TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.q.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "sequences": w.N, "tokens": w.T, "hqk": w.Hqk, "hv": w.Hv,
+                   "head_dim": D, "state": str(w.initial_state.dtype).replace("torch.", "")
+                   if w.initial_state is not None else None, "l2norm": w.use_qk_l2norm,
+                   "batch_invariant": bool(args.batch_invariant)},
+        "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
+        "mfma_frac": round(flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": round(kern_ms, 4),
+        "kernel_ms_p20_p80": [round(sorted(launch_ms)[int(0.2 * (len(launch_ms) - 1))], 4),
+                              round(sorted(launch_ms)[int(0.8 * (len(launch_ms) - 1))], 4)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": KERNEL, "algorithmic_bytes": byts, "algorithmic_flops": flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -170,6 +170,14 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
     if (T > 0 && (!aligned16(q->data, esz, q->strides, 2) || !aligned16(k->data, esz, k->strides, 2)))
         return fail(GDN_ERR_UNSUPPORTED, "q and k rows must be 16-byte aligned (pointer and token/head strides)");
 
+    // Per-row offsets inside one 64-token chunk are 32-bit; rows must not overlap.
+    const int64_t kRowLimit = ((int64_t)1 << 31) / (gdn::kChunk + 1);
+    const gdn_tensor *rows[4] = {q, k, v, out};
+    for (const gdn_tensor *t : rows)
+        if (T > 1 && (t->strides[0] < gdn::kHeadDim || t->strides[0] * (int64_t)esz >= kRowLimit))
+            return fail(GDN_ERR_UNSUPPORTED, "token strides of q, k, v and out must be >= 128 elements "
+                                             "and < 32 MiB");
+
     // ---- gates
     if (g) {
         if ((rc = check_basic(g, "g", 2, msg, false))) return fail(rc, msg);
@@ -177,6 +185,8 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
             return fail(GDN_ERR_INVALID_ARGUMENT, "g must be [T, Hv]");
         if (g->dtype != GDN_F32 && g->dtype != GDN_BF16 && g->dtype != GDN_F16)
             return fail(GDN_ERR_INVALID_ARGUMENT, "g must be f32, bf16 or f16");
+        if (T > 1 && g->strides[0] * (int64_t)dt_size(g->dtype) >= kRowLimit)
+            return fail(GDN_ERR_UNSUPPORTED, "g token stride too large");
     }
     if (beta) {
         if ((rc = check_basic(beta, "beta", 2, msg, false))) return fail(rc, msg);
@@ -184,6 +194,8 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
             return fail(GDN_ERR_INVALID_ARGUMENT, "beta must be [T, Hv]");
         if (beta->dtype != GDN_F32 && beta->dtype != io)
             return fail(GDN_ERR_INVALID_ARGUMENT, "beta must be f32 or q's dtype");
+        if (T > 1 && beta->strides[0] * (int64_t)dt_size(beta->dtype) >= kRowLimit)
+            return fail(GDN_ERR_UNSUPPORTED, "beta token stride too large");
     }
 
     // ---- cu_seqlens
@@ -209,6 +221,14 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
             st[i]->sizes[3] != gdn::kHeadDim)
             return fail(GDN_ERR_INVALID_ARGUMENT, std::string(st_name[i]) + " must be [N, Hv, 128, 128]");
     }
+    for (int i = 0; i < 2; ++i) {
+        if (!st[i] || N == 0) continue;
+        const int64_t se = (int64_t)dt_size(st[i]->dtype);
+        if (!aligned16(st[i]->data, (size_t)se, st[i]->strides, 3) || st[i]->strides[2] < gdn::kHeadDim ||
+            st[i]->strides[2] * se * gdn::kHeadDim >= kRowLimit)
+            return fail(GDN_ERR_UNSUPPORTED, std::string(st_name[i]) +
+                                                 ": rows must be 16-byte aligned, >= 128 elements apart (pointer and strides)");
+    }
     if (initial_state && output_state && initial_state->data == output_state->data && N > 0)
         return fail(GDN_ERR_ALIAS, "output_state must not alias initial_state");
     if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale must be finite");
@@ -218,36 +238,45 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
     if (N == 0) return GDN_OK;
 
     gdn::ScanParams p{};
-    p.q = q->data; p.k = k->data; p.v = v->data;
-    p.q_st = q->strides[0]; p.q_sh = q->strides[1];
-    p.k_st = k->strides[0]; p.k_sh = k->strides[1];
-    p.v_st = v->strides[0]; p.v_sh = v->strides[1];
-    p.g = g ? g->data : nullptr;
-    p.g_st = g ? g->strides[0] : 0; p.g_sh = g ? g->strides[1] : 0; p.g_dt = g ? g->dtype : GDN_F32;
-    p.beta = beta ? beta->data : nullptr;
-    p.b_st = beta ? beta->strides[0] : 0; p.b_sh = beta ? beta->strides[1] : 0;
-    p.b_dt = beta ? beta->dtype : GDN_F32;
+    const int64_t es = (int64_t)esz;
+    p.q = static_cast<const char *>(q->data);
+    p.k = static_cast<const char *>(k->data);
+    p.v = static_cast<const char *>(v->data);
+    p.q_st = (int32_t)(q->strides[0] * es); p.q_sh = q->strides[1] * es;
+    p.k_st = (int32_t)(k->strides[0] * es); p.k_sh = k->strides[1] * es;
+    p.v_st = (int32_t)(v->strides[0] * es); p.v_sh = v->strides[1] * es;
+    if (g) {
+        const int64_t ge = (int64_t)dt_size(g->dtype);
+        p.g = static_cast<const char *>(g->data);
+        p.g_st = (int32_t)(g->strides[0] * ge); p.g_sh = g->strides[1] * ge; p.g_dt = g->dtype;
+    }
+    if (beta) {
+        const int64_t be = (int64_t)dt_size(beta->dtype);
+        p.beta = static_cast<const char *>(beta->data);
+        p.b_st = (int32_t)(beta->strides[0] * be); p.b_sh = beta->strides[1] * be; p.b_dt = beta->dtype;
+    }
     p.cu = cu_seqlens->data; p.cu_i64 = cu_seqlens->dtype == GDN_I64;
-    p.s_in = initial_state ? initial_state->data : nullptr;
     if (initial_state) {
-        p.si_n = initial_state->strides[0]; p.si_h = initial_state->strides[1];
-        p.si_v = initial_state->strides[2]; p.si_dt = initial_state->dtype;
+        const int64_t se = (int64_t)dt_size(initial_state->dtype);
+        p.s_in = static_cast<const char *>(initial_state->data);
+        p.si_n = initial_state->strides[0] * se; p.si_h = initial_state->strides[1] * se;
+        p.si_v = (int32_t)(initial_state->strides[2] * se); p.si_dt = initial_state->dtype;
     }
-    p.s_out = output_state ? output_state->data : nullptr;
     if (output_state) {
-        p.so_n = output_state->strides[0]; p.so_h = output_state->strides[1];
-        p.so_v = output_state->strides[2]; p.so_dt = output_state->dtype;
+        const int64_t se = (int64_t)dt_size(output_state->dtype);
+        p.s_out = static_cast<char *>(output_state->data);
+        p.so_n = output_state->strides[0] * se; p.so_h = output_state->strides[1] * se;
+        p.so_v = (int32_t)(output_state->strides[2] * se); p.so_dt = output_state->dtype;
     }
-    p.state_vec = 0;
-    p.out = out->data; p.o_st = out->strides[0]; p.o_sh = out->strides[1];
+    p.out = static_cast<char *>(out->data);
+    p.o_st = (int32_t)(out->strides[0] * es); p.o_sh = out->strides[1] * es;
     p.scale = scale == 0.0f ? 1.0f / std::sqrt((float)gdn::kHeadDim) : scale;
     p.N = (int32_t)N; p.Hqk = (int32_t)Hqk; p.Hv = (int32_t)Hv; p.r = (int32_t)(Hv / Hqk);
     p.l2norm = use_qk_l2norm != 0;
     (void)batch_invariant;   // the fused scan never splits a sequence
 
     const bool bf = io == GDN_BF16;
-    const int rg = 1;
-    hipError_t e = gdn::launch_fused_scan(p, bf, rg, static_cast<hipStream_t>(stream));
+    hipError_t e = gdn::launch_fused_scan(p, bf, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return GDN_OK;
 }

@@ -8,8 +8,8 @@
 // entry, the chunk (UT / WY) form of the recurrence is
 //
 //   A_ij  = b_i (k_i . k_j) exp(G_i - G_j)           j < i   (strictly lower)
-//   T     = (I + A)^-1 diag(b)                                (UT transform)
-//   Vnew  = T (V - diag(gamma) K S0^T)
+//   T'    = (I + A)^-1                                        (UT transform)
+//   Vnew  = T' ( b o (V - diag(gamma) K S0^T) )               (rows scaled by b)
 //   O     = scale [ diag(gamma) Q S0^T + ((Q K^T) o D) Vnew ],  D_ij = exp(G_i-G_j), j <= i
 //   S_L   = gamma_L S0 + Vnew^T diag(exp(G_L - G)) K
 //
@@ -17,21 +17,27 @@
 // normalisation is folded into per-row factors (rk, rq) so the MFMA operands
 // are the caller's exact q/k values.
 //
-// Mapping to the hardware (one workgroup per sequence and per group of RG
-// value heads that share one q/k head; 4 waves per value head):
-//   * the fp32 state of each value head lives in MFMA accumulators for the
-//     whole sequence: wave w of a head owns state rows v in [32w, 32w+32) as
-//     four 32x32 accumulator tiles of S^T (rows k, columns v);
-//   * the accumulator layout is reused directly as the B operand of the next
-//     products (S0^T in K S0^T / Q S0^T, and Z / Vnew in T Z, P Vnew and the
-//     state update): the contraction index of those products is permuted to
-//     match the accumulator's row order, and the LDS-side operand is read
-//     with the same permutation, so the state never leaves registers;
-//   * K, Q, K^T (bf16 path), T and P are staged in LDS; the intra-chunk
-//     inverse is computed with 16-row diagonal blocks by forward substitution
-//     and two block-merge steps;
-//   * the bf16 path runs v_mfma_f32_32x32x16_bf16 (fp32 accumulate); the fp32
-//     path runs v_mfma_f32_32x32x2_f32 so fp32 inputs keep fp32 accuracy.
+// Mapping to the hardware.  One workgroup (4 waves) scans one value head of
+// one sequence; two workgroups share a CU (LDS < 80 KB, <= 256 VGPRs) so one
+// can run matrix work while the other waits or solves.
+//   * The fp32 state lives in MFMA accumulators for the whole sequence: wave
+//     w owns state rows v in [32w, 32w+32) as four 32x32 tiles of S^T.
+//   * Accumulators are reused directly as B operands (S0^T, Z, Vnew): the
+//     contraction index of those products is permuted to the accumulator's
+//     row order and the LDS-side operand is read with the same permutation.
+//   * Per chunk: [L] stage K, K^T, Q and gates in LDS; [A] K S0^T and Q S0^T
+//     (each wave its own state rows) plus the Gram tiles; [B] A and P into
+//     LDS (P reuses Q's space) and the next chunk's loads are issued into
+//     registers; [C] one wave forms T' (16-row diagonal blocks by forward
+//     substitution, then 16->32->64 block merges on MFMA); [D] Vnew, O and
+//     the state update.
+//   * Global accesses go through buffer resources whose range ends at the
+//     chunk's last valid token, so ragged tails load zeros and drop stores
+//     without branches.
+//   * Value heads that share a q/k head are mapped to workgroups that land on
+//     the same XCD at the same time, so their q/k reads meet in that L2.
+//   * bf16 inputs run v_mfma_f32_32x32x16_bf16 / 16x16x16 (fp32 accumulate);
+//     fp32 inputs run the fp32 MFMAs so they keep fp32 accuracy.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -46,74 +52,141 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = kChunk;
 constexpr int D = kHeadDim;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9-family data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcWord3);
+}
 
 // ----------------------------------------------------------------- MFMA ----
-// 32x32 MFMA lane layout (wave64): lane l, row/col index l % 32, half h = l / 32.
-//   A operand: row m = l % 32, contraction slots owned by half h.
-//   B operand: col n = l % 32, contraction slots owned by half h.
-//   Accumulator (16 fp32): col n = l % 32, row 8*(r/4) + 4*h + r%4 for reg r.
+// 32x32 MFMA lane layout (wave64): lane l, index l % 32, half h = l / 32.
+//   A operand: row m = l % 32; B operand: col n = l % 32; contraction slots
+//   owned by half h.  Accumulator (16 fp32): col n = l % 32, row
+//   8*(r/4) + 4*h + r%4 for register r.
+// 16x16 MFMA: lane l, index l % 16, group g = l / 16.  Accumulator (4 fp32):
+//   col n = l % 16, row 4*g + r.
 template <typename OT> struct Mma;
 template <> struct Mma<bf16> {
-    static constexpr int E = 8;                     // operand elements per lane
+    static constexpr int E = 8;                     // 32x32 operand elements per lane
+    static constexpr int E16 = 4;                   // 16x16 operand elements per lane
     typedef bf16x8 frag;
+    typedef bf16x4 frag16;
     __device__ static f32x16 run(frag a, frag b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static f32x4 run16(frag16 a, frag16 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
 };
 template <> struct Mma<float> {
     static constexpr int E = 1;
+    static constexpr int E16 = 1;
     typedef float frag;
+    typedef float frag16;
     __device__ static f32x16 run(frag a, frag b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
     }
+    __device__ static f32x4 run16(frag16 a, frag16 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
 };
 
-// Row of accumulator register r for half h.
+// Row of 32x32 accumulator register r for half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// "Accumulator order" operand fragment: step s of a 32-wide contraction
-// block starting at cb; slot e of half h holds contraction index
-// cb + acc_row(s*E + e, h).  Read from row `row` of a row-major LDS matrix.
-template <typename OT>
-__device__ __forceinline__ typename Mma<OT>::frag ld_acc_order(const OT *M, int ld, int row, int cb, int s, int h) {
-    if constexpr (std::is_same<OT, bf16>::value) {
+template <typename T> struct is_bf : std::is_same<T, bf16> {};
+
+// 32x32 operand, accumulator order: step s of a 32-wide contraction block at
+// cb; slot e of half h holds index cb + acc_row(s*E + e, h).  Row-major LDS.
+template <typename OT, typename ST>
+__device__ __forceinline__ typename Mma<OT>::frag ld_acc(const ST *M, int ld, int row, int cb, int s, int h) {
+    if constexpr (is_bf<OT>::value && is_bf<ST>::value) {
         const bf16 *p = M + row * ld + cb + 16 * s + 4 * h;
         const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(p);
         const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(p + 8);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else if constexpr (is_bf<OT>::value) {        // fp32 LDS -> bf16 operand
+        const float *p = M + row * ld + cb + 16 * s + 4 * h;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 8);
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f[e] = (bf16)lo[e]; f[4 + e] = (bf16)hi[e]; }
+        return f;
     } else {
         return M[row * ld + cb + acc_row(s, h)];
     }
 }
 
-// Same contraction order, but the LDS matrix is stored transposed
-// (element (row, idx) at M[idx * ld + row]); fp32 path only.
-__device__ __forceinline__ float ld_acc_order_t(const float *M, int ld, int row, int cb, int s, int h) {
-    return M[(cb + acc_row(s, h)) * ld + row];
+// Same order, element (row, idx) stored at M[idx * ld + row] (column read).
+template <typename OT, typename ST>
+__device__ __forceinline__ typename Mma<OT>::frag ld_acc_t(const ST *M, int ld, int row, int cb, int s, int h) {
+    if constexpr (is_bf<OT>::value) {
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (bf16)(float)M[(cb + acc_row(8 * s + e, h)) * ld + row];
+        return f;
+    } else {
+        return M[(cb + acc_row(s, h)) * ld + row];
+    }
 }
 
-// Natural-order fragment (both operands from LDS): step s covers contraction
-// [2E*s, 2E*s + 2E); half h holds E consecutive indices.
+// 32x32 operand, natural order: step s covers [2E*s, 2E*s + 2E), half h holds
+// E consecutive indices.  Row-major LDS in the operand type.
 template <typename OT>
-__device__ __forceinline__ typename Mma<OT>::frag ld_natural(const OT *M, int ld, int row, int s, int h) {
-    if constexpr (std::is_same<OT, bf16>::value) {
+__device__ __forceinline__ typename Mma<OT>::frag ld_nat(const OT *M, int ld, int row, int s, int h) {
+    if constexpr (is_bf<OT>::value) {
         return *reinterpret_cast<const bf16x8 *>(M + row * ld + 16 * s + 8 * h);
     } else {
         return M[row * ld + 2 * s + h];
     }
 }
 
-// Accumulator registers of step s as an operand fragment (accumulator order).
+// Accumulator registers of step s as a 32x32 operand (accumulator order).
 template <typename OT>
 __device__ __forceinline__ typename Mma<OT>::frag acc_frag(const f32x16 &a, int s) {
-    if constexpr (std::is_same<OT, bf16>::value) {
+    if constexpr (is_bf<OT>::value) {
         bf16x8 f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = (bf16)a[8 * s + e];
         return f;
+    } else {
+        return a[s];
+    }
+}
+
+// 16x16 operands, accumulator order: step s, slot e of group g holds index
+// 4*g + s*E16 + e.  Row read (row-major) and column read variants, from fp32 LDS.
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::frag16 ld16_row(const float *M, int ld, int row, int cb, int s, int g) {
+    if constexpr (is_bf<OT>::value) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(M + row * ld + cb + 4 * g);
+        return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    } else {
+        return M[row * ld + cb + 4 * g + s];
+    }
+}
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::frag16 ld16_col(const float *M, int ld, int col, int rb, int s, int g) {
+    if constexpr (is_bf<OT>::value) {
+        bf16x4 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = (bf16)M[(rb + 4 * g + e) * ld + col];
+        return f;
+    } else {
+        return M[(rb + 4 * g + s) * ld + col];
+    }
+}
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::frag16 acc16_frag(const f32x4 &a, int s) {
+    if constexpr (is_bf<OT>::value) {
+        return bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
     } else {
         return a[s];
     }
@@ -126,415 +199,629 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
-__device__ __forceinline__ float load_gate(const void *p, int64_t off, int dt) {
-    if (dt == GDN_F32) return static_cast<const float *>(p)[off];
-    if (dt == GDN_BF16) return (float)static_cast<const bf16 *>(p)[off];
-    return (float)static_cast<const _Float16 *>(p)[off];
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
 }
 
 __device__ __forceinline__ int64_t load_cu(const void *cu, int i, int is64) {
     return is64 ? static_cast<const int64_t *>(cu)[i] : (int64_t) static_cast<const int32_t *>(cu)[i];
 }
 
+// Gate loads keep the raw bits; they are converted when first used, so the
+// load is not waited for when it is issued.
+__device__ __forceinline__ uint32_t gate_bits(__amdgpu_buffer_rsrc_t r, int off, int dt) {
+    return dt == GDN_F32 ? __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)
+                         : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float gate_value(uint32_t bits, int dt) {
+    if (dt == GDN_F32) return __builtin_bit_cast(float, bits);
+    if (dt == GDN_BF16) return bf16_bits_to_float(bits & 0xffffu);
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xffffu));
+}
+
 // ---------------------------------------------------------- LDS layout ----
-template <typename IO, int RG> struct Smem {
-    static constexpr bool BF = std::is_same<IO, bf16>::value;
-    static constexpr int KLD = BF ? 136 : 132;   // K, Q rows (elements)
-    static constexpr int TLD = 72;               // K^T rows (bf16 path)
-    static constexpr int FLD = 68;               // fp32 64x64 (A, then T)
-    static constexpr int OLD = BF ? 72 : 68;     // IO-typed 64x64 operands (T copy, P)
-    static constexpr int RLD = 33;               // merge scratch
+// Per-row factor arrays (64 floats each), written once per chunk.  The state
+// is held as S = sigma * S~ (sigma a per-sequence scalar, see the kernel):
+//   RG  in-chunk log-gate cumsum G_i        RK  rk_i (1 without L2 norm)
+//   RQ  rq_i                                FA  b_i rk_i            (rows of A)
+//   PQ  rq_i                  (rows of P)   FZ  sigma gamma_i rk_i  (rows of K S~^T)
+//   FB  b_i                   (rows of Z)   FY  sigma gamma_i rq_i  (rows of Q S~^T)
+//   FU  rk_i exp(G_L - G_i) / sigma'        (state update)
+//   EA  b_i rk_i gamma_i, EQ rq_i gamma_i, CJ rk_j / gamma_j: A and P entries
+//       as products when the chunk's total decay is moderate (no exp per entry)
+// followed by gamma_L.
+enum { RG_ = 0, RK_ = 1, RQ_ = 2, FA_ = 3, PQ_ = 4, FZ_ = 5, FB_ = 6, FY_ = 7, FU_ = 8, EA_ = 9, EQ_ = 10,
+       CJ_ = 11, NROWF = 12 };
+constexpr float kFastDecay = -60.f;   // G_L above this: exp(G_i - G_j) = gamma_i / gamma_j is safe
+constexpr float kRenorm = 0x1p-40f;   // sigma below this is folded back into the state
+
+template <typename IO> struct Smem {
+    static constexpr bool BF = is_bf<IO>::value;
+    static constexpr int KLD = BF ? 136 : 132;   // K, Q rows (elements of IO)
+    static constexpr int TLD = 68;               // K^T rows (bf16 path)
+    static constexpr int OLD = 68;               // T', P rows (elements of IO)
+    static constexpr int FLD = 68;               // fp32 64x64 work matrix (A, inverse blocks)
+    static constexpr int KB = C * KLD * (int)sizeof(IO);
     static constexpr int K_OFF = 0;
-    static constexpr int Q_OFF = K_OFF + C * KLD * (int)sizeof(IO);
-    static constexpr int KT_OFF = Q_OFF + C * KLD * (int)sizeof(IO);
-    static constexpr int ROW_OFF = KT_OFF + (BF ? D * TLD * 2 : 0);   // rk[64], rq[64]
-    static constexpr int HEAD_OFF = ROW_OFF + 2 * C * 4;
-    // per head: Tf (fp32), Tb (bf16 copy, bf16 path only), P, R, G/gam/dec/bet
-    static constexpr int TF = 0;
-    static constexpr int TB = TF + C * FLD * 4;
-    static constexpr int P = TB + (BF ? C * OLD * 2 : 0);
-    static constexpr int R = P + C * OLD * (int)sizeof(IO);
-    static constexpr int SC = R + 32 * RLD * 4;
-    static constexpr int HEAD_BYTES = SC + 4 * C * 4;
-    static constexpr int BYTES = HEAD_OFF + RG * HEAD_BYTES;
+    static constexpr int KT_OFF = K_OFF + KB;
+    static constexpr int Q_OFF = KT_OFF + (BF ? D * TLD * 2 : 0);
+    // bf16: P and T' reuse Q's space once Q has been consumed
+    static constexpr int P_OFF = BF ? Q_OFF : Q_OFF + KB;
+    static constexpr int T_OFF = P_OFF + C * OLD * (int)sizeof(IO);
+    static constexpr int AF_OFF = BF ? Q_OFF + KB : T_OFF + C * OLD * (int)sizeof(IO);
+    static constexpr int ROW_OFF = AF_OFF + C * FLD * 4;
+    static constexpr int BYTES = ROW_OFF + (NROWF * C + 4) * 4;
+    static_assert(!BF || T_OFF + C * OLD * 2 <= Q_OFF + KB, "P and T' must fit in Q's space");
+    static_assert(!BF || BYTES <= 80 * 1024, "two workgroups per CU");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
-    static_assert(Q_OFF % 16 == 0 && KT_OFF % 16 == 0 && HEAD_OFF % 16 == 0 && HEAD_BYTES % 16 == 0, "align");
+    static_assert(KT_OFF % 16 == 0 && Q_OFF % 16 == 0 && AF_OFF % 16 == 0 && T_OFF % 16 == 0 &&
+                  ROW_OFF % 16 == 0, "align");
 };
 
-template <typename IO, int RG>
-__global__ __launch_bounds__(256 * RG) void fused_scan_kernel(const ScanParams p) {
-    using L = Smem<IO, RG>;
+// Sum over the 16 lanes of a DPP row (every lane gets the total).
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    return x;
+}
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// K, Q and the gates of the next chunk, loaded while the current chunk runs
+// (consumed only after the chunk's last barrier, so no wait is forced early).
+template <typename IO> struct Prefetch;
+template <> struct Prefetch<bf16> {
+    i32x4 kq[2][4];      // K and Q: 4 rows x 8 columns per thread
+    uint32_t g, b;       // raw gate bits of token `lane` (wave 0)
+};
+template <> struct Prefetch<float> {
+    f32x4 kq[2][8];      // K and Q: 8 rows x 4 columns per thread
+    uint32_t g, b;
+};
+// This chunk's V in accumulator layout (rows 32*ib + acc_row(r, h32), column
+// v0), one element per register; loaded at the start of the chunk and first
+// read in the last phase.
+struct VRegs {
+    uint32_t x[32];
+};
+__device__ __forceinline__ float vreg_at(const VRegs &v, int e, bool bf) {
+    return bf ? bf16_bits_to_float(v.x[e] & 0xffffu) : __builtin_bit_cast(float, v.x[e]);
+}
+
+struct ChunkRef {
+    int64_t t0;
+    int L;
+};
+
+// Loads one chunk's inputs into registers.  Each lane keeps one VGPR offset;
+// for full chunks the per-row offsets go in the scalar offset operand, for
+// the ragged last chunk they go in the (range-checked) vector offset so rows
+// past the end load zeros.
+template <typename IO>
+__device__ __forceinline__ void issue_loads(Prefetch<IO> &pf, const ScanParams &p, ChunkRef ch, int hq, int h,
+                                            int tid, int lane, int ws) {
+    constexpr bool BF = is_bf<IO>::value;
+    constexpr int ES = (int)sizeof(IO);
+    const int L = ch.L;
+    const auto rk = rsrc(p.k + ch.t0 * p.k_st + hq * p.k_sh, L > 0 ? (L - 1) * p.k_st + D * ES : 0);
+    const auto rq = rsrc(p.q + ch.t0 * p.q_st + hq * p.q_sh, L > 0 ? (L - 1) * p.q_st + D * ES : 0);
+    if constexpr (BF) {
+        const int rq4 = tid >> 4, cg = tid & 15;
+        const int vk = 4 * rq4 * p.k_st + 16 * cg, vq = 4 * rq4 * p.q_st + 16 * cg;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            pf.kq[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rk, vk + t * p.k_st, 0, 0);
+            pf.kq[1][t] = __builtin_amdgcn_raw_buffer_load_b128(rq, vq + t * p.q_st, 0, 0);
+        }
+    } else {
+        const int r0 = tid >> 5, cg = tid & 31;
+        const int vk = r0 * p.k_st + 16 * cg, vq = r0 * p.q_st + 16 * cg;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pf.kq[0][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vk + 8 * j * p.k_st, 0, 0));
+            pf.kq[1][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vq + 8 * j * p.q_st, 0, 0));
+        }
+    }
+    if (ws == 0) {   // gates of token `lane`
+        pf.g = 0;
+        pf.b = 0;
+        if (p.g) {
+            const auto rg = rsrc(p.g + ch.t0 * p.g_st + h * p.g_sh, L > 0 ? (L - 1) * p.g_st + 4 : 0);
+            pf.g = gate_bits(rg, lane * p.g_st, p.g_dt);
+        }
+        if (p.beta) {
+            const auto rb = rsrc(p.beta + ch.t0 * p.b_st + h * p.b_sh, L > 0 ? (L - 1) * p.b_st + 4 : 0);
+            pf.b = gate_bits(rb, lane * p.b_st, p.b_dt);
+        }
+    }
+}
+
+template <typename IO>
+__device__ __forceinline__ void issue_v(VRegs &vr, const ScanParams &p, ChunkRef ch, int h, int h32, int v0) {
+    constexpr bool BF = is_bf<IO>::value;
+    constexpr int ES = (int)sizeof(IO);
+    const int L = ch.L;
+    const bool full = L == C;
+    const auto rv = rsrc(p.v + ch.t0 * p.v_st + h * p.v_sh, L > 0 ? (L - 1) * p.v_st + D * ES : 0);
+    const int vv = 4 * h32 * p.v_st + v0 * ES;
+    auto vall = [&](bool in_soffset) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const int ro = (32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3)) * p.v_st;
+            if constexpr (BF)
+                vr.x[e] = in_soffset ? __builtin_amdgcn_raw_buffer_load_b16(rv, vv, ro, 0)
+                                     : __builtin_amdgcn_raw_buffer_load_b16(rv, vv + ro, 0, 0);
+            else
+                vr.x[e] = in_soffset ? __builtin_amdgcn_raw_buffer_load_b32(rv, vv, ro, 0)
+                                     : __builtin_amdgcn_raw_buffer_load_b32(rv, vv + ro, 0, 0);
+        }
+    };
+    if (full) vall(true);
+    else vall(false);
+}
+
+__device__ __forceinline__ ChunkRef chunk_at(int64_t bos, int64_t eos, int c) {
+    ChunkRef ch;
+    ch.t0 = bos + (int64_t)c * C;
+    const int64_t rem = eos - ch.t0;
+    ch.L = rem <= 0 ? 0 : (rem >= C ? C : (int)rem);
+    return ch;
+}
+
+// bf16: two workgroups per CU (LDS < 80 KB) need <= 256 registers per lane;
+// fp32 (LDS-bound to one workgroup per CU) keeps the full register file.
+template <typename IO>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(is_bf<IO>::value ? 2 : 1,
+                                                                    is_bf<IO>::value ? 2 : 1))) void
+fused_scan_kernel(const ScanParams p) {
+    using L = Smem<IO>;
     using M = Mma<IO>;
     using frag = typename M::frag;
     constexpr bool BF = L::BF;
     constexpr int E = M::E;
-    constexpr int S32 = 32 / (2 * E);       // MFMA steps per 32-wide contraction block
-    constexpr int NT = 256 * RG;
+    constexpr int S32 = 32 / (2 * E);       // 32x32 MFMA steps per 32-wide contraction block
+    constexpr int S16 = 16 / (4 * M::E16);  // 16x16 MFMA steps per 16-wide contraction block
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     IO *Ks = reinterpret_cast<IO *>(smem + L::K_OFF);
-    IO *Qs = reinterpret_cast<IO *>(smem + L::Q_OFF);
     bf16 *KTs = reinterpret_cast<bf16 *>(smem + L::KT_OFF);
-    float *rks = reinterpret_cast<float *>(smem + L::ROW_OFF);
-    float *rqs = rks + C;
+    IO *Qs = reinterpret_cast<IO *>(smem + L::Q_OFF);
+    IO *Ps = reinterpret_cast<IO *>(smem + L::P_OFF);
+    IO *Ts = reinterpret_cast<IO *>(smem + L::T_OFF);
+    float *Af = reinterpret_cast<float *>(smem + L::AF_OFF);
+    float *RF = reinterpret_cast<float *>(smem + L::ROW_OFF);     // per-row factors
+    auto rf = [&](int which) { return RF + which * C; };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int grp = wave >> 2, ws = wave & 3;
-    const int h32 = lane >> 5, l32 = lane & 31;
-
-    char *hbase = smem + L::HEAD_OFF + grp * L::HEAD_BYTES;
-    float *Tf = reinterpret_cast<float *>(hbase + L::TF);
-    IO *Pm = reinterpret_cast<IO *>(hbase + L::P);
-    float *Rs = reinterpret_cast<float *>(hbase + L::R);
-    float *Gs = reinterpret_cast<float *>(hbase + L::SC);
-    float *gams = Gs + C, *decs = Gs + 2 * C, *bets = Gs + 3 * C;
-    const IO *Top;
-    int TOLD;
-    if constexpr (BF) {
-        Top = reinterpret_cast<const IO *>(hbase + L::TB);
-        TOLD = L::OLD;
-    } else {
-        Top = reinterpret_cast<const IO *>(Tf);
-        TOLD = L::FLD;
-    }
-
-    const int HG = p.Hv / RG;
-    const int n = blockIdx.x / HG, hg = blockIdx.x % HG;
-    const int h = hg * RG + grp;              // this wave's value head
-    const int hq = (hg * RG) / p.r;           // shared q/k head
+    // ---- work item: XCD-aware so the r value heads of one q/k head meet in one L2
+    const int r = p.r;
+    const int b = blockIdx.x;
+    const int within = b % (8 * r);
+    const int pidx = (b / (8 * r)) * 8 + (within & 7);
+    if (pidx >= p.N * p.Hqk) return;
+    const int n = pidx / p.Hqk, hq = pidx % p.Hqk;
+    const int h = hq * r + (within >> 3);
     const int64_t bos = load_cu(p.cu, n, p.cu_i64), eos = load_cu(p.cu, n + 1, p.cu_i64);
-    const int v0 = ws * 32 + l32;             // this lane's state row v
-
-    const IO *qg = static_cast<const IO *>(p.q);
-    const IO *kg = static_cast<const IO *>(p.k);
-    const IO *vg = static_cast<const IO *>(p.v);
-    IO *og = static_cast<IO *>(p.out);
 
     // ---- initial state: S[b] holds S^T rows k = 32b + acc_row(r, h32), column v0
     f32x16 S[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) S[b] = zero16();
-    if (p.s_in) {
-        const int64_t base = (int64_t)n * p.si_n + (int64_t)h * p.si_h + (int64_t)v0 * p.si_v;
+    for (int bb = 0; bb < 4; ++bb) S[bb] = zero16();
+    {
+        const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
+        const int h32 = lane >> 5, v0 = ws * 32 + (lane & 31);
+        if (p.s_in) {
+            const auto rs = rsrc(p.s_in + n * p.si_n + h * p.si_h, (int64_t)D * p.si_v);
+            if (p.si_dt == GDN_F32) {
+                const int vo = v0 * p.si_v + 16 * h32;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+                for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k0 = 32 * b + 8 * j + 4 * h32;
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4 x = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo + 4 * (32 * bb + 8 * j), 0, 0));
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    float x;
-                    if (p.si_dt == GDN_F32) x = static_cast<const float *>(p.s_in)[base + k0 + t];
-                    else x = (float)static_cast<const bf16 *>(p.s_in)[base + k0 + t];
-                    S[b][4 * j + t] = x;
-                }
+                        for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = x[t];
+                    }
+            } else {
+                const int vo = v0 * p.si_v + 8 * h32;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bf16x4 x = __builtin_bit_cast(
+                            bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rs, vo + 2 * (32 * bb + 8 * j), 0, 0));
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = (float)x[t];
+                    }
             }
+        }
     }
 
     const int nchunks = (int)((eos - bos + C - 1) / C);
+    float sigma = 1.f;          // true state = sigma * S (uniform across the workgroup)
+    Prefetch<IO> pf;
+    if (nchunks > 0) issue_loads<IO>(pf, p, chunk_at(bos, eos, 0), hq, h, threadIdx.x, threadIdx.x & 63, threadIdx.x >> 6);
+
     for (int c = 0; c < nchunks; ++c) {
-        const int64_t t0 = bos + (int64_t)c * C;
-        const int Lc = (int)min((int64_t)C, eos - t0);
+        const ChunkRef ch = chunk_at(bos, eos, c);
+        const int Lc = ch.L;
+        // Lane indices are re-derived from an opaque copy each chunk so that the
+        // compiler recomputes per-element addresses and masks (a few ALU ops)
+        // instead of hoisting hundreds of them out of the loop into registers.
+        int tid_o = threadIdx.x;
+        asm volatile("" : "+v"(tid_o));
+        const int tid = tid_o, lane = tid & 63;
+        const int ws = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int h32 = lane >> 5, l32 = lane & 31;
+        const int v0 = ws * 32 + l32;
 
-        // ---- phase 1: stage K, Q (+K^T), row norms; gates and in-chunk cumsum
-
+        // ---- [L] stage K, K^T, Q and row norms; gates and the in-chunk log-gate cumsum
+        VRegs vcur;
+        issue_v<IO>(vcur, p, ch, h, h32, v0);
         if constexpr (BF) {
-            // unit = (matrix, 4-row quad, 8-column group): 4 x 16-byte rows
-            for (int u = tid; u < 512; u += NT) {
-                const int mat = u >> 8, rq = (u >> 4) & 15, cg = u & 15;
-                const bf16 *src = mat ? qg : kg;
-                const int64_t st = mat ? p.q_st : p.k_st;
-                const int64_t off = (int64_t)hq * (mat ? p.q_sh : p.k_sh) + 8 * cg;
-                bf16x8 x[4];
+            const int rq4 = tid >> 4, cg = tid & 15;
+#pragma unroll
+            for (int mat = 0; mat < 2; ++mat) {
                 float ss[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const int i = 4 * rq + t;
-                    if (i < Lc) {
-                        x[t] = *reinterpret_cast<const bf16x8 *>(src + (t0 + i) * st + off);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) x[t][e] = (bf16)0.f;
-                    }
+                    const bf16x8 x = __builtin_bit_cast(bf16x8, pf.kq[mat][t]);
                     float a = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) a += (float)x[t][e] * (float)x[t][e];
-                    ss[t] = a;
+                    for (int e = 0; e < 8; ++e) a += (float)x[e] * (float)x[e];
+                    ss[t] = row_sum16(a);
+                    *reinterpret_cast<i32x4 *>((mat ? Qs : Ks) + (4 * rq4 + t) * L::KLD + 8 * cg) = pf.kq[mat][t];
                 }
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                    for (int o = 1; o < 16; o <<= 1) ss[t] += __shfl_xor(ss[t], o);
-                }
-                IO *dst = mat ? Qs : Ks;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    *reinterpret_cast<bf16x8 *>(dst + (4 * rq + t) * L::KLD + 8 * cg) = x[t];
                 if (cg == 0) {
-                    float *rn = mat ? rqs : rks;
+                    f32x4 rn;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) rn[4 * rq + t] = p.l2norm ? rsqrtf(ss[t] + 1e-6f) : 1.f;
+                    for (int t = 0; t < 4; ++t) rn[t] = p.l2norm ? rsqrtf(ss[t] + 1e-6f) : 1.f;
+                    *reinterpret_cast<f32x4 *>(rf(mat ? RQ_ : RK_) + 4 * rq4) = rn;
                 }
-                if (mat == 0) {
+            }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        bf16x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
-                        *reinterpret_cast<bf16x4 *>(KTs + (8 * cg + e) * L::TLD + 4 * rq) = col;
-                    }
-                }
+            for (int e = 0; e < 8; ++e) {
+                bf16x4 col;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) col[t] = __builtin_bit_cast(bf16x8, pf.kq[0][t])[e];
+                *reinterpret_cast<bf16x4 *>(KTs + (8 * cg + e) * L::TLD + 4 * rq4) = col;
             }
         } else {
-            // unit = (matrix, row, 4-float group)
-            for (int u = tid; u < 2 * C * 32; u += NT) {
-                const int mat = u >> 11, i = (u >> 5) & 63, cg = u & 31;
-                const float *src = reinterpret_cast<const float *>(mat ? qg : kg);
-                const int64_t st = mat ? p.q_st : p.k_st;
-                const int64_t off = (int64_t)hq * (mat ? p.q_sh : p.k_sh) + 4 * cg;
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
-                if (i < Lc) x = *reinterpret_cast<const f32x4 *>(src + (t0 + i) * st + off);
-                float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+            const int r0 = tid >> 5, cg = tid & 31;
 #pragma unroll
-                for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
-                float *dst = reinterpret_cast<float *>(mat ? Qs : Ks);
-                *reinterpret_cast<f32x4 *>(dst + i * L::KLD + 4 * cg) = x;
-                if (cg == 0) (mat ? rqs : rks)[i] = p.l2norm ? rsqrtf(ss + 1e-6f) : 1.f;
-            }
+            for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const f32x4 x = pf.kq[mat][j];
+                    float ss = row_sum16(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
+                    ss += __shfl_xor(ss, 16);
+                    *reinterpret_cast<f32x4 *>((mat ? Qs : Ks) + (r0 + 8 * j) * L::KLD + 4 * cg) = x;
+                    if (cg == 0) rf(mat ? RQ_ : RK_)[r0 + 8 * j] = p.l2norm ? rsqrtf(ss + 1e-6f) : 1.f;
+                }
         }
-
-        if (ws == 0) {   // one wave per value head: gates and the in-chunk log-gate cumsum
-            const int i = lane;
-            const bool valid = i < Lc;
-            float a = 1.f, b = 1.f;
-            if (valid && p.g) a = load_gate(p.g, (t0 + i) * p.g_st + (int64_t)h * p.g_sh, p.g_dt);
-            if (valid && p.beta) b = load_gate(p.beta, (t0 + i) * p.b_st + (int64_t)h * p.b_sh, p.b_dt);
-            float G = valid ? fmaxf(__logf(a), -80.f) : 0.f;
+        // wave 0, lane i = token i of the chunk
+        float g_G = 0.f, g_b = 0.f, g_gam = 1.f, g_dec = 1.f;
+        if (ws == 0) {
+            const bool valid = lane < Lc;
+            const float ga = p.g ? gate_value(pf.g, p.g_dt) : 1.f;
+            const float gb = p.beta ? gate_value(pf.b, p.b_dt) : 1.f;
+            float G = valid ? fmaxf(__logf(ga), -80.f) : 0.f;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const float y = __shfl_up(G, o);
                 if (lane >= o) G += y;
             }
             const float GL = __shfl(G, 63);
-            Gs[i] = G;
-            gams[i] = __expf(G);
-            decs[i] = __expf(GL - G);
-            bets[i] = valid ? b : 0.f;
+            g_G = G;
+            g_b = valid ? gb : 0.f;
+            g_gam = __expf(G);
+            g_dec = __expf(GL - G);
+            rf(RG_)[lane] = G;
+            if (lane == 63) RF[NROWF * C] = g_gam;    // gamma_L
         }
         __syncthreads();
 
-        // ---- phase 2: Gram tiles K K^T and Q K^T (lower 32x32 tiles) -> A (fp32) and P per head
-        for (int tile = wave; tile < 6; tile += 4 * RG) {
-            const int isq = tile >= 3, tt = tile - 3 * isq;
-            const int bi = tt > 0, bj = tt == 2;
-            const IO *As = isq ? Qs : Ks;
-            f32x16 acc = zero16();
+        // ---- [A] per-row factors (wave 0); Y = Q S0^T for this wave's rows; Gram tiles
+        // The true state is sigma * S~.  After this chunk it is
+        //   gamma_L sigma S~ + K^T U  =  sigma' (S~ + K^T U / sigma'),  sigma' = gamma_L sigma,
+        // so the decay costs no per-element work; when sigma' gets small it is
+        // folded back into S~ (renorm) to keep U / sigma' in range.
+        const float gLc =
+            __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, RF[NROWF * C])));
+        const float sig_next = sigma * gLc;
+        const bool renorm = !(sig_next >= kRenorm);
+        if (ws == 0) {
+            const float rk = rf(RK_)[lane], rq = rf(RQ_)[lane];
+            rf(FA_)[lane] = g_b * rk;
+            rf(PQ_)[lane] = rq;
+            rf(FZ_)[lane] = sigma * g_gam * rk;
+            rf(FB_)[lane] = g_b;
+            rf(FY_)[lane] = sigma * g_gam * rq;
+            rf(FU_)[lane] = renorm ? rk * g_dec : rk * g_dec / sig_next;
+            rf(EA_)[lane] = g_b * rk * g_gam;
+            rf(EQ_)[lane] = rq * g_gam;
+            rf(CJ_)[lane] = rk / g_gam;
+        }
+        (void)g_G;
+        f32x16 Y[2] = {zero16(), zero16()};
+        {
+            frag sb[4][S32];
 #pragma unroll
-            for (int s = 0; s < D / (2 * E); ++s) {
-                const frag a = ld_natural<IO>(As, L::KLD, 32 * bi + l32, s, h32);
-                const frag bb = ld_natural<IO>(Ks, L::KLD, 32 * bj + l32, s, h32);
-                acc = M::run(a, bb, acc);
+            for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                for (int s = 0; s < S32; ++s) sb[bb][s] = acc_frag<IO>(S[bb], s);
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int s = 0; s < S32; ++s)
+                        Y[ib] = M::run(ld_acc<IO>(Qs, L::KLD, 32 * ib + l32, 32 * bb, s, h32), sb[bb][s], Y[ib]);
+        }
+        // tiles: 0..2 = K K^T (0,0) (1,0) (1,1); 3..5 = Q K^T (same); wave w takes w and w + 4
+        f32x16 gt[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tile = ws + 4 * u;
+            if (tile < 6) {
+                const int isq = tile >= 3, tt = tile - 3 * isq;
+                const int bi = tt > 0, bj = tt == 2;
+                const IO *As = isq ? Qs : Ks;
+#pragma unroll
+                for (int s = 0; s < D / (2 * E); ++s)
+                    gt[u] = M::run(ld_nat<IO>(As, L::KLD, 32 * bi + l32, s, h32),
+                                   ld_nat<IO>(Ks, L::KLD, 32 * bj + l32, s, h32), gt[u]);
             }
-            const int j = 32 * bj + l32;
-            const float rkj = rks[j];
+        }
+        __syncthreads();
+
+        // ---- [B] next chunk's K, Q, gates in flight; A (fp32) and P into LDS
+        issue_loads<IO>(pf, p, chunk_at(bos, eos, c + 1), hq, h, tid, lane, ws);
 #pragma unroll
-            for (int hh = 0; hh < RG; ++hh) {
-                char *hb = smem + L::HEAD_OFF + hh * L::HEAD_BYTES;
-                float *Tfh = reinterpret_cast<float *>(hb + L::TF);
-                IO *Ph = reinterpret_cast<IO *>(hb + L::P);
-                const float *Gh = reinterpret_cast<const float *>(hb + L::SC);
-                const float *bh = Gh + 3 * C;
-                const float Gj = Gh[j];
+        for (int u = 0; u < 2; ++u) {
+            const int tile = ws + 4 * u;
+            if (tile < 6) {
+                const int isq = tile >= 3, tt = tile - 3 * isq;
+                const int bi = tt > 0, bj = tt == 2;
+                const int j = 32 * bj + l32;
+                const float rkj = rf(RK_)[j], Gj = rf(RG_)[j];
+                // i - j for register rr is d0 + 8*(rr/4) + rr%4
+                const int d0 = 32 * (bi - bj) + 4 * h32 - l32;
+                const bool fast = rf(RG_)[C - 1] > kFastDecay;
+                const float cj = rf(CJ_)[j];
+                if (isq) {        // P = rq_i rk_j (q_i . k_j) exp(G_i - G_j)  for j <= i
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = 32 * bi + acc_row(r, h32);
-                    if (!isq) {
-                        const float val = (j < i) ? bh[i] * rks[i] * rkj * acc[r] * __expf(Gh[i] - Gj) : 0.f;
-                        Tfh[i * L::FLD + j] = val;
-                    } else {
-                        const float val = (j <= i) ? rqs[i] * rkj * acc[r] * __expf(Gh[i] - Gj) : 0.f;
-                        Ph[i * L::OLD + j] = (IO)val;
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int i0 = 32 * bi + 8 * jj + 4 * h32;
+                        IO *dst = Ps + i0 * L::OLD + j;
+                        if (fast) {
+                            const f32x4 E4 = ld4(rf(EQ_) + i0);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                dst[t * L::OLD] = (IO)(d0 + 8 * jj + t >= 0 ? E4[t] * cj * gt[u][4 * jj + t] : 0.f);
+                        } else {
+                            const f32x4 G4 = ld4(rf(RG_) + i0), F4 = ld4(rf(PQ_) + i0);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) {
+                                const float val = F4[t] * rkj * gt[u][4 * jj + t] * __expf(fminf(G4[t] - Gj, 0.f));
+                                dst[t * L::OLD] = (IO)(d0 + 8 * jj + t >= 0 ? val : 0.f);
+                            }
+                        }
+                    }
+                } else {          // A = b_i rk_i rk_j (k_i . k_j) exp(G_i - G_j)  for j < i
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int i0 = 32 * bi + 8 * jj + 4 * h32;
+                        float *dst = Af + i0 * L::FLD + j;
+                        if (fast) {
+                            const f32x4 E4 = ld4(rf(EA_) + i0);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                dst[t * L::FLD] = d0 + 8 * jj + t > 0 ? E4[t] * cj * gt[u][4 * jj + t] : 0.f;
+                        } else {
+                            const f32x4 G4 = ld4(rf(RG_) + i0), F4 = ld4(rf(FA_) + i0);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) {
+                                const float val = F4[t] * rkj * gt[u][4 * jj + t] * __expf(fminf(G4[t] - Gj, 0.f));
+                                dst[t * L::FLD] = d0 + 8 * jj + t > 0 ? val : 0.f;
+                            }
+                        }
                     }
                 }
             }
         }
         __syncthreads();
 
-        // ---- phase 3: T = (I + A)^-1 diag(b), 16-row diagonal blocks then two merges
+        // ---- [C] one wave: T' = (I + A)^-1 into Ts (operand type)
         if (ws == 0) {
-            const int b = lane >> 4, cc = lane & 15;
-            float *blk = Tf + (16 * b) * L::FLD + 16 * b;
-            float x[16];
+            // (1) 16x16 diagonal blocks by forward substitution, lane = (block, column)
+            {
+                const int bk = lane >> 4, cc = lane & 15;
+                float *blk = Af + (16 * bk) * L::FLD + 16 * bk;
+                float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
+                for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 1; i < 16; ++i) {
-                float s = 0.f;
+                for (int i = 1; i < 16; ++i) {
+                    f32x4 a4[4];
 #pragma unroll
-                for (int m = 0; m < i; ++m) s += blk[i * L::FLD + m] * x[m];
-                if (i > cc) x[i] = -s;
+                    for (int q = 0; q < 4; ++q)
+                        if (4 * q < i) a4[q] = ld4(blk + i * L::FLD + 4 * q);
+                    float s = 0.f;
+#pragma unroll
+                    for (int m = 0; m < i; ++m) s += a4[m >> 2][m & 3] * x[m];
+                    x[i] = i > cc ? -s : x[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    blk[i * L::FLD + cc] = x[i];
+                    Ts[(16 * bk + i) * L::OLD + 16 * bk + cc] = (IO)x[i];
+                }
+                if ((bk & 1) == 0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) Ts[(16 * bk + i) * L::OLD + 16 * bk + 16 + cc] = (IO)0.f;
+                }
             }
+            // (2) 16 -> 32: T'_{2x+1,2x} = -D_{2x+1} A_{2x+1,2x} D_{2x}, x = 0, 1
+            {
+                const int g = lane >> 4, nn = lane & 15;
+                f32x4 R[2];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) blk[i * L::FLD + cc] = x[i];
-            if ((b & 1) == 0) {
+                for (int x2 = 0; x2 < 2; ++x2) {
+                    const int lo = 32 * x2, hi = 32 * x2 + 16;
+                    R[x2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 16; ++i) blk[i * L::FLD + 16 + cc] = 0.f;
+                    for (int s = 0; s < S16; ++s)
+                        R[x2] = M::run16(ld16_row<IO>(Af, L::FLD, hi + nn, lo, s, g),
+                                         ld16_col<IO>(Af, L::FLD, lo + nn, lo, s, g), R[x2]);
+                }
+#pragma unroll
+                for (int x2 = 0; x2 < 2; ++x2) {
+                    const int lo = 32 * x2, hi = 32 * x2 + 16;
+                    f32x4 Tq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < S16; ++s)
+                        Tq = M::run16(ld16_row<IO>(Af, L::FLD, hi + nn, hi, s, g), acc16_frag<IO>(R[x2], s), Tq);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int i = hi + 4 * g + rr;
+                        Af[i * L::FLD + lo + nn] = -Tq[rr];
+                        Ts[i * L::OLD + lo + nn] = (IO)(-Tq[rr]);
+                    }
+                }
             }
-        }
-        __syncthreads();
-        const int tg = tid & 255;
-        float rv[4];
+            // (3) 32 -> 64: T'_21 = -T'_22 A_21 T'_11
+            {
+                f32x16 R2 = zero16();
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {      // R = A_{2x+1,2x} Dinv_{2x}
-            const int idx = tg + 256 * e, x2 = idx >> 8, i = (idx >> 4) & 15, j = idx & 15;
-            const float *Ar = Tf + (32 * x2 + 16 + i) * L::FLD + 32 * x2;
-            const float *Dc = Tf + (32 * x2) * L::FLD + 32 * x2 + j;
-            float a = 0.f;
+                for (int s = 0; s < S32; ++s)        // R2 = A_21 T'_11 (contraction order as in ld_acc)
+                    R2 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 0, s, h32),
+                                ld_acc_t<IO>(Af, L::FLD, l32, 0, s, h32), R2);
+                f32x16 T21 = zero16();
 #pragma unroll
-            for (int m = 0; m < 16; ++m) a += Ar[m] * Dc[m * L::FLD];
-            Rs[x2 * 256 + i * 16 + j] = a;
-        }
-        __syncthreads();
+                for (int s = 0; s < S32; ++s)
+                    T21 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 32, s, h32), acc_frag<IO>(R2, s), T21);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {      // T_{2x+1,2x} = -Dinv_{2x+1} R
-            const int idx = tg + 256 * e, x2 = idx >> 8, i = (idx >> 4) & 15, j = idx & 15;
-            const float *Dr = Tf + (32 * x2 + 16 + i) * L::FLD + 32 * x2 + 16;
-            float a = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) a += Dr[m] * Rs[x2 * 256 + m * 16 + j];
-            Tf[(32 * x2 + 16 + i) * L::FLD + 32 * x2 + j] = -a;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {      // R2 = A_{21} T_{11}   (32x32 blocks)
-            const int idx = tg + 256 * e, i = idx >> 5, j = idx & 31;
-            const float *Ar = Tf + (32 + i) * L::FLD;
-            float a = 0.f;
-#pragma unroll
-            for (int m = 0; m < 32; ++m) a += Ar[m] * Tf[m * L::FLD + j];
-            rv[e] = a;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = tg + 256 * e;
-            Rs[(idx >> 5) * L::RLD + (idx & 31)] = rv[e];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {      // T_{21} = -T_{22} R2
-            const int idx = tg + 256 * e, i = idx >> 5, j = idx & 31;
-            const float *Tr = Tf + (32 + i) * L::FLD + 32;
-            float a = 0.f;
-#pragma unroll
-            for (int m = 0; m < 32; ++m) a += Tr[m] * Rs[m * L::RLD + j];
-            Tf[(32 + i) * L::FLD + j] = -a;
-        }
-        __syncthreads();
-        for (int idx = tg; idx < 3 * 1024; idx += 256) {   // T <- T diag(b), operand copy
-            const int blk = idx >> 10, w = idx & 1023;
-            const int i = 32 * (blk >= 1) + (w >> 5), j = 32 * (blk == 2) + (w & 31);
-            const float t = Tf[i * L::FLD + j] * bets[j];
-            if constexpr (BF) reinterpret_cast<bf16 *>(hbase + L::TB)[i * L::OLD + j] = (bf16)t;
-            else Tf[i * L::FLD + j] = t;
+                for (int rr = 0; rr < 16; ++rr) Ts[(32 + acc_row(rr, h32)) * L::OLD + l32] = (IO)(-T21[rr]);
+            }
         }
         __syncthreads();
 
-        // ---- phase 4: state products for this wave's 32 state rows.  Stages are
-        // ordered so that at most two 64x32 accumulator pairs are live at once.
-        frag sb[4][S32];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int s = 0; s < S32; ++s) sb[b][s] = acc_frag<IO>(S[b], s);
-        // Z = V - gamma * rk * (K S0^T)
+        // ---- [D] Vnew, output and state update for this wave's 32 state rows
         frag zb[2][S32];
+        {
+            frag sb[4][S32];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            float vreg[16];
+            for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 32 * ib + acc_row(r, h32);
-                vreg[r] = (i < Lc) ? (float)vg[(t0 + i) * p.v_st + (int64_t)h * p.v_sh + v0] : 0.f;
+                for (int s = 0; s < S32; ++s) sb[bb][s] = acc_frag<IO>(S[bb], s);
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                f32x16 X = zero16();
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int s = 0; s < S32; ++s)
+                        X = M::run(ld_acc<IO>(Ks, L::KLD, 32 * ib + l32, 32 * bb, s, h32), sb[bb][s], X);
+                // Z = b o (V - gamma rk (K S0^T))
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int i0 = 32 * ib + 8 * jj + 4 * h32;
+                    const f32x4 fz = ld4(rf(FZ_) + i0), fb = ld4(rf(FB_) + i0);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int rr = 4 * jj + t;
+                        X[rr] = (vreg_at(vcur, 16 * ib + rr, BF) - fz[t] * X[rr]) * fb[t];
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < S32; ++s) zb[ib][s] = acc_frag<IO>(X, s);
             }
-            f32x16 X = zero16();
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int s = 0; s < S32; ++s)
-                    X = M::run(ld_acc_order<IO>(Ks, L::KLD, 32 * ib + l32, 32 * b, s, h32), sb[b][s], X);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 32 * ib + acc_row(r, h32);
-                X[r] = vreg[r] - gams[i] * rks[i] * X[r];
-            }
-#pragma unroll
-            for (int s = 0; s < S32; ++s) zb[ib][s] = acc_frag<IO>(X, s);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // Vnew = T Z   (T lower block-triangular: skip the zero upper 32x32 block)
+        // Vnew = T' Z   (T' lower block-triangular: skip the zero upper 32x32 block)
         f32x16 Vn[2] = {zero16(), zero16()};
 #pragma unroll
         for (int s = 0; s < S32; ++s) {
-            Vn[0] = M::run(ld_acc_order<IO>(Top, TOLD, l32, 0, s, h32), zb[0][s], Vn[0]);
-            Vn[1] = M::run(ld_acc_order<IO>(Top, TOLD, 32 + l32, 0, s, h32), zb[0][s], Vn[1]);
-            Vn[1] = M::run(ld_acc_order<IO>(Top, TOLD, 32 + l32, 32, s, h32), zb[1][s], Vn[1]);
+            Vn[0] = M::run(ld_acc<IO>(Ts, L::OLD, l32, 0, s, h32), zb[0][s], Vn[0]);
+            Vn[1] = M::run(ld_acc<IO>(Ts, L::OLD, 32 + l32, 0, s, h32), zb[0][s], Vn[1]);
+            Vn[1] = M::run(ld_acc<IO>(Ts, L::OLD, 32 + l32, 32, s, h32), zb[1][s], Vn[1]);
         }
-        __builtin_amdgcn_sched_barrier(0);
         frag nb[2][S32];
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
             for (int s = 0; s < S32; ++s) nb[ib][s] = acc_frag<IO>(Vn[ib], s);
-        // O = scale [ gamma * rq * (Q S0^T) + P Vnew ], one 32-row block at a time
+        // O = scale [ gamma rq (Q S0^T) + P Vnew ]
+        {
+            constexpr int ES = (int)sizeof(IO);
+            const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * ES);
+            const int vo = 4 * h32 * p.o_st + v0 * ES;
+            auto store_rows = [&](const f32x16 &o, int ib, bool full) {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            f32x16 Y = zero16();
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int rofs = (32 * ib + 8 * (rr >> 2) + (rr & 3)) * p.o_st;
+                    if constexpr (BF) {
+                        const unsigned short x = __builtin_bit_cast(unsigned short, (bf16)(o[rr] * p.scale));
+                        if (full) __builtin_amdgcn_raw_buffer_store_b16(x, ro, vo, rofs, 0);
+                        else __builtin_amdgcn_raw_buffer_store_b16(x, ro, vo + rofs, 0, 0);
+                    } else {
+                        const uint32_t x = __builtin_bit_cast(uint32_t, o[rr] * p.scale);
+                        if (full) __builtin_amdgcn_raw_buffer_store_b32(x, ro, vo, rofs, 0);
+                        else __builtin_amdgcn_raw_buffer_store_b32(x, ro, vo + rofs, 0, 0);
+                    }
+                }
+            };
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
-                for (int s = 0; s < S32; ++s)
-                    Y = M::run(ld_acc_order<IO>(Qs, L::KLD, 32 * ib + l32, 32 * b, s, h32), sb[b][s], Y);
+                for (int jj = 0; jj < 4; ++jj) {
+                    const f32x4 fy = ld4(rf(FY_) + 32 * ib + 8 * jj + 4 * h32);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 32 * ib + acc_row(r, h32);
-                Y[r] *= gams[i] * rqs[i];
+                    for (int t = 0; t < 4; ++t) Y[ib][4 * jj + t] *= fy[t];
+                }
+#pragma unroll
+                for (int jb = 0; jb <= ib; ++jb)
+#pragma unroll
+                    for (int s = 0; s < S32; ++s)
+                        Y[ib] = M::run(ld_acc<IO>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), nb[jb][s], Y[ib]);
+                if (Lc == C) store_rows(Y[ib], ib, true);
+                else store_rows(Y[ib], ib, false);
             }
-#pragma unroll
-            for (int jb = 0; jb <= ib; ++jb)
-#pragma unroll
-                for (int s = 0; s < S32; ++s)
-                    Y = M::run(ld_acc_order<IO>(Pm, L::OLD, 32 * ib + l32, 32 * jb, s, h32), nb[jb][s], Y);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 32 * ib + acc_row(r, h32);
-                if (i < Lc) og[(t0 + i) * p.o_st + (int64_t)h * p.o_sh + v0] = (IO)(Y[r] * p.scale);
-            }
-            __builtin_amdgcn_sched_barrier(0);
         }
-        // S <- gamma_L S + K^T (rk * dec * Vnew)
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 32 * ib + acc_row(r, h32);
-                Vn[ib][r] *= rks[i] * decs[i];
-            }
+        // S~ <- S~ + K^T (FU o Vnew)  (sigma' carries the decay)
         frag ub[2][S32];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+        for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x4 fu = ld4(rf(FU_) + 32 * ib + 8 * jj + 4 * h32);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) Vn[ib][4 * jj + t] *= fu[t];
+            }
 #pragma unroll
             for (int s = 0; s < S32; ++s) ub[ib][s] = acc_frag<IO>(Vn[ib], s);
-        const float gL = gams[C - 1];
+        }
+        if (renorm) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+            for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[b][r] *= gL;
+                for (int rr = 0; rr < 16; ++rr) S[bb][rr] *= sig_next;
+            sigma = 1.f;
+        } else {
+            sigma = sig_next;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                 for (int s = 0; s < S32; ++s) {
                     frag a;
-                    if constexpr (BF) a = ld_acc_order<bf16>(KTs, L::TLD, 32 * b + l32, 32 * ib, s, h32);
-                    else a = ld_acc_order_t(reinterpret_cast<const float *>(Ks), L::KLD, 32 * b + l32, 32 * ib, s, h32);
-                    S[b] = M::run(a, ub[ib][s], S[b]);
+                    if constexpr (BF) a = ld_acc<bf16>(KTs, L::TLD, 32 * bb + l32, 32 * ib, s, h32);
+                    else a = ld_acc_t<float>(Ks, L::KLD, 32 * bb + l32, 32 * ib, s, h32);
+                    S[bb] = M::run(a, ub[ib][s], S[bb]);
                 }
         }
         __syncthreads();
@@ -542,35 +829,54 @@ __global__ __launch_bounds__(256 * RG) void fused_scan_kernel(const ScanParams p
 
     // ---- final state
     if (p.s_out) {
-        const int64_t base = (int64_t)n * p.so_n + (int64_t)h * p.so_h + (int64_t)v0 * p.so_v;
+        if (sigma != 1.f) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k0 = 32 * b + 8 * j + 4 * h32;
+                for (int rr = 0; rr < 16; ++rr) S[bb][rr] *= sigma;
+        }
+        const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
+        const int h32 = lane >> 5, v0 = ws * 32 + (lane & 31);
+        const auto rs = rsrc(p.s_out + n * p.so_n + h * p.so_h, (int64_t)D * p.so_v);
+        if (p.so_dt == GDN_F32) {
+            const int vo = v0 * p.so_v + 16 * h32;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float x = S[b][4 * j + t];
-                    if (p.so_dt == GDN_F32) static_cast<float *>(p.s_out)[base + k0 + t] = x;
-                    else static_cast<bf16 *>(p.s_out)[base + k0 + t] = (bf16)x;
+            for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f32x4 x;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) x[t] = S[bb][4 * j + t];
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), rs, vo + 4 * (32 * bb + 8 * j), 0, 0);
                 }
-            }
+        } else {
+            const int vo = v0 * p.so_v + 8 * h32;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    bf16x4 x;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) x[t] = (bf16)S[bb][4 * j + t];
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), rs, vo + 2 * (32 * bb + 8 * j), 0, 0);
+                }
+        }
     }
 }
 
-template <typename IO, int RG>
+template <typename IO>
 hipError_t launch(const ScanParams &p, hipStream_t stream) {
-    const int64_t blocks = (int64_t)p.N * (p.Hv / RG);
+    const int64_t pairs = (int64_t)p.N * p.Hqk;
+    const int64_t blocks = ((pairs + 7) / 8) * 8 * p.r;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((fused_scan_kernel<IO, RG>), dim3((unsigned)blocks), dim3(256 * RG), 0, stream, p);
+    hipLaunchKernelGGL((fused_scan_kernel<IO>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, int rg, hipStream_t stream) {
-    if (io_bf16) return rg == 2 ? launch<bf16, 2>(p, stream) : launch<bf16, 1>(p, stream);
-    return launch<float, 1>(p, stream);
+hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, hipStream_t stream) {
+    return io_bf16 ? launch<bf16>(p, stream) : launch<float>(p, stream);
 }
 
 }  // namespace gdn

@@ -1,0 +1,159 @@
+"""GPU invariants of the scan through the C ABI: API identities, batch
+invariance, determinism, strided views, state chaining and edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_workloads as W
+from _harness import BF16_TOL, F32_TOL, nerr, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def _w(lengths=(100, 37, 64), Hqk=2, Hv=4, dtype=torch.bfloat16, seed=21, **kw):
+    return W.build(list(lengths), Hqk, Hv, dtype, seed=seed, **kw)
+
+
+def test_api_defaults_are_bitwise(gdn):
+    """g = None == all ones; beta = None == all ones; scale 0 == 1/sqrt(128)."""
+    w = _w()
+    say("[gpu] api defaults")
+    o1, f1 = run_gpu(gdn, W.Workload(**{**w.__dict__, "g": None, "beta": None}), True)
+    ones = torch.ones_like(w.g)
+    o2, f2 = run_gpu(gdn, W.Workload(**{**w.__dict__, "g": ones, "beta": ones.clone()}), True)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    o3, f3 = run_gpu(gdn, W.Workload(**{**w.__dict__, "scale": 1.0 / np.sqrt(128.0)}), True)
+    o4, f4 = run_gpu(gdn, w, True)
+    assert torch.equal(o3, o4) and torch.equal(f3, f4)
+
+
+def test_run_to_run_bitwise(gdn):
+    w = _w(seed=22)
+    say("[gpu] run-to-run determinism")
+    o1, f1 = run_gpu(gdn, w, True)
+    o2, f2 = run_gpu(gdn, w, True)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_batch_invariance_bitwise(gdn, dtype):
+    """With batch_invariant a sequence's output and state do not depend on the
+    rest of the batch or on its position in it."""
+    lens = [150, 3, 77, 0, 64]
+    w = W.build(lens, 2, 4, dtype, seed=23)
+    say(f"[gpu] batch invariance {dtype}")
+    out, fin = run_gpu(gdn, w, True)
+    cu = w.cu_seqlens.tolist()
+    for n in (0, 2, 4):
+        sub = W.slice_item(w, n, range(w.Hv))
+        sub = W.Workload(**{**sub.__dict__, "q": w.q[cu[n]:cu[n + 1]], "k": w.k[cu[n]:cu[n + 1]]})
+        o1, f1 = run_gpu(gdn, sub, True)
+        assert torch.equal(o1, out[cu[n]:cu[n + 1]]), n
+        assert torch.equal(f1[0], fin[n]), n
+    # the same sequences in reverse order
+    order = list(reversed(range(len(lens))))
+    rev = W.Workload(
+        "rev", torch.cat([w.q[cu[n]:cu[n + 1]] for n in order]), torch.cat([w.k[cu[n]:cu[n + 1]] for n in order]),
+        torch.cat([w.v[cu[n]:cu[n + 1]] for n in order]), torch.cat([w.g[cu[n]:cu[n + 1]] for n in order]),
+        torch.cat([w.beta[cu[n]:cu[n + 1]] for n in order]),
+        torch.tensor([0] + list(np.cumsum([lens[n] for n in order])), dtype=torch.int64),
+        w.initial_state[order].contiguous(), w.state_dtype, w.use_qk_l2norm)
+    o2, f2 = run_gpu(gdn, rev, True)
+    cu2 = rev.cu_seqlens.tolist()
+    for pos, n in enumerate(order):
+        assert torch.equal(o2[cu2[pos]:cu2[pos + 1]], out[cu[n]:cu[n + 1]])
+        assert torch.equal(f2[pos], fin[n])
+
+
+def test_strided_views_of_fused_qkv(gdn):
+    """q, k, v as views into one fused [T, 2*Hqk + Hv, 128] buffer (token stride
+    larger than the tensor's own row) give bitwise the contiguous result."""
+    w = _w(seed=24)
+    say("[gpu] strided q/k/v views")
+    T, Hqk, Hv = w.T, w.Hqk, w.Hv
+    fused = torch.empty(T, 2 * Hqk + Hv, 128, dtype=w.q.dtype)
+    fused[:, :Hqk] = w.q
+    fused[:, Hqk:2 * Hqk] = w.k
+    fused[:, 2 * Hqk:] = w.v
+    fd = fused.to(DEV)
+    sv = W.Workload(**{**w.to(DEV).__dict__, "q": fd[:, :Hqk], "k": fd[:, Hqk:2 * Hqk], "v": fd[:, 2 * Hqk:]})
+    assert sv.q.stride(0) == (2 * Hqk + Hv) * 128 and not sv.q.is_contiguous()
+    o1, f1 = run_gpu(gdn, sv, True)
+    o2, f2 = run_gpu(gdn, w, True)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_cu_seqlens_int32_equals_int64(gdn):
+    w = _w(seed=25)
+    say("[gpu] int32 vs int64 cu_seqlens")
+    o1, f1 = run_gpu(gdn, W.Workload(**{**w.__dict__, "cu_seqlens": w.cu_seqlens.to(torch.int32)}), True)
+    o2, f2 = run_gpu(gdn, W.Workload(**{**w.__dict__, "cu_seqlens": w.cu_seqlens.to(torch.int64)}), True)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, BF16_TOL), (torch.float32, F32_TOL)])
+def test_state_chaining_matches_whole(gdn, dtype, tol):
+    """Two calls passing the fp32 state (split inside a chunk) match one call."""
+    w = W.build([300], 2, 4, dtype, seed=26, gate="long")
+    say(f"[gpu] state chaining {dtype}")
+    out, fin = run_gpu(gdn, w, True)
+    cut = 141
+    a = W.Workload(**{**w.__dict__, "q": w.q[:cut], "k": w.k[:cut], "v": w.v[:cut], "g": w.g[:cut],
+                      "beta": w.beta[:cut], "cu_seqlens": torch.tensor([0, cut])})
+    oa, fa = run_gpu(gdn, a, True)
+    b = W.Workload(**{**w.__dict__, "q": w.q[cut:], "k": w.k[cut:], "v": w.v[cut:], "g": w.g[cut:],
+                      "beta": w.beta[cut:], "cu_seqlens": torch.tensor([0, 300 - cut]),
+                      "initial_state": fa.cpu()})
+    ob, fb = run_gpu(gdn, b, True)
+    ro, rf = run_oracle(w)
+    assert nerr(torch.cat([oa, ob]), ro) <= tol and nerr(fb, rf) <= tol
+    assert nerr(torch.cat([oa, ob]).float(), out.float().cpu().numpy()) <= tol
+
+
+def test_zero_gate_resets_state(gdn):
+    """a_t = 0 (hard reset) inside a chunk: finite and matching the oracle."""
+    w = _w(lengths=(130,), seed=27)
+    g = w.g.clone()
+    g[[5, 70, 129]] = 0.0
+    w = W.Workload(**{**w.__dict__, "g": g})
+    say("[gpu] zero gates")
+    out, fin = run_gpu(gdn, w, True)
+    ro, rf = run_oracle(w)
+    assert torch.isfinite(out).all() and torch.isfinite(fin).all()
+    assert nerr(out, ro) <= BF16_TOL and nerr(fin, rf) <= BF16_TOL
+
+
+def test_strong_decay_slow_path(gdn):
+    """Gates small enough that a chunk's total log-decay passes -60 (entry-wise
+    exp path) still match the oracle."""
+    w = _w(lengths=(200, 64), seed=28)
+    w = W.Workload(**{**w.__dict__, "g": torch.full_like(w.g, 0.2)})
+    say("[gpu] strong decay")
+    out, fin = run_gpu(gdn, w, True)
+    ro, rf = run_oracle(w)
+    assert nerr(out, ro) <= BF16_TOL and nerr(fin, rf) <= BF16_TOL
+
+
+def test_bf16_gates_and_fp16_gate(gdn):
+    w = _w(seed=29)
+    say("[gpu] gate dtypes")
+    ref = run_gpu(gdn, w, True)
+    for gdt in (torch.bfloat16, torch.float16):
+        w2 = W.Workload(**{**w.__dict__, "g": w.g.to(gdt), "beta": w.beta.to(torch.bfloat16)})
+        out, fin = run_gpu(gdn, w2, True)
+        ro, rf = run_oracle(w2)
+        assert nerr(out, ro) <= BF16_TOL and nerr(fin, rf) <= BF16_TOL
+    del ref
+
+
+def test_no_output_state_writes_nothing_else(gdn):
+    w = _w(seed=30)
+    say("[gpu] output_state NULL")
+    wd = w.to(DEV)
+    out = torch.full((w.T, w.Hv, 128), 7.0, dtype=w.q.dtype, device=DEV)
+    gdn.gdn_chunk_prefill(wd.q, wd.k, wd.v, wd.g, wd.beta, 0.0, wd.cu_seqlens, wd.initial_state, None,
+                          True, True, out)
+    torch.cuda.synchronize()
+    ro, _ = run_oracle(w)
+    assert nerr(out, ro) <= BF16_TOL
