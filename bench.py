@@ -16,7 +16,8 @@ Algorithmic work (chunk length 64, whatever the kernels use internally):
 
 Other modes (used to produce the committed rocprofv3 summaries):
   --copy-calibration   a plain device copy of known size (for PMC scaling)
-  --summarize-pmc DIR  turn rocprofv3 --pmc outputs into profiles/*.txt
+  --summarize-pmc DIR  turn rocprofv3 --pmc outputs (rocpd .db) into profiles/*.txt
+  --summarize-trace DIR OUT  kernel-trace statistics (rocpd .db) into a text summary
 """
 import argparse
 import glob
@@ -111,41 +112,66 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}))
 
 
-def _pmc_rows(d):
-    import csv
+def _db_files(d):
+    return sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+
+
+def _pmc_values(d, name_part, counter):
+    """Per-dispatch values of `counter` for kernels whose name contains
+    name_part, from rocprofv3's rocpd database(s) under d."""
+    import sqlite3
+    vals = {}
+    for f in _db_files(d):
+        con = sqlite3.connect(f)
+        for disp, kname, cname, v in con.execute(
+                "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+            if name_part in kname and cname == counter:
+                vals[(f, disp)] = vals.get((f, disp), 0.0) + float(v)
+        con.close()
+    return list(vals.values())
+
+
+def _kernel_stats(d):
+    """(name, calls, average ns, total ns, percent) rows from rocprofv3 --kernel-trace."""
+    import sqlite3
     rows = []
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
-        with open(f) as fh:
-            rows += list(csv.DictReader(fh))
+    for f in _db_files(d):
+        con = sqlite3.connect(f)
+        rows += con.execute("select name, total_calls, average, total_duration, percentage from top_kernels").fetchall()
+        con.close()
     return rows
 
 
-def _per_dispatch(rows, name_part, counter):
-    vals = {}
-    for r in rows:
-        if name_part in r.get("Kernel_Name", "") and r.get("Counter_Name") == counter:
-            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
-            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-    return list(vals.values())
+def summarize_trace(base, out_path, command):
+    rows = _kernel_stats(base)
+    lines = [f"# rocprofv3 --kernel-trace --stats summary (rocpd top_kernels; durations in microseconds)",
+             f"# command: {command}",
+             "# kernel | calls | average_us | total_us | percent"]
+    for name, calls, avg, tot, pct in rows[:12]:
+        short = name.replace("(anonymous namespace)", "anon").replace("void ", "")
+        short = short[:short.rfind("(")] if "(" in short else short
+        lines.append(f"{short[:100]} | {calls} | {avg:.3f} | {tot:.1f} | {pct:.2f}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes):
     """Reads four rocprofv3 --pmc output dirs (kernel FETCH_SIZE, WRITE_SIZE;
     copy FETCH_SIZE, WRITE_SIZE) and writes the traffic summary file."""
-    kf = _per_dispatch(_pmc_rows(os.path.join(base, "pmc_fetch")), KERNEL, "FETCH_SIZE")
-    kw = _per_dispatch(_pmc_rows(os.path.join(base, "pmc_write")), KERNEL, "WRITE_SIZE")
-    cf = _per_dispatch(_pmc_rows(os.path.join(base, "pmc_copy_fetch")), "", "FETCH_SIZE")
-    cw = _per_dispatch(_pmc_rows(os.path.join(base, "pmc_copy_write")), "", "WRITE_SIZE")
+    kf = _pmc_values(os.path.join(base, "pmc_fetch"), KERNEL, "FETCH_SIZE")
+    kw = _pmc_values(os.path.join(base, "pmc_write"), KERNEL, "WRITE_SIZE")
+    cf = _pmc_values(os.path.join(base, "pmc_copy_fetch"), "copyBuffer", "FETCH_SIZE")
+    cw = _pmc_values(os.path.join(base, "pmc_copy_write"), "copyBuffer", "WRITE_SIZE")
     copy_bytes = float(1 << 30)
     # counters are KiB per dispatch; the copy reads and writes copy_bytes once
-    f_fac = copy_bytes / (max(cf) * 1024.0)
-    w_fac = copy_bytes / (max(cw) * 1024.0)
+    f_fac = copy_bytes / (statistics.median(cf) * 1024.0)
+    w_fac = copy_bytes / (statistics.median(cw) * 1024.0)
     fetch = statistics.median(kf) * 1024.0 * f_fac
     write = statistics.median(kw) * 1024.0 * w_fac
     lines = [
         "# HBM traffic of fused_scan_kernel, large_batch workload (32 x 8192 tokens, Hqk 16, Hv 32, bf16)",
-        "# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by the same counters",
-        "# read for a plain 1 GiB device copy (bench.py --copy-calibration).",
+        "# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the same counter",
+        "# read for a plain 1 GiB device-to-device copy (bench.py --copy-calibration).",
         f"# kernel FETCH_SIZE command: {cmd_fetch}",
         f"# kernel WRITE_SIZE command: {cmd_write}",
         f"# copy FETCH_SIZE command:   {cmd_cf}",
@@ -155,8 +181,8 @@ def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes):
         f"dispatches_write = {len(kw)}",
         f"raw_fetch_kib_median = {statistics.median(kf):.1f}",
         f"raw_write_kib_median = {statistics.median(kw):.1f}",
-        f"copy_fetch_kib = {max(cf):.1f}",
-        f"copy_write_kib = {max(cw):.1f}",
+        f"copy_fetch_kib = {statistics.median(cf):.1f}",
+        f"copy_write_kib = {statistics.median(cw):.1f}",
         f"fetch_scale = {f_fac:.4f}",
         f"write_scale = {w_fac:.4f}",
         f"fetch_bytes_per_launch = {fetch:.0f}",
@@ -178,11 +204,13 @@ def main():
     ap.add_argument("--workload", default="large_batch")
     ap.add_argument("--variant", default=None)
     ap.add_argument("--batch-invariant", type=int, default=0)
-    ap.add_argument("--cpu-sample-seqs", type=int, default=4)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", default=None)
     ap.add_argument("--pmc-commands", default="{}")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"), default=None)
+    ap.add_argument("--trace-command", default="?")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -192,6 +220,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_command)
         return
 
     import torch
