@@ -10,8 +10,10 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
+#include <utility>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -85,10 +87,13 @@ bool aligned16(const void *p, size_t esz, const int64_t *strides, int n) {
     return true;
 }
 
+constexpr int64_t kMinSegment = 1024;   // shortest segment of the split path (16 chunks)
+
 std::mutex g_dev_mu;
 int g_dev_checked[64];   // 0 unknown, 1 gfx950, 2 other
+int g_dev_cus[64];
 
-int check_device(std::string &msg) {
+int check_device(std::string &msg, int *dev_out, int *cus_out) {
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
         (void)hipGetLastError();
@@ -110,6 +115,7 @@ int check_device(std::string &msg) {
             return GDN_ERR_HIP;
         }
         g_dev_checked[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_cus[dev] = prop.multiProcessorCount;
         if (g_dev_checked[dev] == 2) {
             msg = std::string("device ") + std::to_string(dev) + " is " + prop.gcnArchName +
                   "; this library is built for gfx950 only";
@@ -120,14 +126,67 @@ int check_device(std::string &msg) {
         msg = "current device is not gfx950";
         return GDN_ERR_ARCH;
     }
+    *dev_out = dev;
+    *cus_out = (dev >= 0 && dev < 64 && g_dev_cus[dev] > 0) ? g_dev_cus[dev] : 256;
     return GDN_OK;
 }
+
+// Workspace of the split path: cached per (device, stream), grown on demand.
+// Growing synchronises the stream once (the old buffer may still be in use);
+// after a warm-up call of the largest shape no call allocates.
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(int dev, hipStream_t st, size_t need, void **out, std::string &msg) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace &w = g_ws[{dev, st}];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            if (hipStreamSynchronize(st) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
+                (void)hipGetLastError();
+                msg = "workspace release failed";
+                return GDN_ERR_HIP;
+            }
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        if (hipMalloc(&w.ptr, need) != hipSuccess) {
+            (void)hipGetLastError();
+            w.ptr = nullptr;
+            msg = "workspace allocation of " + std::to_string(need) + " bytes failed";
+            return GDN_ERR_HIP;
+        }
+        w.bytes = need;
+    }
+    *out = w.ptr;
+    return GDN_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
 extern "C" const char *gdn_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" void gdn_release_workspace(void) {}
+extern "C" void gdn_release_workspace(void) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    for (auto &kv : g_ws) {
+        if (kv.second.ptr) {
+            int cur = 0;
+            (void)hipGetDevice(&cur);
+            (void)hipSetDevice(kv.first.first);
+            (void)hipStreamSynchronize(kv.first.second);
+            (void)hipFree(kv.second.ptr);
+            (void)hipSetDevice(cur);
+        }
+    }
+    g_ws.clear();
+    (void)hipGetLastError();
+}
 
 extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
                                  const gdn_tensor *g, const gdn_tensor *beta, float scale,
@@ -234,7 +293,8 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
     if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale must be finite");
 
     // ---- device
-    if ((rc = check_device(msg))) return fail(rc, msg);
+    int dev = 0, cus = 256;
+    if ((rc = check_device(msg, &dev, &cus))) return fail(rc, msg);
     if (N == 0) return GDN_OK;
 
     gdn::ScanParams p{};
@@ -273,10 +333,53 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
     p.scale = scale == 0.0f ? 1.0f / std::sqrt((float)gdn::kHeadDim) : scale;
     p.N = (int32_t)N; p.Hqk = (int32_t)Hqk; p.Hv = (int32_t)Hv; p.r = (int32_t)(Hv / Hqk);
     p.l2norm = use_qk_l2norm != 0;
-    (void)batch_invariant;   // the fused scan never splits a sequence
-
     const bool bf = io == GDN_BF16;
-    hipError_t e = gdn::launch_fused_scan(p, bf, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+
+    // Split path (T precompute -> MN precompute -> state fixup -> CP prefill) when
+    // one work item per (sequence, head) leaves the GPU under-filled.  Never with
+    // batch_invariant (the split changes the reduction order of a sequence).
+    const int64_t fill = 2 * (int64_t)cus;
+    int64_t lseg = 0;
+    if (!batch_invariant && N * Hv < fill && T > 0) {
+        lseg = (T * Hv + fill - 1) / fill;
+        lseg = (lseg + gdn::kChunk - 1) / gdn::kChunk * gdn::kChunk;
+        if (lseg < kMinSegment) lseg = kMinSegment;
+        if (lseg >= T) lseg = 0;   // no sequence is long enough to split
+    }
+    hipError_t e;
+    if (lseg == 0) {
+        e = gdn::launch_fused_scan(p, bf, gdn::kScan, hs);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return GDN_OK;
+    }
+    const int64_t cap = T / lseg + N + 1;
+    const size_t seg_bytes = align_up((size_t)cap * sizeof(gdn::SegEntry), 256);
+    const size_t first_bytes = align_up((size_t)(N + 2) * sizeof(int32_t), 256);
+    const size_t map_bytes = (size_t)cap * (size_t)Hv * gdn::kHeadDim * gdn::kHeadDim * sizeof(float);
+    void *wsp = nullptr;
+    if ((rc = get_workspace(dev, hs, seg_bytes + first_bytes + 3 * map_bytes, &wsp, msg))) return fail(rc, msg);
+    char *w = static_cast<char *>(wsp);
+    gdn::SegEntry *segs = reinterpret_cast<gdn::SegEntry *>(w);
+    int32_t *seg_first = reinterpret_cast<int32_t *>(w + seg_bytes);
+    int32_t *nsegs = seg_first + (N + 1);
+    p.segs = segs;
+    p.nsegs = nsegs;
+    p.seg_cap = (int32_t)cap;
+    p.ws_n = reinterpret_cast<float *>(w + seg_bytes + first_bytes);
+    p.ws_m = reinterpret_cast<float *>(w + seg_bytes + first_bytes + map_bytes);
+    p.ws_sin = reinterpret_cast<float *>(w + seg_bytes + first_bytes + 2 * map_bytes);
+    gdn::FixParams f{};
+    f.segs = segs;
+    f.seg_first = seg_first;
+    f.s_in = p.s_in; f.si_n = p.si_n; f.si_h = p.si_h; f.si_v = p.si_v; f.si_dt = p.si_dt;
+    f.ws_n = p.ws_n; f.ws_m = p.ws_m; f.ws_sin = p.ws_sin;
+    f.N = (int32_t)N; f.Hv = (int32_t)Hv;
+    if ((e = gdn::launch_plan(p.cu, p.cu_i64, (int)N, lseg, segs, nsegs, seg_first, (int)cap, hs)) != hipSuccess ||
+        (e = gdn::launch_fused_scan(p, bf, gdn::kMapN, hs)) != hipSuccess ||
+        (e = gdn::launch_fused_scan(p, bf, gdn::kMapM, hs)) != hipSuccess ||
+        (e = gdn::launch_fixup(f, hs)) != hipSuccess ||
+        (e = gdn::launch_fused_scan(p, bf, gdn::kScan, hs)) != hipSuccess)
+        return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return GDN_OK;
 }

@@ -12,6 +12,19 @@ namespace gdn {
 constexpr int kHeadDim = 128;   // K = V = 128 (every shape on the API page)
 constexpr int kChunk = 64;      // tokens per chunk, aligned to each sequence start
 
+// One work item of the split path: a run of whole chunks of one sequence.
+struct SegEntry {
+    int64_t bos, eos;          // token range [bos, eos)
+    int32_t n;                 // sequence
+    int32_t first, last;       // first / last segment of its sequence
+    int32_t pad;
+};
+
+// Kernel modes: the scan proper, or one of the two segment maps of the split
+// path (S_end = S_start M + N): N = scan from a zero state, M = scan of the
+// identity with v = 0.  Map modes write no output rows.
+enum ScanMode { kScan = 0, kMapN = 1, kMapM = 2 };
+
 // Everything one scan launch needs.  Per-row strides are in bytes and fit in
 // 32 bits with 64 rows of headroom (the host checks); per-head and
 // per-sequence strides are 64-bit.
@@ -39,10 +52,35 @@ struct ScanParams {
     float scale;
     int32_t N, Hqk, Hv, r;          // r = Hv / Hqk
     int32_t l2norm;
+    // split path (segs == nullptr: one work item per sequence)
+    const SegEntry *segs;
+    const int32_t *nsegs;           // number of valid entries (device)
+    int32_t seg_cap;                // entries the grid covers
+    float *ws_n, *ws_m, *ws_sin;    // [seg_cap][Hv][128][128] fp32, V-major
 };
 
-// Fused chunked scan: one workgroup per (sequence, value head).  io_bf16
-// selects bf16 q/k/v/out (bf16 MFMA) or fp32 (fp32 MFMA).
-hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, hipStream_t stream);
+// Fix-up of the split path: per (sequence, value head), serially over its
+// segments, S_in(i+1) = S_in(i) M_i + N_i.
+struct FixParams {
+    const SegEntry *segs;
+    const int32_t *seg_first;       // [N + 1] first segment of each sequence
+    const char *s_in;               // caller's initial state (nullptr: zero)
+    int64_t si_n, si_h;
+    int32_t si_v, si_dt;
+    const float *ws_n, *ws_m;
+    float *ws_sin;
+    int32_t N, Hv;
+};
+
+// Fused chunked scan: one workgroup per (sequence or segment, value head).
+// io_bf16 selects bf16 q/k/v/out (bf16 MFMA) or fp32 (fp32 MFMA).
+hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, int mode, hipStream_t stream);
+
+// Split plan: cu_seqlens -> segment table of at most `cap` entries of `lseg`
+// tokens (a multiple of the chunk), one entry for an empty sequence.
+hipError_t launch_plan(const void *cu, int cu_i64, int N, int64_t lseg, SegEntry *segs, int32_t *nsegs,
+                       int32_t *seg_first, int cap, hipStream_t stream);
+
+hipError_t launch_fixup(const FixParams &f, hipStream_t stream);
 
 }  // namespace gdn

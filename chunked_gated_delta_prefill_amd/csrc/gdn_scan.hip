@@ -370,12 +370,72 @@ __device__ __forceinline__ ChunkRef chunk_at(int64_t bos, int64_t eos, int c) {
     return ch;
 }
 
+// ---- state I/O: accumulator tiles S[b] (S^T rows k = 32b + acc_row(r, h32),
+// column v0) <-> a V-major [128][128] block at `base` with row stride `rs` bytes.
+__device__ __forceinline__ void load_state(f32x16 (&S)[4], const char *base, int rs, int dt, int v0, int h32) {
+    const auto r = rsrc(base, (int64_t)D * rs);
+    if (dt == GDN_F32) {
+        const int vo = v0 * rs + 16 * h32;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 x =
+                    __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vo + 4 * (32 * bb + 8 * j), 0, 0));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = x[t];
+            }
+    } else {
+        const int vo = v0 * rs + 8 * h32;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x4 x =
+                    __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, vo + 2 * (32 * bb + 8 * j), 0, 0));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = (float)x[t];
+            }
+    }
+}
+
+__device__ __forceinline__ void store_state(const f32x16 (&S)[4], char *base, int rs, int dt, int v0, int h32) {
+    const auto r = rsrc(base, (int64_t)D * rs);
+    if (dt == GDN_F32) {
+        const int vo = v0 * rs + 16 * h32;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f32x4 x;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = S[bb][4 * j + t];
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, vo + 4 * (32 * bb + 8 * j), 0, 0);
+            }
+    } else {
+        const int vo = v0 * rs + 8 * h32;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 x;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = (bf16)S[bb][4 * j + t];
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, vo + 2 * (32 * bb + 8 * j), 0, 0);
+            }
+    }
+}
+
+constexpr int64_t kMapBytes = (int64_t)D * D * 4;   // one fp32 [128][128] block of the workspace
+
 // bf16: two workgroups per CU (LDS < 80 KB) need <= 256 registers per lane;
 // fp32 (LDS-bound to one workgroup per CU) keeps the full register file.
-template <typename IO>
+template <typename IO, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(is_bf<IO>::value ? 2 : 1,
                                                                     is_bf<IO>::value ? 2 : 1))) void
 fused_scan_kernel(const ScanParams p) {
+    constexpr bool OUT = MODE == kScan;     // map modes produce no output rows
+    constexpr bool HASV = MODE != kMapM;    // the M map scans v = 0
     using L = Smem<IO>;
     using M = Mma<IO>;
     using frag = typename M::frag;
@@ -399,10 +459,28 @@ fused_scan_kernel(const ScanParams p) {
     const int b = blockIdx.x;
     const int within = b % (8 * r);
     const int pidx = (b / (8 * r)) * 8 + (within & 7);
-    if (pidx >= p.N * p.Hqk) return;
-    const int n = pidx / p.Hqk, hq = pidx % p.Hqk;
+    const int items = p.segs ? p.seg_cap : p.N;
+    if (pidx >= items * p.Hqk) return;
+    const int item = pidx / p.Hqk, hq = pidx % p.Hqk;
     const int h = hq * r + (within >> 3);
-    const int64_t bos = load_cu(p.cu, n, p.cu_i64), eos = load_cu(p.cu, n + 1, p.cu_i64);
+    int n;
+    int64_t bos, eos;
+    bool first = true, last = true;
+    if (p.segs) {
+        if (item >= *p.nsegs) return;
+        const SegEntry e = p.segs[item];
+        n = e.n;
+        bos = e.bos;
+        eos = e.eos;
+        first = e.first != 0;
+        last = e.last != 0;
+        if (MODE != kScan && last) return;   // maps are needed for all but the last segment
+    } else {
+        n = item;
+        bos = load_cu(p.cu, n, p.cu_i64);
+        eos = load_cu(p.cu, n + 1, p.cu_i64);
+    }
+    const int64_t map_off = ((int64_t)item * p.Hv + h) * kMapBytes;
 
     // ---- initial state: S[b] holds S^T rows k = 32b + acc_row(r, h32), column v0
     f32x16 S[4];
@@ -411,31 +489,16 @@ fused_scan_kernel(const ScanParams p) {
     {
         const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
         const int h32 = lane >> 5, v0 = ws * 32 + (lane & 31);
-        if (p.s_in) {
-            const auto rs = rsrc(p.s_in + n * p.si_n + h * p.si_h, (int64_t)D * p.si_v);
-            if (p.si_dt == GDN_F32) {
-                const int vo = v0 * p.si_v + 16 * h32;
+        if (MODE == kScan) {
+            if (!first)
+                load_state(S, reinterpret_cast<const char *>(p.ws_sin) + map_off, D * 4, GDN_F32, v0, h32);
+            else if (p.s_in)
+                load_state(S, p.s_in + n * p.si_n + h * p.si_h, p.si_v, p.si_dt, v0, h32);
+        } else if (MODE == kMapM) {           // identity: S^T[k][v0] = (k == v0)
 #pragma unroll
-                for (int bb = 0; bb < 4; ++bb)
+            for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const f32x4 x = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo + 4 * (32 * bb + 8 * j), 0, 0));
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = x[t];
-                    }
-            } else {
-                const int vo = v0 * p.si_v + 8 * h32;
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const bf16x4 x = __builtin_bit_cast(
-                            bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rs, vo + 2 * (32 * bb + 8 * j), 0, 0));
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = (float)x[t];
-                    }
-            }
+                for (int rr = 0; rr < 16; ++rr) S[bb][rr] = (32 * bb + acc_row(rr, h32) == v0) ? 1.f : 0.f;
         }
     }
 
@@ -459,7 +522,11 @@ fused_scan_kernel(const ScanParams p) {
 
         // ---- [L] stage K, K^T, Q and row norms; gates and the in-chunk log-gate cumsum
         VRegs vcur;
-        issue_v<IO>(vcur, p, ch, h, h32, v0);
+        if constexpr (HASV) issue_v<IO>(vcur, p, ch, h, h32, v0);
+        else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) vcur.x[e] = 0u;
+        }
         if constexpr (BF) {
             const int rq4 = tid >> 4, cg = tid & 15;
 #pragma unroll
@@ -546,7 +613,7 @@ fused_scan_kernel(const ScanParams p) {
         }
         (void)g_G;
         f32x16 Y[2] = {zero16(), zero16()};
-        {
+        if constexpr (OUT) {
             frag sb[4][S32];
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
@@ -565,7 +632,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tile = ws + 4 * u;
-            if (tile < 6) {
+            if (tile < (OUT ? 6 : 3)) {
                 const int isq = tile >= 3, tt = tile - 3 * isq;
                 const int bi = tt > 0, bj = tt == 2;
                 const IO *As = isq ? Qs : Ks;
@@ -582,7 +649,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tile = ws + 4 * u;
-            if (tile < 6) {
+            if (tile < (OUT ? 6 : 3)) {
                 const int isq = tile >= 3, tt = tile - 3 * isq;
                 const int bi = tt > 0, bj = tt == 2;
                 const int j = 32 * bj + l32;
@@ -748,6 +815,7 @@ fused_scan_kernel(const ScanParams p) {
             Vn[1] = M::run(ld_acc<IO>(Ts, L::OLD, 32 + l32, 0, s, h32), zb[0][s], Vn[1]);
             Vn[1] = M::run(ld_acc<IO>(Ts, L::OLD, 32 + l32, 32, s, h32), zb[1][s], Vn[1]);
         }
+        if constexpr (OUT) {
         frag nb[2][S32];
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
@@ -791,6 +859,7 @@ fused_scan_kernel(const ScanParams p) {
             }
         }
         // S~ <- S~ + K^T (FU o Vnew)  (sigma' carries the decay)
+        }
         frag ub[2][S32];
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
@@ -827,8 +896,10 @@ fused_scan_kernel(const ScanParams p) {
         __syncthreads();
     }
 
-    // ---- final state
-    if (p.s_out) {
+    // ---- final state (scan: the caller's output state, by the last segment only;
+    // maps: the workspace)
+    const bool write_caller = MODE == kScan && last && p.s_out;
+    if (write_caller || MODE != kScan) {
         if (sigma != 1.f) {
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
@@ -837,46 +908,145 @@ fused_scan_kernel(const ScanParams p) {
         }
         const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
         const int h32 = lane >> 5, v0 = ws * 32 + (lane & 31);
-        const auto rs = rsrc(p.s_out + n * p.so_n + h * p.so_h, (int64_t)D * p.so_v);
-        if (p.so_dt == GDN_F32) {
-            const int vo = v0 * p.so_v + 16 * h32;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f32x4 x;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) x[t] = S[bb][4 * j + t];
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), rs, vo + 4 * (32 * bb + 8 * j), 0, 0);
-                }
-        } else {
-            const int vo = v0 * p.so_v + 8 * h32;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf16x4 x;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) x[t] = (bf16)S[bb][4 * j + t];
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), rs, vo + 2 * (32 * bb + 8 * j), 0, 0);
-                }
-        }
+        if (MODE == kScan)
+            store_state(S, p.s_out + n * p.so_n + h * p.so_h, p.so_v, p.so_dt, v0, h32);
+        else
+            store_state(S, reinterpret_cast<char *>(MODE == kMapN ? p.ws_n : p.ws_m) + map_off, D * 4, GDN_F32, v0,
+                        h32);
     }
 }
 
-template <typename IO>
+// ------------------------------------------------------------ split path --
+// Plan: cu_seqlens -> segment table.  One workgroup; sequences in tiles of 256
+// with a block-wide inclusive scan of their segment counts.
+__global__ __launch_bounds__(256) void plan_kernel(const void *cu, int cu_i64, int N, int64_t lseg, SegEntry *segs,
+                                                   int32_t *nsegs, int32_t *seg_first, int cap) {
+    __shared__ int32_t part[256];
+    const int tid = threadIdx.x;
+    int base = 0;
+    for (int n0 = 0; n0 < N; n0 += 256) {
+        const int n = n0 + tid;
+        int cnt = 0;
+        int64_t bos = 0, eos = 0;
+        if (n < N) {
+            bos = load_cu(cu, n, cu_i64);
+            eos = load_cu(cu, n + 1, cu_i64);
+            const int64_t len = eos - bos;
+            cnt = len <= 0 ? 1 : (int)((len + lseg - 1) / lseg);   // an empty sequence keeps one entry
+        }
+        part[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int v = tid >= off ? part[tid - off] : 0;
+            __syncthreads();
+            part[tid] += v;
+            __syncthreads();
+        }
+        const int first = base + part[tid] - cnt;
+        const int tile_total = part[255];
+        if (n < N) {
+            seg_first[n] = first;
+            for (int sgi = 0; sgi < cnt; ++sgi) {
+                const int idx = first + sgi;
+                if (idx < cap) {
+                    SegEntry e;
+                    e.bos = bos + sgi * lseg;
+                    e.eos = eos < bos + (sgi + 1) * lseg ? eos : bos + (sgi + 1) * lseg;
+                    e.n = n;
+                    e.first = sgi == 0;
+                    e.last = sgi == cnt - 1;
+                    e.pad = 0;
+                    segs[idx] = e;
+                }
+            }
+        }
+        base += tile_total;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        seg_first[N] = base;
+        *nsegs = base < cap ? base : cap;
+    }
+}
+
+// State fix-up: per (sequence, value head), S_in(i+1) = S_in(i) M_i + N_i over
+// its segments, in fp32 (v_mfma_f32_32x32x2_f32).  With the state held as
+// accumulator tiles of S^T (rows k, columns v):
+//   (S M)^T[k][v] = sum_v' M[v'][k] S^T[v'][v]
+// the accumulator is the B operand (contraction v' in accumulator order) and
+// M, staged V-major in LDS, is read column-wise as the A operand.
+__global__ __launch_bounds__(256) void fixup_kernel(const FixParams f) {
+    constexpr int MLD = 132;
+    __shared__ __attribute__((aligned(16))) float Ms[D * MLD];
+    const int n = blockIdx.x / f.Hv, h = blockIdx.x % f.Hv;
+    const int s0 = f.seg_first[n], cnt = f.seg_first[n + 1] - s0;
+    if (cnt <= 1) return;
+    const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
+    const int h32 = lane >> 5, l32 = lane & 31, v0 = ws * 32 + l32;
+    f32x16 S[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) S[bb] = zero16();
+    if (f.s_in) load_state(S, f.s_in + n * f.si_n + h * f.si_h, f.si_v, f.si_dt, v0, h32);
+    for (int i = 0; i + 1 < cnt; ++i) {
+        const int64_t off = ((int64_t)(s0 + i) * f.Hv + h) * kMapBytes;
+        const float *Mg = reinterpret_cast<const float *>(reinterpret_cast<const char *>(f.ws_m) + off);
+        for (int u = tid; u < D * 32; u += 256) {
+            const int row = u >> 5, c4 = u & 31;
+            *reinterpret_cast<f32x4 *>(Ms + row * MLD + 4 * c4) = *reinterpret_cast<const f32x4 *>(Mg + row * D + 4 * c4);
+        }
+        __syncthreads();
+        f32x16 Sn[4];
+        load_state(Sn, reinterpret_cast<const char *>(f.ws_n) + off, D * 4, GDN_F32, v0, h32);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int st = 0; st < 16; ++st)
+                    Sn[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ms[(32 * cb + acc_row(st, h32)) * MLD + 32 * mb + l32],
+                                                                  S[cb][st], Sn[mb], 0, 0, 0);
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) S[bb] = Sn[bb];
+        store_state(S, reinterpret_cast<char *>(f.ws_sin) + ((int64_t)(s0 + i + 1) * f.Hv + h) * kMapBytes, D * 4,
+                    GDN_F32, v0, h32);
+        __syncthreads();
+    }
+}
+
+template <typename IO, int MODE>
 hipError_t launch(const ScanParams &p, hipStream_t stream) {
-    const int64_t pairs = (int64_t)p.N * p.Hqk;
+    const int64_t items = p.segs ? p.seg_cap : p.N;
+    const int64_t pairs = items * p.Hqk;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * p.r;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((fused_scan_kernel<IO>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fused_scan_kernel<IO, MODE>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, hipStream_t stream) {
-    return io_bf16 ? launch<bf16>(p, stream) : launch<float>(p, stream);
+hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, int mode, hipStream_t stream) {
+    if (io_bf16) {
+        if (mode == kMapN) return launch<bf16, kMapN>(p, stream);
+        if (mode == kMapM) return launch<bf16, kMapM>(p, stream);
+        return launch<bf16, kScan>(p, stream);
+    }
+    if (mode == kMapN) return launch<float, kMapN>(p, stream);
+    if (mode == kMapM) return launch<float, kMapM>(p, stream);
+    return launch<float, kScan>(p, stream);
+}
+
+hipError_t launch_plan(const void *cu, int cu_i64, int N, int64_t lseg, SegEntry *segs, int32_t *nsegs,
+                       int32_t *seg_first, int cap, hipStream_t stream) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu, cu_i64, N, lseg, segs, nsegs, seg_first, cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_fixup(const FixParams &f, hipStream_t stream) {
+    const int64_t blocks = (int64_t)f.N * f.Hv;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(fixup_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, f);
+    return hipGetLastError();
 }
 
 }  // namespace gdn

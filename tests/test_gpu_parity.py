@@ -22,13 +22,15 @@ def test_tiny_fp32(gdn, variant, bi):
 
 
 @pytest.mark.parametrize("variant", [None, "gates_bf16", "long_memory"])
-def test_varlen_bf16(gdn, variant):
-    check(gdn, W.make(1, variant=variant), BF16_TOL, True)
+@pytest.mark.parametrize("bi", [True, False])
+def test_varlen_bf16(gdn, variant, bi):
+    check(gdn, W.make(1, variant=variant), BF16_TOL, bi)
 
 
-def test_many_short_bf16_state(gdn):
+@pytest.mark.parametrize("bi", [True, False])
+def test_many_short_bf16_state(gdn, bi):
     w = W.make(3)
-    out, fin = check(gdn, w, BF16_TOL, True)
+    out, fin = check(gdn, w, BF16_TOL, bi)
     # empty sequences pass the (bf16) initial state through bitwise
     for n in (0, 127, 255):
         assert torch.equal(fin[n].cpu(), w.initial_state[n])
