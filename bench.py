@@ -155,6 +155,28 @@ def summarize_trace(base, out_path, command):
     print("\n".join(lines))
 
 
+def summarize_counters(dirs, out_path, commands):
+    """Median per-dispatch value of every counter found for the scan kernel in
+    the rocprofv3 --pmc output directories `dirs`; writes a text summary."""
+    import sqlite3
+    vals = {}
+    for d in dirs:
+        for f in _db_files(d):
+            con = sqlite3.connect(f)
+            for disp, kname, cname, v in con.execute(
+                    "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+                if KERNEL in kname and "kScan" not in cname:
+                    vals.setdefault(cname, {}).setdefault((f, disp), 0.0)
+                    vals[cname][(f, disp)] += float(v)
+            con.close()
+    lines = ["# rocprofv3 --pmc counters of fused_scan_kernel (median over dispatches, summed over the device)"]
+    lines += [f"# command: {c}" for c in commands]
+    for cname in sorted(vals):
+        lines.append(f"{cname} = {statistics.median(vals[cname].values()):.0f}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes):
     """Reads four rocprofv3 --pmc output dirs (kernel FETCH_SIZE, WRITE_SIZE;
     copy FETCH_SIZE, WRITE_SIZE) and writes the traffic summary file."""
@@ -210,6 +232,8 @@ def main():
     ap.add_argument("--summarize-pmc", default=None)
     ap.add_argument("--pmc-commands", default="{}")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"), default=None)
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
+                    help="rocprofv3 --pmc output dirs; the last argument is the output file")
     ap.add_argument("--trace-command", default="?")
     args = ap.parse_args()
 
@@ -220,6 +244,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1],
+                           json.loads(args.pmc_commands).get("commands", []))
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_command)

@@ -521,12 +521,6 @@ fused_scan_kernel(const ScanParams p) {
         const int v0 = ws * 32 + l32;
 
         // ---- [L] stage K, K^T, Q and row norms; gates and the in-chunk log-gate cumsum
-        VRegs vcur;
-        if constexpr (HASV) issue_v<IO>(vcur, p, ch, h, h32, v0);
-        else {
-#pragma unroll
-            for (int e = 0; e < 32; ++e) vcur.x[e] = 0u;
-        }
         if constexpr (BF) {
             const int rq4 = tid >> 4, cg = tid & 15;
 #pragma unroll
@@ -701,7 +695,13 @@ fused_scan_kernel(const ScanParams p) {
         }
         __syncthreads();
 
-        // ---- [C] one wave: T' = (I + A)^-1 into Ts (operand type)
+        // ---- [C] this chunk's V in flight (first read in [D]); one wave: T' = (I + A)^-1
+        VRegs vcur;
+        if constexpr (HASV) issue_v<IO>(vcur, p, ch, h, h32, v0);
+        else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) vcur.x[e] = 0u;
+        }
         if (ws == 0) {
             // (1) 16x16 diagonal blocks by forward substitution, lane = (block, column)
             {
