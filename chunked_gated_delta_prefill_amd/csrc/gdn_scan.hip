@@ -54,6 +54,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = kChunk;
 constexpr int D = kHeadDim;
@@ -96,6 +98,10 @@ template <> struct Mma<float> {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
 };
+
+__device__ __forceinline__ f32x4 mfma16f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 // Row of 32x32 accumulator register r for half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -238,13 +244,11 @@ constexpr float kRenorm = 0x1p-40f;   // sigma below this is folded back into th
 template <typename IO> struct Smem {
     static constexpr bool BF = is_bf<IO>::value;
     static constexpr int KLD = BF ? 136 : 132;   // K, Q rows (elements of IO)
-    static constexpr int TLD = 68;               // K^T rows (bf16 path)
     static constexpr int OLD = 68;               // T', P rows (elements of IO)
     static constexpr int FLD = 68;               // fp32 64x64 work matrix (A, inverse blocks)
     static constexpr int KB = C * KLD * (int)sizeof(IO);
     static constexpr int K_OFF = 0;
-    static constexpr int KT_OFF = K_OFF + KB;
-    static constexpr int Q_OFF = KT_OFF + (BF ? D * TLD * 2 : 0);
+    static constexpr int Q_OFF = K_OFF + KB;
     // bf16: P and T' reuse Q's space once Q has been consumed
     static constexpr int P_OFF = BF ? Q_OFF : Q_OFF + KB;
     static constexpr int T_OFF = P_OFF + C * OLD * (int)sizeof(IO);
@@ -254,7 +258,7 @@ template <typename IO> struct Smem {
     static_assert(!BF || T_OFF + C * OLD * 2 <= Q_OFF + KB, "P and T' must fit in Q's space");
     static_assert(!BF || BYTES <= 80 * 1024, "two workgroups per CU");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
-    static_assert(KT_OFF % 16 == 0 && Q_OFF % 16 == 0 && AF_OFF % 16 == 0 && T_OFF % 16 == 0 &&
+    static_assert(Q_OFF % 16 == 0 && AF_OFF % 16 == 0 && T_OFF % 16 == 0 &&
                   ROW_OFF % 16 == 0, "align");
 };
 
@@ -268,6 +272,45 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// Sum of squares of 8 bf16 values (products exact in fp32, fp32 accumulation).
+__device__ __forceinline__ float sumsq8(bf16x8 x) {
+    const bf16x2 x0 = __builtin_shufflevector(x, x, 0, 1), x1 = __builtin_shufflevector(x, x, 2, 3);
+    const bf16x2 x2 = __builtin_shufflevector(x, x, 4, 5), x3 = __builtin_shufflevector(x, x, 6, 7);
+    const float a = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, __builtin_amdgcn_fdot2_f32_bf16(x0, x0, 0.f, false), false);
+    const float b = __builtin_amdgcn_fdot2_f32_bf16(x3, x3, __builtin_amdgcn_fdot2_f32_bf16(x1, x1, 0.f, false), false);
+    return a + b;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts of 1, 2, 4, 8 inside
+// each 16-lane row, then the row totals carried across rows.
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_add(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// 32x32 bf16 A operand of a product contracting over tokens, rows = K columns
+// [m0, m0 + 32), read straight from row-major K with the transposing LDS load
+// (within 16 lanes, output lane i element e comes from source lane i/4 + 4e,
+// element i%4; source lane j points at token t0 + j/4, column m0' + 4 (j%4)).
+// Slots follow the accumulator order of ld_acc: tokens cb + 16s + 4h + {0..3}
+// and the same + 8.
+__device__ __forceinline__ bf16x8 ld_acc_tr(const bf16 *Ks, int ld, int m0, int cb, int s, int lane) {
+    const int i = lane & 15, h = lane >> 5, g16 = (lane >> 4) & 1;
+    const bf16 *p = Ks + (cb + 16 * s + 4 * h + (i >> 2)) * ld + m0 + 16 * g16 + 4 * (i & 3);
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * ld));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // K, Q and the gates of the next chunk, loaded while the current chunk runs
 // (consumed only after the chunk's last barrier, so no wait is forced early).
@@ -446,7 +489,6 @@ fused_scan_kernel(const ScanParams p) {
 
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     IO *Ks = reinterpret_cast<IO *>(smem + L::K_OFF);
-    bf16 *KTs = reinterpret_cast<bf16 *>(smem + L::KT_OFF);
     IO *Qs = reinterpret_cast<IO *>(smem + L::Q_OFF);
     IO *Ps = reinterpret_cast<IO *>(smem + L::P_OFF);
     IO *Ts = reinterpret_cast<IO *>(smem + L::T_OFF);
@@ -529,10 +571,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const bf16x8 x = __builtin_bit_cast(bf16x8, pf.kq[mat][t]);
-                    float a = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) a += (float)x[e] * (float)x[e];
-                    ss[t] = row_sum16(a);
+                    ss[t] = row_sum16(sumsq8(x));
                     *reinterpret_cast<i32x4 *>((mat ? Qs : Ks) + (4 * rq4 + t) * L::KLD + 8 * cg) = pf.kq[mat][t];
                 }
                 if (cg == 0) {
@@ -541,13 +580,6 @@ fused_scan_kernel(const ScanParams p) {
                     for (int t = 0; t < 4; ++t) rn[t] = p.l2norm ? rsqrtf(ss[t] + 1e-6f) : 1.f;
                     *reinterpret_cast<f32x4 *>(rf(mat ? RQ_ : RK_) + 4 * rq4) = rn;
                 }
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 col;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) col[t] = __builtin_bit_cast(bf16x8, pf.kq[0][t])[e];
-                *reinterpret_cast<bf16x4 *>(KTs + (8 * cg + e) * L::TLD + 4 * rq4) = col;
             }
         } else {
             const int r0 = tid >> 5, cg = tid & 31;
@@ -568,13 +600,8 @@ fused_scan_kernel(const ScanParams p) {
             const bool valid = lane < Lc;
             const float ga = p.g ? gate_value(pf.g, p.g_dt) : 1.f;
             const float gb = p.beta ? gate_value(pf.b, p.b_dt) : 1.f;
-            float G = valid ? fmaxf(__logf(ga), -80.f) : 0.f;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(G, o);
-                if (lane >= o) G += y;
-            }
-            const float GL = __shfl(G, 63);
+            const float G = wave_prefix_sum(valid ? fmaxf(__logf(ga), -80.f) : 0.f);
+            const float GL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
             g_G = G;
             g_b = valid ? gb : 0.f;
             g_gam = __expf(G);
@@ -695,42 +722,63 @@ fused_scan_kernel(const ScanParams p) {
         }
         __syncthreads();
 
-        // ---- [C] this chunk's V in flight (first read in [D]); one wave: T' = (I + A)^-1
+        // ---- [C] this chunk's V in flight (first read in [D]); T' = (I + A)^-1:
+        // each wave inverts one 16x16 diagonal block, then one wave merges them
         VRegs vcur;
         if constexpr (HASV) issue_v<IO>(vcur, p, ch, h, h32, v0);
         else {
 #pragma unroll
             for (int e = 0; e < 32; ++e) vcur.x[e] = 0u;
         }
-        if (ws == 0) {
-            // (1) 16x16 diagonal blocks by forward substitution, lane = (block, column)
-            {
-                const int bk = lane >> 4, cc = lane & 15;
-                float *blk = Af + (16 * bk) * L::FLD + 16 * bk;
-                float x[16];
+        {
+            // (1) D = (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly
+            // lower block N (N^16 = 0), on fp32 16x16x4 MFMAs.  An accumulator X
+            // (register r of lane group g holds X[4g + r][lane % 16]) serves as the B
+            // operand X, or as the A operand X^T, with contraction index 4g + s at
+            // step s; the transposed powers are carried so every product reads
+            // operands straight from accumulators.
+            const int g = lane >> 4, nn = lane & 15;
+            float *blk = Af + (16 * ws) * L::FLD + 16 * ws;
+            const f32x4 nrow = ld4(blk + nn * L::FLD + 4 * g);      // N[nn][4g + s]
+            f32x4 ncol;                                              // N[4g + s][nn]
 #pragma unroll
-                for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
+            for (int q = 0; q < 4; ++q) ncol[q] = blk[(4 * g + q) * L::FLD + nn];
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 n2 = z4, n2t = z4;
 #pragma unroll
-                for (int i = 1; i < 16; ++i) {
-                    f32x4 a4[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (4 * q < i) a4[q] = ld4(blk + i * L::FLD + 4 * q);
-                    float s = 0.f;
-#pragma unroll
-                    for (int m = 0; m < i; ++m) s += a4[m >> 2][m & 3] * x[m];
-                    x[i] = i > cc ? -s : x[i];
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    blk[i * L::FLD + cc] = x[i];
-                    Ts[(16 * bk + i) * L::OLD + 16 * bk + cc] = (IO)x[i];
-                }
-                if ((bk & 1) == 0) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) Ts[(16 * bk + i) * L::OLD + 16 * bk + 16 + cc] = (IO)0.f;
-                }
+            for (int q = 0; q < 4; ++q) {
+                n2 = mfma16f32(nrow[q], ncol[q], n2);      // N N
+                n2t = mfma16f32(ncol[q], nrow[q], n2t);    // N^T N^T
             }
+            f32x4 m2 = n2;                                 // I + N^2
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m2[q] += (4 * g + q == nn) ? 1.f : 0.f;
+            f32x4 n4 = z4, n4t = z4, r1 = m2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                n4 = mfma16f32(n2t[q], n2[q], n4);         // N^2 N^2
+                n4t = mfma16f32(n2[q], n2t[q], n4t);       // (N^2)^T (N^2)^T
+                r1 = mfma16f32(-nrow[q], m2[q], r1);       // (I + N^2) - N (I + N^2)
+            }
+            f32x4 n8t = z4, r2 = r1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                n8t = mfma16f32(n4[q], n4t[q], n8t);       // (N^4)^T (N^4)^T
+                r2 = mfma16f32(n4t[q], r1[q], r2);         // R1 + N^4 R1
+            }
+            f32x4 dinv = r2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dinv = mfma16f32(n8t[q], r2[q], dinv);   // R2 + N^8 R2
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = 4 * g + q;
+                blk[i * L::FLD + nn] = dinv[q];
+                Ts[(16 * ws + i) * L::OLD + 16 * ws + nn] = (IO)dinv[q];
+                if ((ws & 1) == 0) Ts[(16 * ws + i) * L::OLD + 16 * ws + 16 + nn] = (IO)0.f;
+            }
+        }
+        __syncthreads();
+        if (ws == 0) {
             // (2) 16 -> 32: T'_{2x+1,2x} = -D_{2x+1} A_{2x+1,2x} D_{2x}, x = 0, 1
             {
                 const int g = lane >> 4, nn = lane & 15;
@@ -888,7 +936,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                 for (int s = 0; s < S32; ++s) {
                     frag a;
-                    if constexpr (BF) a = ld_acc<bf16>(KTs, L::TLD, 32 * bb + l32, 32 * ib, s, h32);
+                    if constexpr (BF) a = ld_acc_tr(Ks, L::KLD, 32 * bb, 32 * ib, s, lane);
                     else a = ld_acc_t<float>(Ks, L::KLD, 32 * bb + l32, 32 * ib, s, h32);
                     S[bb] = M::run(a, ub[ib][s], S[bb]);
                 }
