@@ -227,17 +227,19 @@ __device__ __forceinline__ float gate_value(uint32_t bits, int dt) {
 
 // ---------------------------------------------------------- LDS layout ----
 // Per-row factor arrays (64 floats each), written once per chunk.  The state
-// is held as S = sigma * S~ (sigma a per-sequence scalar, see the kernel):
+// is held as S = sigma * S~ (sigma a per-sequence scalar, see the kernel); c
+// is the query scale:
 //   RG  in-chunk log-gate cumsum G_i        RK  rk_i (1 without L2 norm)
 //   RQ  rq_i                                FA  b_i rk_i            (rows of A)
-//   PQ  rq_i                  (rows of P)   FZ  sigma gamma_i rk_i  (rows of K S~^T)
-//   FB  b_i                   (rows of Z)   FY  sigma gamma_i rq_i  (rows of Q S~^T)
-//   FU  rk_i exp(G_L - G_i) / sigma'        (state update)
-//   EA  b_i rk_i gamma_i, EQ rq_i gamma_i, CJ rk_j / gamma_j: A and P entries
-//       as products when the chunk's total decay is moderate (no exp per entry)
+//   PQ  c rq_i                (rows of P)   FZ  sigma gamma_i rk_i  (rows of K S~^T)
+//   FB  b_i        (columns of T' = T diag(b))
+//   FY  c sigma gamma_i rq_i  (output rows)
+//   FU  rk_i exp(G_L - G_i) / sigma'        (state update; without / sigma' on renorm)
+//   EA  b_i rk_i gamma_i, CJ rk_j / gamma_j: A entries as a product when the
+//       chunk's total decay is moderate (no exp per entry)
 // followed by gamma_L.
-enum { RG_ = 0, RK_ = 1, RQ_ = 2, FA_ = 3, PQ_ = 4, FZ_ = 5, FB_ = 6, FY_ = 7, FU_ = 8, EA_ = 9, EQ_ = 10,
-       CJ_ = 11, NROWF = 12 };
+enum { RG_ = 0, RK_ = 1, RQ_ = 2, FA_ = 3, PQ_ = 4, FZ_ = 5, FB_ = 6, FY_ = 7, FU_ = 8, EA_ = 9, CJ_ = 10,
+       NROWF = 11 };
 constexpr float kFastDecay = -60.f;   // G_L above this: exp(G_i - G_j) = gamma_i / gamma_j is safe
 constexpr float kRenorm = 0x1p-40f;   // sigma below this is folded back into the state
 
@@ -250,12 +252,11 @@ template <typename IO> struct Smem {
     static constexpr int K_OFF = 0;
     static constexpr int Q_OFF = K_OFF + KB;
     // bf16: P and T' reuse Q's space once Q has been consumed
-    static constexpr int P_OFF = BF ? Q_OFF : Q_OFF + KB;
+    static constexpr int P_OFF = Q_OFF + KB;
     static constexpr int T_OFF = P_OFF + C * OLD * (int)sizeof(IO);
-    static constexpr int AF_OFF = BF ? Q_OFF + KB : T_OFF + C * OLD * (int)sizeof(IO);
+    static constexpr int AF_OFF = T_OFF + C * OLD * (int)sizeof(IO);
     static constexpr int ROW_OFF = AF_OFF + C * FLD * 4;
     static constexpr int BYTES = ROW_OFF + (NROWF * C + 4) * 4;
-    static_assert(!BF || T_OFF + C * OLD * 2 <= Q_OFF + KB, "P and T' must fit in Q's space");
     static_assert(!BF || BYTES <= 80 * 1024, "two workgroups per CU");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(Q_OFF % 16 == 0 && AF_OFF % 16 == 0 && T_OFF % 16 == 0 &&
@@ -611,7 +612,7 @@ fused_scan_kernel(const ScanParams p) {
         }
         __syncthreads();
 
-        // ---- [A] per-row factors (wave 0); Y = Q S0^T for this wave's rows; Gram tiles
+        // ---- [A] per-row factors (wave 0); Gram tiles
         // The true state is sigma * S~.  After this chunk it is
         //   gamma_L sigma S~ + K^T U  =  sigma' (S~ + K^T U / sigma'),  sigma' = gamma_L sigma,
         // so the decay costs no per-element work; when sigma' gets small it is
@@ -620,35 +621,23 @@ fused_scan_kernel(const ScanParams p) {
             __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, RF[NROWF * C])));
         const float sig_next = sigma * gLc;
         const bool renorm = !(sig_next >= kRenorm);
+        const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                              int, rf(RG_)[C - 1]))) > kFastDecay;
         if (ws == 0) {
             const float rk = rf(RK_)[lane], rq = rf(RQ_)[lane];
             rf(FA_)[lane] = g_b * rk;
-            rf(PQ_)[lane] = rq;
+            rf(PQ_)[lane] = rq * p.scale;
             rf(FZ_)[lane] = sigma * g_gam * rk;
             rf(FB_)[lane] = g_b;
-            rf(FY_)[lane] = sigma * g_gam * rq;
+            rf(FY_)[lane] = sigma * g_gam * rq * p.scale;
             rf(FU_)[lane] = renorm ? rk * g_dec : rk * g_dec / sig_next;
             rf(EA_)[lane] = g_b * rk * g_gam;
-            rf(EQ_)[lane] = rq * g_gam;
             rf(CJ_)[lane] = rk / g_gam;
         }
         (void)g_G;
-        f32x16 Y[2] = {zero16(), zero16()};
-        if constexpr (OUT) {
-            frag sb[4][S32];
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                for (int s = 0; s < S32; ++s) sb[bb][s] = acc_frag<IO>(S[bb], s);
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                    for (int s = 0; s < S32; ++s)
-                        Y[ib] = M::run(ld_acc<IO>(Qs, L::KLD, 32 * ib + l32, 32 * bb, s, h32), sb[bb][s], Y[ib]);
-        }
-        // tiles: 0..2 = K K^T (0,0) (1,0) (1,1); 3..5 = Q K^T (same); wave w takes w and w + 4
+        // tiles (bi, bj) = (0,0) (1,0) (1,1) of K K^T (0..2) and Q K^T (3..5); wave w takes
+        // w and w + 4.  Each is computed transposed: register rows are the column
+        // index j = 32 bj + acc_row, the lane is the row index i = 32 bi + l32.
         f32x16 gt[2] = {zero16(), zero16()};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -659,62 +648,97 @@ fused_scan_kernel(const ScanParams p) {
                 const IO *As = isq ? Qs : Ks;
 #pragma unroll
                 for (int s = 0; s < D / (2 * E); ++s)
-                    gt[u] = M::run(ld_nat<IO>(As, L::KLD, 32 * bi + l32, s, h32),
-                                   ld_nat<IO>(Ks, L::KLD, 32 * bj + l32, s, h32), gt[u]);
+                    gt[u] = M::run(ld_nat<IO>(Ks, L::KLD, 32 * bj + l32, s, h32),
+                                   ld_nat<IO>(As, L::KLD, 32 * bi + l32, s, h32), gt[u]);
             }
         }
         __syncthreads();
 
         // ---- [B] next chunk's K, Q, gates in flight; A (fp32) and P into LDS
         issue_loads<IO>(pf, p, chunk_at(bos, eos, c + 1), hq, h, tid, lane, ws);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tile = ws + 4 * u;
-            if (tile < (OUT ? 6 : 3)) {
-                const int isq = tile >= 3, tt = tile - 3 * isq;
+        {
+            // Lane row i = 32 bi + l32; register 4 jj + t is column j = 32 bj + 8 jj + 4 h32 + t.
+            //   A = b_i rk_i rk_j (k_i . k_j) exp(G_i - G_j)   for j < i   (fp32)
+            //   P = c rq_i rk_j (q_i . k_j) exp(G_i - G_j)      for j <= i  (slow)
+            //   P = (q_i . k_j) / sigma'(renorm only)          for j <= i  (fast: the row
+            //       and column factors move to the output rows and to the shared Vnew
+            //       operand, see [D])
+            // Four consecutive columns are stored at once; every factor read is
+            // issued before the first store.
+            constexpr int NT = OUT ? 6 : 3;
+            const float cP = renorm ? 1.f / sig_next : 1.f;
+            auto store4 = [&](int u, int jj, f32x4 v) {
+                const int tile = ws + 4 * u, isq = tile >= 3, tt = tile - 3 * isq;
                 const int bi = tt > 0, bj = tt == 2;
-                const int j = 32 * bj + l32;
-                const float rkj = rf(RK_)[j], Gj = rf(RG_)[j];
-                // i - j for register rr is d0 + 8*(rr/4) + rr%4
-                const int d0 = 32 * (bi - bj) + 4 * h32 - l32;
-                const bool fast = rf(RG_)[C - 1] > kFastDecay;
-                const float cj = rf(CJ_)[j];
-                if (isq) {        // P = rq_i rk_j (q_i . k_j) exp(G_i - G_j)  for j <= i
+                const int i = 32 * bi + l32, j0 = 32 * bj + 8 * jj + 4 * h32;
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int i0 = 32 * bi + 8 * jj + 4 * h32;
-                        IO *dst = Ps + i0 * L::OLD + j;
-                        if (fast) {
-                            const f32x4 E4 = ld4(rf(EQ_) + i0);
+                for (int t = 0; t < 4; ++t) v[t] = i - (j0 + t) + isq > 0 ? v[t] : 0.f;
+                if (isq) {
+                    if constexpr (BF) {
+                        const bf16x4 b4 = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+                        *reinterpret_cast<bf16x4 *>(Ps + i * L::OLD + j0) = b4;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(Ps + i * L::OLD + j0) = v;
+                    }
+                } else {
+                    *reinterpret_cast<f32x4 *>(Af + i * L::FLD + j0) = v;
+                }
+            };
+            auto tile_rc = [&](int u, int &isq, int &i, int &jb) {
+                const int tile = ws + 4 * u;
+                isq = tile >= 3;
+                const int tt = tile - 3 * isq;
+                i = 32 * (tt > 0) + l32;
+                jb = 32 * (tt == 2) + 4 * h32;
+            };
+            if (fast) {
+                f32x4 CJ4[2][4];
+                float ea[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    int isq, i, jb;
+                    tile_rc(u, isq, i, jb);
+                    if (ws + 4 * u < NT && !isq) {
+                        ea[u] = rf(EA_)[i];
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) CJ4[u][jj] = ld4(rf(CJ_) + jb + 8 * jj);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    int isq, i, jb;
+                    tile_rc(u, isq, i, jb);
+                    if (ws + 4 * u < NT) {
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            f32x4 v;
 #pragma unroll
                             for (int t = 0; t < 4; ++t)
-                                dst[t * L::OLD] = (IO)(d0 + 8 * jj + t >= 0 ? E4[t] * cj * gt[u][4 * jj + t] : 0.f);
-                        } else {
-                            const f32x4 G4 = ld4(rf(RG_) + i0), F4 = ld4(rf(PQ_) + i0);
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                const float val = F4[t] * rkj * gt[u][4 * jj + t] * __expf(fminf(G4[t] - Gj, 0.f));
-                                dst[t * L::OLD] = (IO)(d0 + 8 * jj + t >= 0 ? val : 0.f);
-                            }
+                                v[t] = isq ? cP * gt[u][4 * jj + t] : ea[u] * CJ4[u][jj][t] * gt[u][4 * jj + t];
+                            store4(u, jj, v);
                         }
                     }
-                } else {          // A = b_i rk_i rk_j (k_i . k_j) exp(G_i - G_j)  for j < i
+                }
+            } else {
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int i0 = 32 * bi + 8 * jj + 4 * h32;
-                        float *dst = Af + i0 * L::FLD + j;
-                        if (fast) {
-                            const f32x4 E4 = ld4(rf(EA_) + i0);
+                for (int u = 0; u < 2; ++u) {
+                    int isq, i, jb;
+                    tile_rc(u, isq, i, jb);
+                    if (ws + 4 * u < NT) {
+                        const float fi = rf(isq ? PQ_ : FA_)[i], Gi = rf(RG_)[i];
+                        f32x4 RK4[4], G4[4];
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            RK4[jj] = ld4(rf(RK_) + jb + 8 * jj);
+                            G4[jj] = ld4(rf(RG_) + jb + 8 * jj);
+                        }
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            f32x4 v;
 #pragma unroll
                             for (int t = 0; t < 4; ++t)
-                                dst[t * L::FLD] = d0 + 8 * jj + t > 0 ? E4[t] * cj * gt[u][4 * jj + t] : 0.f;
-                        } else {
-                            const f32x4 G4 = ld4(rf(RG_) + i0), F4 = ld4(rf(FA_) + i0);
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                const float val = F4[t] * rkj * gt[u][4 * jj + t] * __expf(fminf(G4[t] - Gj, 0.f));
-                                dst[t * L::FLD] = d0 + 8 * jj + t > 0 ? val : 0.f;
-                            }
+                                v[t] = fi * RK4[jj][t] * gt[u][4 * jj + t] * __expf(fminf(Gi - G4[jj][t], 0.f));
+                            store4(u, jj, v);
                         }
                     }
                 }
@@ -739,6 +763,7 @@ fused_scan_kernel(const ScanParams p) {
             // operands straight from accumulators.
             const int g = lane >> 4, nn = lane & 15;
             float *blk = Af + (16 * ws) * L::FLD + 16 * ws;
+            const float bcol = rf(FB_)[16 * ws + nn];
             const f32x4 nrow = ld4(blk + nn * L::FLD + 4 * g);      // N[nn][4g + s]
             f32x4 ncol;                                              // N[4g + s][nn]
 #pragma unroll
@@ -773,7 +798,7 @@ fused_scan_kernel(const ScanParams p) {
             for (int q = 0; q < 4; ++q) {
                 const int i = 4 * g + q;
                 blk[i * L::FLD + nn] = dinv[q];
-                Ts[(16 * ws + i) * L::OLD + 16 * ws + nn] = (IO)dinv[q];
+                Ts[(16 * ws + i) * L::OLD + 16 * ws + nn] = (IO)(dinv[q] * bcol);
                 if ((ws & 1) == 0) Ts[(16 * ws + i) * L::OLD + 16 * ws + 16 + nn] = (IO)0.f;
             }
         }
@@ -795,6 +820,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                 for (int x2 = 0; x2 < 2; ++x2) {
                     const int lo = 32 * x2, hi = 32 * x2 + 16;
+                    const float bcol = rf(FB_)[lo + nn];
                     f32x4 Tq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < S16; ++s)
@@ -803,7 +829,7 @@ fused_scan_kernel(const ScanParams p) {
                     for (int rr = 0; rr < 4; ++rr) {
                         const int i = hi + 4 * g + rr;
                         Af[i * L::FLD + lo + nn] = -Tq[rr];
-                        Ts[i * L::OLD + lo + nn] = (IO)(-Tq[rr]);
+                        Ts[i * L::OLD + lo + nn] = (IO)(-Tq[rr] * bcol);
                     }
                 }
             }
@@ -818,14 +844,21 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                 for (int s = 0; s < S32; ++s)
                     T21 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 32, s, h32), acc_frag<IO>(R2, s), T21);
+                const float bcol = rf(FB_)[l32];
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) Ts[(32 + acc_row(rr, h32)) * L::OLD + l32] = (IO)(-T21[rr]);
+                for (int rr = 0; rr < 16; ++rr) Ts[(32 + acc_row(rr, h32)) * L::OLD + l32] = (IO)(-T21[rr] * bcol);
             }
         }
         __syncthreads();
 
         // ---- [D] Vnew, output and state update for this wave's 32 state rows
+        //   Z' = V - FZ o (K S~^T)       Vnew = T' Z'   (T' = T diag(b))
+        //   ub = FU o Vnew  (bf16 operand of the state update S~ += K^T ub)
+        //   output, computed transposed (lane = token t, registers = 4 consecutive v):
+        //     fast: O^T = FY_t [ (S~ Q^T) + ub^T P^T ]   (P = masked q.k, see [B])
+        //     slow: O^T = FY_t (S~ Q^T) + Vnew^T P^T
         frag zb[2][S32];
+        f32x16 Y[2] = {zero16(), zero16()};
         {
             frag sb[4][S32];
 #pragma unroll
@@ -840,22 +873,30 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                     for (int s = 0; s < S32; ++s)
                         X = M::run(ld_acc<IO>(Ks, L::KLD, 32 * ib + l32, 32 * bb, s, h32), sb[bb][s], X);
-                // Z = b o (V - gamma rk (K S0^T))
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int i0 = 32 * ib + 8 * jj + 4 * h32;
-                    const f32x4 fz = ld4(rf(FZ_) + i0), fb = ld4(rf(FB_) + i0);
+                    const f32x4 fz = ld4(rf(FZ_) + 32 * ib + 8 * jj + 4 * h32);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const int rr = 4 * jj + t;
-                        X[rr] = (vreg_at(vcur, 16 * ib + rr, BF) - fz[t] * X[rr]) * fb[t];
+                        X[rr] = fmaf(-fz[t], X[rr], vreg_at(vcur, 16 * ib + rr, BF));
                     }
                 }
 #pragma unroll
                 for (int s = 0; s < S32; ++s) zb[ib][s] = acc_frag<IO>(X, s);
             }
+            // (S~ Q^T) for this wave's state rows: S~ as the A operand gives the transpose
+            if constexpr (OUT) {
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                        for (int s = 0; s < S32; ++s)
+                            Y[ib] = M::run(sb[bb][s], ld_acc<IO>(Qs, L::KLD, 32 * ib + l32, 32 * bb, s, h32), Y[ib]);
+            }
         }
-        // Vnew = T' Z   (T' lower block-triangular: skip the zero upper 32x32 block)
+        // Vnew = T' Z'   (T' lower block-triangular: skip the zero upper 32x32 block)
         f32x16 Vn[2] = {zero16(), zero16()};
 #pragma unroll
         for (int s = 0; s < S32; ++s) {
@@ -864,49 +905,24 @@ fused_scan_kernel(const ScanParams p) {
             Vn[1] = M::run(ld_acc<IO>(Ts, L::OLD, 32 + l32, 32, s, h32), zb[1][s], Vn[1]);
         }
         if constexpr (OUT) {
-        frag nb[2][S32];
+            if (!fast) {   // slow: FY_t (S~ Q^T) + Vnew^T P^T, with its own Vnew operand
+                frag nb[2][S32];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+                for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int s = 0; s < S32; ++s) nb[ib][s] = acc_frag<IO>(Vn[ib], s);
-        // O = scale [ gamma rq (Q S0^T) + P Vnew ]
-        {
-            constexpr int ES = (int)sizeof(IO);
-            const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * ES);
-            const int vo = 4 * h32 * p.o_st + v0 * ES;
-            auto store_rows = [&](const f32x16 &o, int ib, bool full) {
+                    for (int s = 0; s < S32; ++s) nb[ib][s] = acc_frag<IO>(Vn[ib], s);
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int rofs = (32 * ib + 8 * (rr >> 2) + (rr & 3)) * p.o_st;
-                    if constexpr (BF) {
-                        const unsigned short x = __builtin_bit_cast(unsigned short, (bf16)(o[rr] * p.scale));
-                        if (full) __builtin_amdgcn_raw_buffer_store_b16(x, ro, vo, rofs, 0);
-                        else __builtin_amdgcn_raw_buffer_store_b16(x, ro, vo + rofs, 0, 0);
-                    } else {
-                        const uint32_t x = __builtin_bit_cast(uint32_t, o[rr] * p.scale);
-                        if (full) __builtin_amdgcn_raw_buffer_store_b32(x, ro, vo, rofs, 0);
-                        else __builtin_amdgcn_raw_buffer_store_b32(x, ro, vo + rofs, 0, 0);
-                    }
+                for (int ib = 0; ib < 2; ++ib) {
+                    const float fy = rf(FY_)[32 * ib + l32];
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
+#pragma unroll
+                    for (int jb = 0; jb <= ib; ++jb)
+#pragma unroll
+                        for (int s = 0; s < S32; ++s)
+                            Y[ib] = M::run(nb[jb][s], ld_acc<IO>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), Y[ib]);
                 }
-            };
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const f32x4 fy = ld4(rf(FY_) + 32 * ib + 8 * jj + 4 * h32);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) Y[ib][4 * jj + t] *= fy[t];
-                }
-#pragma unroll
-                for (int jb = 0; jb <= ib; ++jb)
-#pragma unroll
-                    for (int s = 0; s < S32; ++s)
-                        Y[ib] = M::run(ld_acc<IO>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), nb[jb][s], Y[ib]);
-                if (Lc == C) store_rows(Y[ib], ib, true);
-                else store_rows(Y[ib], ib, false);
             }
-        }
-        // S~ <- S~ + K^T (FU o Vnew)  (sigma' carries the decay)
         }
         frag ub[2][S32];
 #pragma unroll
@@ -919,6 +935,40 @@ fused_scan_kernel(const ScanParams p) {
             }
 #pragma unroll
             for (int s = 0; s < S32; ++s) ub[ib][s] = acc_frag<IO>(Vn[ib], s);
+        }
+        if constexpr (OUT) {
+            if (fast) {
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+                    for (int jb = 0; jb <= ib; ++jb)
+#pragma unroll
+                        for (int s = 0; s < S32; ++s)
+                            Y[ib] = M::run(ub[jb][s], ld_acc<IO>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), Y[ib]);
+                    const float fy = rf(FY_)[32 * ib + l32];
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
+                }
+            }
+            // store: lane = token 32 ib + l32 (rows past the chunk end fall outside the
+            // buffer range), registers 4q..4q+3 = v 32 ws + 8q + 4 h32 + 0..3
+            constexpr int ES = (int)sizeof(IO);
+            const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * ES);
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const int base = (32 * ib + l32) * p.o_st + (32 * ws + 4 * h32) * ES;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if constexpr (BF) {
+                        const bf16x4 b4 = {(bf16)Y[ib][4 * q], (bf16)Y[ib][4 * q + 1], (bf16)Y[ib][4 * q + 2],
+                                           (bf16)Y[ib][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b4), ro, base + 8 * q * ES, 0, 0);
+                    } else {
+                        const f32x4 f4 = {Y[ib][4 * q], Y[ib][4 * q + 1], Y[ib][4 * q + 2], Y[ib][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, f4), ro, base + 8 * q * ES, 0, 0);
+                    }
+                }
+            }
         }
         if (renorm) {
 #pragma unroll
