@@ -563,7 +563,7 @@ fused_scan_kernel(const ScanParams p) {
         const int h32 = lane >> 5, l32 = lane & 31;
         const int v0 = ws * 32 + l32;
 
-        // ---- [L] stage K, K^T, Q and row norms; gates and the in-chunk log-gate cumsum
+        // ---- [L] stage K and Q, row norms; gates and the in-chunk log-gate cumsum
         if constexpr (BF) {
             const int rq4 = tid >> 4, cg = tid & 15;
 #pragma unroll
@@ -665,83 +665,82 @@ fused_scan_kernel(const ScanParams p) {
             //       operand, see [D])
             // Four consecutive columns are stored at once; every factor read is
             // issued before the first store.
-            constexpr int NT = OUT ? 6 : 3;
+            // Wave w holds tile w (A tiles (0,0) (1,0) (1,1) for w < 3, P tile (0,0) for
+            // w = 3) and, when w < 2, P tile (1, w); the map modes need no P.
             const float cP = renorm ? 1.f / sig_next : 1.f;
-            auto store4 = [&](int u, int jj, f32x4 v) {
-                const int tile = ws + 4 * u, isq = tile >= 3, tt = tile - 3 * isq;
-                const int bi = tt > 0, bj = tt == 2;
-                const int i = 32 * bi + l32, j0 = 32 * bj + 8 * jj + 4 * h32;
+            auto mask_row = [&](f32x4 &v, int i, int j0, int keep_diag) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = i - (j0 + t) + isq > 0 ? v[t] : 0.f;
-                if (isq) {
-                    if constexpr (BF) {
-                        const bf16x4 b4 = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-                        *reinterpret_cast<bf16x4 *>(Ps + i * L::OLD + j0) = b4;
-                    } else {
-                        *reinterpret_cast<f32x4 *>(Ps + i * L::OLD + j0) = v;
-                    }
+                for (int t = 0; t < 4; ++t) v[t] = i - (j0 + t) + keep_diag > 0 ? v[t] : 0.f;
+            };
+            auto a_tile = [&](const f32x16 &acc, int bi, int bj) {
+                const int i = 32 * bi + l32, jb = 32 * bj + 4 * h32;
+                f32x4 v[4];
+                if (fast) {
+                    const float ea = rf(EA_)[i];
+                    f32x4 cj[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) cj[jj] = ld4(rf(CJ_) + jb + 8 * jj);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[jj][t] = ea * cj[jj][t] * acc[4 * jj + t];
                 } else {
-                    *reinterpret_cast<f32x4 *>(Af + i * L::FLD + j0) = v;
+                    const float fi = rf(FA_)[i], Gi = rf(RG_)[i];
+                    f32x4 rk[4], G4[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        rk[jj] = ld4(rf(RK_) + jb + 8 * jj);
+                        G4[jj] = ld4(rf(RG_) + jb + 8 * jj);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            v[jj][t] = fi * rk[jj][t] * acc[4 * jj + t] * __expf(fminf(Gi - G4[jj][t], 0.f));
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    mask_row(v[jj], i, jb + 8 * jj, 0);
+                    *reinterpret_cast<f32x4 *>(Af + i * L::FLD + jb + 8 * jj) = v[jj];
                 }
             };
-            auto tile_rc = [&](int u, int &isq, int &i, int &jb) {
-                const int tile = ws + 4 * u;
-                isq = tile >= 3;
-                const int tt = tile - 3 * isq;
-                i = 32 * (tt > 0) + l32;
-                jb = 32 * (tt == 2) + 4 * h32;
+            auto p_tile = [&](const f32x16 &acc, int bi, int bj) {
+                const int i = 32 * bi + l32, jb = 32 * bj + 4 * h32;
+                f32x4 v[4];
+                if (fast) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[jj][t] = cP * acc[4 * jj + t];
+                } else {
+                    const float fi = rf(PQ_)[i], Gi = rf(RG_)[i];
+                    f32x4 rk[4], G4[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        rk[jj] = ld4(rf(RK_) + jb + 8 * jj);
+                        G4[jj] = ld4(rf(RG_) + jb + 8 * jj);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            v[jj][t] = fi * rk[jj][t] * acc[4 * jj + t] * __expf(fminf(Gi - G4[jj][t], 0.f));
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    mask_row(v[jj], i, jb + 8 * jj, 1);
+                    if constexpr (BF) {
+                        const bf16x4 b4 = {(bf16)v[jj][0], (bf16)v[jj][1], (bf16)v[jj][2], (bf16)v[jj][3]};
+                        *reinterpret_cast<bf16x4 *>(Ps + i * L::OLD + jb + 8 * jj) = b4;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(Ps + i * L::OLD + jb + 8 * jj) = v[jj];
+                    }
+                }
             };
-            if (fast) {
-                f32x4 CJ4[2][4];
-                float ea[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    int isq, i, jb;
-                    tile_rc(u, isq, i, jb);
-                    if (ws + 4 * u < NT && !isq) {
-                        ea[u] = rf(EA_)[i];
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) CJ4[u][jj] = ld4(rf(CJ_) + jb + 8 * jj);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    int isq, i, jb;
-                    tile_rc(u, isq, i, jb);
-                    if (ws + 4 * u < NT) {
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            f32x4 v;
-#pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                v[t] = isq ? cP * gt[u][4 * jj + t] : ea[u] * CJ4[u][jj][t] * gt[u][4 * jj + t];
-                            store4(u, jj, v);
-                        }
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    int isq, i, jb;
-                    tile_rc(u, isq, i, jb);
-                    if (ws + 4 * u < NT) {
-                        const float fi = rf(isq ? PQ_ : FA_)[i], Gi = rf(RG_)[i];
-                        f32x4 RK4[4], G4[4];
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            RK4[jj] = ld4(rf(RK_) + jb + 8 * jj);
-                            G4[jj] = ld4(rf(RG_) + jb + 8 * jj);
-                        }
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            f32x4 v;
-#pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                v[t] = fi * RK4[jj][t] * gt[u][4 * jj + t] * __expf(fminf(Gi - G4[jj][t], 0.f));
-                            store4(u, jj, v);
-                        }
-                    }
-                }
+            if (ws < 3) a_tile(gt[0], ws > 0, ws == 2);
+            if constexpr (OUT) {
+                if (ws == 3) p_tile(gt[0], 0, 0);
+                if (ws < 2) p_tile(gt[1], 1, ws);
             }
         }
         __syncthreads();
