@@ -142,7 +142,27 @@ def _kernel_stats(d):
     return rows
 
 
-def summarize_trace(base, out_path, command):
+def _dispatch_durations(d, name_part):
+    """Per-dispatch durations (microseconds, in launch order) of the kernels
+    whose name contains name_part, from the rocpd 'kernels' view."""
+    import sqlite3
+    out = []
+    for f in _db_files(d):
+        con = sqlite3.connect(f)
+        try:
+            cur = con.execute("select * from kernels")
+            cols = [c[0] for c in cur.description]
+            ni, si, ei = cols.index("name"), cols.index("start"), cols.index("end")
+            for row in cur.fetchall():
+                if name_part in str(row[ni]):
+                    out.append((row[si], (row[ei] - row[si]) / 1e3))
+        except (sqlite3.Error, ValueError):
+            pass
+        con.close()
+    return [dur for _, dur in sorted(out)]
+
+
+def summarize_trace(base, out_path, command, last=0):
     rows = _kernel_stats(base)
     lines = [f"# rocprofv3 --kernel-trace --stats summary (rocpd top_kernels; durations in microseconds)",
              f"# command: {command}",
@@ -151,6 +171,13 @@ def summarize_trace(base, out_path, command):
         short = name.replace("(anonymous namespace)", "anon").replace("void ", "")
         short = short[:short.rfind("(")] if "(" in short else short
         lines.append(f"{short[:100]} | {calls} | {avg:.3f} | {tot:.1f} | {pct:.2f}")
+    durs = _dispatch_durations(base, KERNEL)
+    if durs and last > 0:
+        tail = durs[-last:]
+        lines.append(f"# {KERNEL}: the last {len(tail)} dispatches (the timed steps, warmup excluded)")
+        lines.append(f"timed_dispatches = {len(tail)}")
+        lines.append(f"timed_average_us = {statistics.fmean(tail):.3f}")
+        lines.append(f"timed_median_us = {statistics.median(tail):.3f}")
     open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -235,6 +262,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 --pmc output dirs; the last argument is the output file")
     ap.add_argument("--trace-command", default="?")
+    ap.add_argument("--trace-last", type=int, default=0,
+                    help="with --summarize-trace: also average the last N dispatches of the scan kernel")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -250,7 +279,7 @@ def main():
                            json.loads(args.pmc_commands).get("commands", []))
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_command)
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_command, args.trace_last)
         return
 
     import torch

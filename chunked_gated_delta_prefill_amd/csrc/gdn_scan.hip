@@ -229,17 +229,13 @@ __device__ __forceinline__ float gate_value(uint32_t bits, int dt) {
 // Per-row factor arrays (64 floats each), written once per chunk.  The state
 // is held as S = sigma * S~ (sigma a per-sequence scalar, see the kernel); c
 // is the query scale:
-//   RG  in-chunk log-gate cumsum G_i        RK  rk_i (1 without L2 norm)
-//   RQ  rq_i                                FA  b_i rk_i            (rows of A)
-//   PQ  c rq_i                (rows of P)   FZ  sigma gamma_i rk_i  (rows of K S~^T)
-//   FB  b_i        (columns of T' = T diag(b))
-//   FY  c sigma gamma_i rq_i  (output rows)
-//   FU  rk_i exp(G_L - G_i) / sigma'        (state update; without / sigma' on renorm)
-//   EA  b_i rk_i gamma_i, CJ rk_j / gamma_j: A entries as a product when the
-//       chunk's total decay is moderate (no exp per entry)
+//   RG  in-chunk log-gate cumsum G_i   GM gamma_i = exp(G_i)   IG 1 / gamma_i
+//   DC  exp(G_L - G_i)                 FB b_i                  (b also scales T' columns)
+//   RK  rk_i, RQ rq_i  (1 without L2 norm; computed with the Gram tiles)
+//   FZ  sigma gamma_i rk_i   (rows of K S~^T)     FY  c sigma gamma_i rq_i  (output rows)
+//   FU  rk_i exp(G_L - G_i) / sigma'   (state update; without / sigma' on renorm)
 // followed by gamma_L.
-enum { RG_ = 0, RK_ = 1, RQ_ = 2, FA_ = 3, PQ_ = 4, FZ_ = 5, FB_ = 6, FY_ = 7, FU_ = 8, EA_ = 9, CJ_ = 10,
-       NROWF = 11 };
+enum { RG_ = 0, GM_ = 1, IG_ = 2, DC_ = 3, FB_ = 4, RK_ = 5, RQ_ = 6, FZ_ = 7, FY_ = 8, FU_ = 9, NROWF = 10 };
 constexpr float kFastDecay = -60.f;   // G_L above this: exp(G_i - G_j) = gamma_i / gamma_j is safe
 constexpr float kRenorm = 0x1p-40f;   // sigma below this is folded back into the state
 
@@ -264,7 +260,7 @@ template <typename IO> struct Smem {
 };
 
 // Sum over the 16 lanes of a DPP row (every lane gets the total).
-__device__ __forceinline__ float row_sum16(float x) {
+__device__ __forceinline__ __attribute__((unused)) float row_sum16(float x) {
     x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
     x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
     x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
@@ -470,7 +466,9 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], char *base, in
     }
 }
 
-constexpr int64_t kMapBytes = (int64_t)D * D * 4;   // one fp32 [128][128] block of the workspace
+constexpr int64_t kMapBytes = (int64_t)D * D * 4;
+// s_waitcnt operand for vmcnt(0) alone (expcnt and lgkmcnt at their maximum)
+constexpr int kWaitVmcnt0 = 0x0F70;   // one fp32 [128][128] block of the workspace
 
 // bf16: two workgroups per CU (LDS < 80 KB) need <= 256 registers per lane;
 // fp32 (LDS-bound to one workgroup per CU) keeps the full register file.
@@ -549,6 +547,12 @@ fused_scan_kernel(const ScanParams p) {
     float sigma = 1.f;          // true state = sigma * S (uniform across the workgroup)
     Prefetch<IO> pf;
     if (nchunks > 0) issue_loads<IO>(pf, p, chunk_at(bos, eos, 0), hq, h, threadIdx.x, threadIdx.x & 63, threadIdx.x >> 6);
+    // Wait for the first chunk's loads here, once.  In the loop the prefetch of
+    // chunk c + 1 is retired by the wait for chunk c's V, so the chunk head
+    // needs no vector-memory wait; without this the loop entry would make the
+    // head wait for everything outstanding, the previous chunk's output stores
+    // included.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     for (int c = 0; c < nchunks; ++c) {
         const ChunkRef ch = chunk_at(bos, eos, c);
@@ -563,56 +567,40 @@ fused_scan_kernel(const ScanParams p) {
         const int h32 = lane >> 5, l32 = lane & 31;
         const int v0 = ws * 32 + l32;
 
-        // ---- [L] stage K and Q, row norms; gates and the in-chunk log-gate cumsum
+        // ---- [L] stage K and Q; gates and the in-chunk log-gate cumsum
         if constexpr (BF) {
             const int rq4 = tid >> 4, cg = tid & 15;
 #pragma unroll
-            for (int mat = 0; mat < 2; ++mat) {
-                float ss[4];
+            for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const bf16x8 x = __builtin_bit_cast(bf16x8, pf.kq[mat][t]);
-                    ss[t] = row_sum16(sumsq8(x));
+                for (int t = 0; t < 4; ++t)
                     *reinterpret_cast<i32x4 *>((mat ? Qs : Ks) + (4 * rq4 + t) * L::KLD + 8 * cg) = pf.kq[mat][t];
-                }
-                if (cg == 0) {
-                    f32x4 rn;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) rn[t] = p.l2norm ? rsqrtf(ss[t] + 1e-6f) : 1.f;
-                    *reinterpret_cast<f32x4 *>(rf(mat ? RQ_ : RK_) + 4 * rq4) = rn;
-                }
-            }
         } else {
             const int r0 = tid >> 5, cg = tid & 31;
 #pragma unroll
             for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const f32x4 x = pf.kq[mat][j];
-                    float ss = row_sum16(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
-                    ss += __shfl_xor(ss, 16);
-                    *reinterpret_cast<f32x4 *>((mat ? Qs : Ks) + (r0 + 8 * j) * L::KLD + 4 * cg) = x;
-                    if (cg == 0) rf(mat ? RQ_ : RK_)[r0 + 8 * j] = p.l2norm ? rsqrtf(ss + 1e-6f) : 1.f;
-                }
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<f32x4 *>((mat ? Qs : Ks) + (r0 + 8 * j) * L::KLD + 4 * cg) = pf.kq[mat][j];
         }
         // wave 0, lane i = token i of the chunk
-        float g_G = 0.f, g_b = 0.f, g_gam = 1.f, g_dec = 1.f;
         if (ws == 0) {
             const bool valid = lane < Lc;
             const float ga = p.g ? gate_value(pf.g, p.g_dt) : 1.f;
             const float gb = p.beta ? gate_value(pf.b, p.b_dt) : 1.f;
             const float G = wave_prefix_sum(valid ? fmaxf(__logf(ga), -80.f) : 0.f);
             const float GL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
-            g_G = G;
-            g_b = valid ? gb : 0.f;
-            g_gam = __expf(G);
-            g_dec = __expf(GL - G);
+            const float gam = __expf(G);
             rf(RG_)[lane] = G;
-            if (lane == 63) RF[NROWF * C] = g_gam;    // gamma_L
+            rf(GM_)[lane] = gam;
+            rf(IG_)[lane] = __expf(-G);
+            rf(DC_)[lane] = __expf(GL - G);
+            rf(FB_)[lane] = valid ? gb : 0.f;
+            if (lane == 63) RF[NROWF * C] = gam;    // gamma_L
         }
         __syncthreads();
 
-        // ---- [A] per-row factors (wave 0); Gram tiles
+        // ---- [A] Gram tiles; row norms from their operands
         // The true state is sigma * S~.  After this chunk it is
         //   gamma_L sigma S~ + K^T U  =  sigma' (S~ + K^T U / sigma'),  sigma' = gamma_L sigma,
         // so the decay costs no per-element work; when sigma' gets small it is
@@ -623,21 +611,12 @@ fused_scan_kernel(const ScanParams p) {
         const bool renorm = !(sig_next >= kRenorm);
         const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                               int, rf(RG_)[C - 1]))) > kFastDecay;
-        if (ws == 0) {
-            const float rk = rf(RK_)[lane], rq = rf(RQ_)[lane];
-            rf(FA_)[lane] = g_b * rk;
-            rf(PQ_)[lane] = rq * p.scale;
-            rf(FZ_)[lane] = sigma * g_gam * rk;
-            rf(FB_)[lane] = g_b;
-            rf(FY_)[lane] = sigma * g_gam * rq * p.scale;
-            rf(FU_)[lane] = renorm ? rk * g_dec : rk * g_dec / sig_next;
-            rf(EA_)[lane] = g_b * rk * g_gam;
-            rf(CJ_)[lane] = rk / g_gam;
-        }
-        (void)g_G;
         // tiles (bi, bj) = (0,0) (1,0) (1,1) of K K^T (0..2) and Q K^T (3..5); wave w takes
         // w and w + 4.  Each is computed transposed: register rows are the column
         // index j = 32 bj + acc_row, the lane is the row index i = 32 bi + l32.
+        // The squared row norms come from the second operands as they are read:
+        // K rows 0..31 (wave 0, tile 0), K rows 32..63 (wave 1, tile 1), Q rows
+        // 0..31 (wave 3, tile 3), Q rows 32..63 (wave 0, tile 4).
         f32x16 gt[2] = {zero16(), zero16()};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -646,10 +625,22 @@ fused_scan_kernel(const ScanParams p) {
                 const int isq = tile >= 3, tt = tile - 3 * isq;
                 const int bi = tt > 0, bj = tt == 2;
                 const IO *As = isq ? Qs : Ks;
+                const bool norm = u == 0 ? ws != 2 : ws == 0;
+                float ss = 0.f;
 #pragma unroll
-                for (int s = 0; s < D / (2 * E); ++s)
-                    gt[u] = M::run(ld_nat<IO>(Ks, L::KLD, 32 * bj + l32, s, h32),
-                                   ld_nat<IO>(As, L::KLD, 32 * bi + l32, s, h32), gt[u]);
+                for (int s = 0; s < D / (2 * E); ++s) {
+                    const frag fb = ld_nat<IO>(As, L::KLD, 32 * bi + l32, s, h32);
+                    gt[u] = M::run(ld_nat<IO>(Ks, L::KLD, 32 * bj + l32, s, h32), fb, gt[u]);
+                    if (norm) {
+                        if constexpr (BF) ss += sumsq8(fb);
+                        else ss = fmaf(fb, fb, ss);
+                    }
+                }
+                if (norm) {
+                    ss += __shfl_xor(ss, 32);
+                    if (h32 == 0)
+                        rf(isq ? RQ_ : RK_)[32 * bi + l32] = p.l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;
+                }
             }
         }
         __syncthreads();
@@ -675,17 +666,20 @@ fused_scan_kernel(const ScanParams p) {
             auto a_tile = [&](const f32x16 &acc, int bi, int bj) {
                 const int i = 32 * bi + l32, jb = 32 * bj + 4 * h32;
                 f32x4 v[4];
-                if (fast) {
-                    const float ea = rf(EA_)[i];
-                    f32x4 cj[4];
+                if (fast) {   // (b_i rk_i gamma_i) (rk_j / gamma_j) (k_i . k_j)
+                    const float ea = rf(FB_)[i] * rf(RK_)[i] * rf(GM_)[i];
+                    f32x4 rk[4], ig[4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) cj[jj] = ld4(rf(CJ_) + jb + 8 * jj);
+                    for (int jj = 0; jj < 4; ++jj) {
+                        rk[jj] = ld4(rf(RK_) + jb + 8 * jj);
+                        ig[jj] = ld4(rf(IG_) + jb + 8 * jj);
+                    }
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[jj][t] = ea * cj[jj][t] * acc[4 * jj + t];
+                        for (int t = 0; t < 4; ++t) v[jj][t] = ea * (rk[jj][t] * ig[jj][t]) * acc[4 * jj + t];
                 } else {
-                    const float fi = rf(FA_)[i], Gi = rf(RG_)[i];
+                    const float fi = rf(FB_)[i] * rf(RK_)[i], Gi = rf(RG_)[i];
                     f32x4 rk[4], G4[4];
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
@@ -713,7 +707,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[jj][t] = cP * acc[4 * jj + t];
                 } else {
-                    const float fi = rf(PQ_)[i], Gi = rf(RG_)[i];
+                    const float fi = p.scale * rf(RQ_)[i], Gi = rf(RG_)[i];
                     f32x4 rk[4], G4[4];
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
@@ -741,6 +735,12 @@ fused_scan_kernel(const ScanParams p) {
             if constexpr (OUT) {
                 if (ws == 3) p_tile(gt[0], 0, 0);
                 if (ws < 2) p_tile(gt[1], 1, ws);
+            }
+            if (ws == 2) {   // row factors of [D], lane = token
+                const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
+                rf(FZ_)[lane] = sigma * gam * rk;
+                rf(FU_)[lane] = renorm ? rk * dec : rk * dec / sig_next;
+                if constexpr (OUT) rf(FY_)[lane] = sigma * gam * rf(RQ_)[lane] * p.scale;
             }
         }
         __syncthreads();
