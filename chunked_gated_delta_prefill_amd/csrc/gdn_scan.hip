@@ -297,12 +297,16 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // 32x32 bf16 A operand of a product contracting over tokens, rows = K columns
 // [m0, m0 + 32), read straight from row-major K with the transposing LDS load
 // (within 16 lanes, output lane i element e comes from source lane i/4 + 4e,
-// element i%4; source lane j points at token t0 + j/4, column m0' + 4 (j%4)).
-// Slots follow the accumulator order of ld_acc: tokens cb + 16s + 4h + {0..3}
-// and the same + 8.
+// element i%4; source lane j points at token t0 + j/4 and at the 4 columns of
+// output lanes 4 (j%4) .. 4 (j%4) + 3).  Slots follow the accumulator order of
+// ld_acc: tokens cb + 16s + 4h + {0..3} and the same + 8.  Operand row m holds
+// K column m0 + m with bits 2 and 3 of m swapped, so that the product's
+// accumulator register r of half h is column m0 + 16 (r/8) + 8h + r%8: the
+// state's natural operand order.
 __device__ __forceinline__ bf16x8 ld_acc_tr(const bf16 *Ks, int ld, int m0, int cb, int s, int lane) {
     const int i = lane & 15, h = lane >> 5, g16 = (lane >> 4) & 1;
-    const bf16 *p = Ks + (cb + 16 * s + 4 * h + (i >> 2)) * ld + m0 + 16 * g16 + 4 * (i & 3);
+    const int q = i & 3, qs = ((q & 1) << 1) | (q >> 1);
+    const bf16 *p = Ks + (cb + 16 * s + 4 * h + (i >> 2)) * ld + m0 + 16 * g16 + 4 * qs;
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * ld));
@@ -410,39 +414,44 @@ __device__ __forceinline__ ChunkRef chunk_at(int64_t bos, int64_t eos, int c) {
     return ch;
 }
 
-// ---- state I/O: accumulator tiles S[b] (S^T rows k = 32b + acc_row(r, h32),
-// column v0) <-> a V-major [128][128] block at `base` with row stride `rs` bytes.
+// ---- state I/O: accumulator tiles S[b] (S^T rows k, column v0) <-> a V-major
+// [128][128] block at `base` with row stride `rs` bytes.  Register r of half h32
+// holds k = 32 b + acc_row(r, h32) in accumulator order (NAT = false) or
+// k = 32 b + 16 (r / 8) + 8 h32 + r % 8 in natural operand order (NAT = true).
+template <bool NAT> __device__ __forceinline__ int state_k(int bb, int r, int h32) {
+    return NAT ? 32 * bb + 16 * (r >> 3) + 8 * h32 + (r & 7) : 32 * bb + acc_row(r, h32);
+}
+
+template <bool NAT>
 __device__ __forceinline__ void load_state(f32x16 (&S)[4], const char *base, int rs, int dt, int v0, int h32) {
     const auto r = rsrc(base, (int64_t)D * rs);
     if (dt == GDN_F32) {
-        const int vo = v0 * rs + 16 * h32;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 x =
-                    __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vo + 4 * (32 * bb + 8 * j), 0, 0));
+            for (int j = 0; j < 4; ++j) {     // registers 4j .. 4j+3 hold 4 consecutive k
+                const f32x4 x = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, v0 * rs + 4 * state_k<NAT>(bb, 4 * j, h32), 0, 0));
 #pragma unroll
                 for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = x[t];
             }
     } else {
-        const int vo = v0 * rs + 8 * h32;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bf16x4 x =
-                    __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, vo + 2 * (32 * bb + 8 * j), 0, 0));
+                const bf16x4 x = __builtin_bit_cast(
+                    bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, v0 * rs + 2 * state_k<NAT>(bb, 4 * j, h32), 0, 0));
 #pragma unroll
                 for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = (float)x[t];
             }
     }
 }
 
+template <bool NAT>
 __device__ __forceinline__ void store_state(const f32x16 (&S)[4], char *base, int rs, int dt, int v0, int h32) {
     const auto r = rsrc(base, (int64_t)D * rs);
     if (dt == GDN_F32) {
-        const int vo = v0 * rs + 16 * h32;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
@@ -450,10 +459,10 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], char *base, in
                 f32x4 x;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) x[t] = S[bb][4 * j + t];
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, vo + 4 * (32 * bb + 8 * j), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r,
+                                                       v0 * rs + 4 * state_k<NAT>(bb, 4 * j, h32), 0, 0);
             }
     } else {
-        const int vo = v0 * rs + 8 * h32;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
@@ -461,7 +470,8 @@ __device__ __forceinline__ void store_state(const f32x16 (&S)[4], char *base, in
                 bf16x4 x;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) x[t] = (bf16)S[bb][4 * j + t];
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, vo + 2 * (32 * bb + 8 * j), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r,
+                                                      v0 * rs + 2 * state_k<NAT>(bb, 4 * j, h32), 0, 0);
             }
     }
 }
@@ -532,14 +542,14 @@ fused_scan_kernel(const ScanParams p) {
         const int h32 = lane >> 5, v0 = ws * 32 + (lane & 31);
         if (MODE == kScan) {
             if (!first)
-                load_state(S, reinterpret_cast<const char *>(p.ws_sin) + map_off, D * 4, GDN_F32, v0, h32);
+                load_state<BF>(S, reinterpret_cast<const char *>(p.ws_sin) + map_off, D * 4, GDN_F32, v0, h32);
             else if (p.s_in)
-                load_state(S, p.s_in + n * p.si_n + h * p.si_h, p.si_v, p.si_dt, v0, h32);
+                load_state<BF>(S, p.s_in + n * p.si_n + h * p.si_h, p.si_v, p.si_dt, v0, h32);
         } else if (MODE == kMapM) {           // identity: S^T[k][v0] = (k == v0)
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) S[bb][rr] = (32 * bb + acc_row(rr, h32) == v0) ? 1.f : 0.f;
+                for (int rr = 0; rr < 16; ++rr) S[bb][rr] = (state_k<BF>(bb, rr, h32) == v0) ? 1.f : 0.f;
         }
     }
 
@@ -611,37 +621,95 @@ fused_scan_kernel(const ScanParams p) {
         const bool renorm = !(sig_next >= kRenorm);
         const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                               int, rf(RG_)[C - 1]))) > kFastDecay;
-        // tiles (bi, bj) = (0,0) (1,0) (1,1) of K K^T (0..2) and Q K^T (3..5); wave w takes
-        // w and w + 4.  Each is computed transposed: register rows are the column
-        // index j = 32 bj + acc_row, the lane is the row index i = 32 bi + l32.
-        // The squared row norms come from the second operands as they are read:
-        // K rows 0..31 (wave 0, tile 0), K rows 32..63 (wave 1, tile 1), Q rows
-        // 0..31 (wave 3, tile 3), Q rows 32..63 (wave 0, tile 4).
+        // Gram tiles (bi, bj) = (0,0) (1,0) (1,1) of K K^T ("A" tiles) and Q K^T ("P"
+        // tiles), each computed transposed: register rows are the column index
+        // j = 32 bj + acc_row, the lane is the row index i = 32 bi + l32.
+        // One pass over the 128-wide contraction reads, per step, the fragments of
+        // K_0, K_1, Q_0, Q_1 (K_b / Q_b = rows 32b .. 32b+31) once and feeds:
+        //   X = K S~^T and (S~ Q^T) for this wave's 32 state rows (S~ as the A operand
+        //   gives the transpose), four accumulator chains;
+        //   this wave's Gram tiles (first operand = K rows of the column block):
+        //     wave 0: A(0,0) = K_0 K_0, P(1,0) = K_0 Q_1      norms of K_0, Q_1
+        //     wave 1: A(1,0) = K_0 K_1, P(1,1) = K_1 Q_1      norms of K_1
+        //     wave 2: A(1,1) = K_1 K_1 (two accumulators: even / odd steps)
+        //     wave 3: P(0,0) = K_0 Q_0 (two accumulators)      norms of Q_0
+        //   the squared row norms (dot2 on the fragments).
+        // The contraction runs in the state's register order (natural for bf16,
+        // accumulator order for fp32); the next step's fragments are read while
+        // this step's MFMAs run.
         f32x16 gt[2] = {zero16(), zero16()};
+        f32x16 X[2] = {zero16(), zero16()}, Y[2] = {zero16(), zero16()};
+        {
+            constexpr int NK = 4 * S32;
+            auto frag_at = [&](const IO *M, int blk, int k) -> frag {
+                if constexpr (BF) return ld_nat<IO>(M, L::KLD, 32 * blk + l32, k, h32);
+                else return ld_acc<IO>(M, L::KLD, 32 * blk + l32, 32 * (k / S32), k % S32, h32);
+            };
+            auto sq = [&](const frag &f) {
+                if constexpr (BF) return sumsq8(f);
+                else return f * f;
+            };
+            auto put_norm = [&](float ss, int which, int blk) {
+                ss += __shfl_xor(ss, 32);
+                if (h32 == 0) rf(which)[32 * blk + l32] = p.l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;
+            };
+            auto pass = [&](auto role) {
+                constexpr int R = decltype(role)::value;
+                frag fk[2][2], fq[2][2];
+                auto load = [&](int k, int st) {
+                    fk[st][0] = frag_at(Ks, 0, k);
+                    fk[st][1] = frag_at(Ks, 1, k);
+                    if constexpr (OUT) {
+                        fq[st][0] = frag_at(Qs, 0, k);
+                        fq[st][1] = frag_at(Qs, 1, k);
+                    }
+                };
+                float ssa = 0.f, ssb = 0.f;
+                load(0, 0);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tile = ws + 4 * u;
-            if (tile < (OUT ? 6 : 3)) {
-                const int isq = tile >= 3, tt = tile - 3 * isq;
-                const int bi = tt > 0, bj = tt == 2;
-                const IO *As = isq ? Qs : Ks;
-                const bool norm = u == 0 ? ws != 2 : ws == 0;
-                float ss = 0.f;
-#pragma unroll
-                for (int s = 0; s < D / (2 * E); ++s) {
-                    const frag fb = ld_nat<IO>(As, L::KLD, 32 * bi + l32, s, h32);
-                    gt[u] = M::run(ld_nat<IO>(Ks, L::KLD, 32 * bj + l32, s, h32), fb, gt[u]);
-                    if (norm) {
-                        if constexpr (BF) ss += sumsq8(fb);
-                        else ss = fmaf(fb, fb, ss);
+                for (int k = 0; k < NK; ++k) {
+                    const int cur = k & 1;
+                    if (k + 1 < NK) load(k + 1, cur ^ 1);
+                    const frag sf = acc_frag<IO>(S[k / S32], k % S32);
+                    const frag k0 = fk[cur][0], k1 = fk[cur][1];
+                    X[0] = M::run(k0, sf, X[0]);
+                    X[1] = M::run(k1, sf, X[1]);
+                    if constexpr (OUT) {
+                        Y[0] = M::run(sf, fq[cur][0], Y[0]);
+                        Y[1] = M::run(sf, fq[cur][1], Y[1]);
+                    }
+                    if constexpr (R == 0) {
+                        gt[0] = M::run(k0, k0, gt[0]);
+                        ssa += sq(k0);
+                        if constexpr (OUT) {
+                            gt[1] = M::run(k0, fq[cur][1], gt[1]);
+                            ssb += sq(fq[cur][1]);
+                        }
+                    } else if constexpr (R == 1) {
+                        gt[0] = M::run(k0, k1, gt[0]);
+                        ssa += sq(k1);
+                        if constexpr (OUT) gt[1] = M::run(k1, fq[cur][1], gt[1]);
+                    } else if constexpr (R == 2) {
+                        gt[cur] = M::run(k1, k1, gt[cur]);
+                    } else if constexpr (OUT) {
+                        gt[cur] = M::run(k0, fq[cur][0], gt[cur]);
+                        ssb += sq(fq[cur][0]);
                     }
                 }
-                if (norm) {
-                    ss += __shfl_xor(ss, 32);
-                    if (h32 == 0)
-                        rf(isq ? RQ_ : RK_)[32 * bi + l32] = p.l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;
+                if constexpr (R == 0) {
+                    put_norm(ssa, RK_, 0);
+                    if constexpr (OUT) put_norm(ssb, RQ_, 1);
+                } else if constexpr (R == 1) {
+                    put_norm(ssa, RK_, 1);
+                } else {
+                    gt[0] += gt[1];
+                    if constexpr (R == 3 && OUT) put_norm(ssb, RQ_, 0);
                 }
-            }
+            };
+            if (ws == 0) pass(std::integral_constant<int, 0>{});
+            else if (ws == 1) pass(std::integral_constant<int, 1>{});
+            else if (ws == 2) pass(std::integral_constant<int, 2>{});
+            else pass(std::integral_constant<int, 3>{});
         }
         __syncthreads();
 
@@ -856,43 +924,22 @@ fused_scan_kernel(const ScanParams p) {
         //   output, computed transposed (lane = token t, registers = 4 consecutive v):
         //     fast: O^T = FY_t [ (S~ Q^T) + ub^T P^T ]   (P = masked q.k, see [B])
         //     slow: O^T = FY_t (S~ Q^T) + Vnew^T P^T
+        // Z' = V - FZ o X, as the bf16 operand of Vnew = T' Z'
         frag zb[2][S32];
-        f32x16 Y[2] = {zero16(), zero16()};
         {
-            frag sb[4][S32];
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                for (int s = 0; s < S32; ++s) sb[bb][s] = acc_frag<IO>(S[bb], s);
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
-                f32x16 X = zero16();
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                    for (int s = 0; s < S32; ++s)
-                        X = M::run(ld_acc<IO>(Ks, L::KLD, 32 * ib + l32, 32 * bb, s, h32), sb[bb][s], X);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const f32x4 fz = ld4(rf(FZ_) + 32 * ib + 8 * jj + 4 * h32);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const int rr = 4 * jj + t;
-                        X[rr] = fmaf(-fz[t], X[rr], vreg_at(vcur, 16 * ib + rr, BF));
+                        X[ib][rr] = fmaf(-fz[t], X[ib][rr], vreg_at(vcur, 16 * ib + rr, BF));
                     }
                 }
 #pragma unroll
-                for (int s = 0; s < S32; ++s) zb[ib][s] = acc_frag<IO>(X, s);
-            }
-            // (S~ Q^T) for this wave's state rows: S~ as the A operand gives the transpose
-            if constexpr (OUT) {
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                        for (int s = 0; s < S32; ++s)
-                            Y[ib] = M::run(sb[bb][s], ld_acc<IO>(Qs, L::KLD, 32 * ib + l32, 32 * bb, s, h32), Y[ib]);
+                for (int st = 0; st < S32; ++st) zb[ib][st] = acc_frag<IO>(X[ib], st);
             }
         }
         // Vnew = T' Z'   (T' lower block-triangular: skip the zero upper 32x32 block)
@@ -978,17 +1025,26 @@ fused_scan_kernel(const ScanParams p) {
         } else {
             sigma = sig_next;
         }
+        {   // S~ += K^T ub: the four state tiles are independent chains; the K^T
+            // fragments of the next contraction step are read while this step runs
+            constexpr int NU = 2 * S32;
+            frag kt[2][4];
+            auto load_kt = [&](int k, frag (&f)[4]) {
+                const int ib = k / S32, st = k % S32;
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int s = 0; s < S32; ++s) {
-                    frag a;
-                    if constexpr (BF) a = ld_acc_tr(Ks, L::KLD, 32 * bb, 32 * ib, s, lane);
-                    else a = ld_acc_t<float>(Ks, L::KLD, 32 * bb + l32, 32 * ib, s, h32);
-                    S[bb] = M::run(a, ub[ib][s], S[bb]);
+                for (int bb = 0; bb < 4; ++bb) {
+                    if constexpr (BF) f[bb] = ld_acc_tr(Ks, L::KLD, 32 * bb, 32 * ib, st, lane);
+                    else f[bb] = ld_acc_t<float>(Ks, L::KLD, 32 * bb + l32, 32 * ib, st, h32);
                 }
+            };
+            load_kt(0, kt[0]);
+#pragma unroll
+            for (int k = 0; k < NU; ++k) {
+                const int cur = k & 1;
+                if (k + 1 < NU) load_kt(k + 1, kt[cur ^ 1]);
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) S[bb] = M::run(kt[cur][bb], ub[k / S32][k % S32], S[bb]);
+            }
         }
         __syncthreads();
     }
@@ -1006,9 +1062,9 @@ fused_scan_kernel(const ScanParams p) {
         const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
         const int h32 = lane >> 5, v0 = ws * 32 + (lane & 31);
         if (MODE == kScan)
-            store_state(S, p.s_out + n * p.so_n + h * p.so_h, p.so_v, p.so_dt, v0, h32);
+            store_state<BF>(S, p.s_out + n * p.so_n + h * p.so_h, p.so_v, p.so_dt, v0, h32);
         else
-            store_state(S, reinterpret_cast<char *>(MODE == kMapN ? p.ws_n : p.ws_m) + map_off, D * 4, GDN_F32, v0,
+            store_state<BF>(S, reinterpret_cast<char *>(MODE == kMapN ? p.ws_n : p.ws_m) + map_off, D * 4, GDN_F32, v0,
                         h32);
     }
 }
@@ -1083,7 +1139,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(const FixParams f) {
     f32x16 S[4];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) S[bb] = zero16();
-    if (f.s_in) load_state(S, f.s_in + n * f.si_n + h * f.si_h, f.si_v, f.si_dt, v0, h32);
+    if (f.s_in) load_state<false>(S, f.s_in + n * f.si_n + h * f.si_h, f.si_v, f.si_dt, v0, h32);
     for (int i = 0; i + 1 < cnt; ++i) {
         const int64_t off = ((int64_t)(s0 + i) * f.Hv + h) * kMapBytes;
         const float *Mg = reinterpret_cast<const float *>(reinterpret_cast<const char *>(f.ws_m) + off);
@@ -1093,7 +1149,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(const FixParams f) {
         }
         __syncthreads();
         f32x16 Sn[4];
-        load_state(Sn, reinterpret_cast<const char *>(f.ws_n) + off, D * 4, GDN_F32, v0, h32);
+        load_state<false>(Sn, reinterpret_cast<const char *>(f.ws_n) + off, D * 4, GDN_F32, v0, h32);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -1104,7 +1160,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(const FixParams f) {
                                                                   S[cb][st], Sn[mb], 0, 0, 0);
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) S[bb] = Sn[bb];
-        store_state(S, reinterpret_cast<char *>(f.ws_sin) + ((int64_t)(s0 + i + 1) * f.Hv + h) * kMapBytes, D * 4,
+        store_state<false>(S, reinterpret_cast<char *>(f.ws_sin) + ((int64_t)(s0 + i + 1) * f.Hv + h) * kMapBytes, D * 4,
                     GDN_F32, v0, h32);
         __syncthreads();
     }
