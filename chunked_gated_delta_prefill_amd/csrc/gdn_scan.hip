@@ -406,6 +406,20 @@ __device__ __forceinline__ void issue_v(VRegs &vr, const ScanParams &p, ChunkRef
     else vall(false);
 }
 
+// bf16 V: each wave loads the 64 x 32 block of its own state columns with
+// 16-byte loads (token 16 j + lane / 4, columns 32 ws + 8 (lane % 4) .. + 8);
+// rows past the chunk end fall outside the buffer range and load zeros.
+struct VWide {
+    i32x4 x[4];
+};
+__device__ __forceinline__ void issue_v_wide(VWide &vw, const ScanParams &p, ChunkRef ch, int h, int ws, int lane) {
+    const int L = ch.L;
+    const auto rv = rsrc(p.v + ch.t0 * p.v_st + h * p.v_sh, L > 0 ? (L - 1) * p.v_st + D * 2 : 0);
+    const int vo = (lane >> 2) * p.v_st + (32 * ws + 8 * (lane & 3)) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vw.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * j * p.v_st, 0, 0);
+}
+
 __device__ __forceinline__ ChunkRef chunk_at(int64_t bos, int64_t eos, int c) {
     ChunkRef ch;
     ch.t0 = bos + (int64_t)c * C;
@@ -815,9 +829,12 @@ fused_scan_kernel(const ScanParams p) {
 
         // ---- [C] this chunk's V in flight (first read in [D]); T' = (I + A)^-1:
         // each wave inverts one 16x16 diagonal block, then one wave merges them
-        VRegs vcur;
-        if constexpr (HASV) issue_v<IO>(vcur, p, ch, h, h32, v0);
-        else {
+        VRegs vcur;       // fp32: one element per register, accumulator layout
+        VWide vwide;      // bf16: 16-byte loads, moved to the accumulator layout through LDS in [D]
+        if constexpr (HASV) {
+            if constexpr (BF) issue_v_wide(vwide, p, ch, h, ws, lane);
+            else issue_v<IO>(vcur, p, ch, h, h32, v0);
+        } else {
 #pragma unroll
             for (int e = 0; e < 32; ++e) vcur.x[e] = 0u;
         }
@@ -927,6 +944,28 @@ fused_scan_kernel(const ScanParams p) {
         // Z' = V - FZ o X, as the bf16 operand of Vnew = T' Z'
         frag zb[2][S32];
         {
+            // bf16 V: this wave's 64 x 32 block goes through its own 4 KB of the
+            // (now free) A area and comes back with transposing reads as 4
+            // consecutive tokens of one column: registers 4q .. 4q+3 of tile ib.
+            float vv[2][16];
+            if constexpr (BF && HASV) {
+                bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::AF_OFF) + ws * (C * 32);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<i32x4 *>(Vw + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = vwide.x[j];
+                const int i = lane & 15, g16 = (lane >> 4) & 1;
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bf16 *src = Vw + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
+                        const bf16x4 x =
+                            __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src));
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) vv[ib][4 * q + t] = (float)x[t];
+                    }
+            }
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
@@ -935,7 +974,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const int rr = 4 * jj + t;
-                        X[ib][rr] = fmaf(-fz[t], X[ib][rr], vreg_at(vcur, 16 * ib + rr, BF));
+                        X[ib][rr] = fmaf(-fz[t], X[ib][rr], BF && HASV ? vv[ib][rr] : vreg_at(vcur, 16 * ib + rr, BF));
                     }
                 }
 #pragma unroll
