@@ -99,10 +99,6 @@ template <> struct Mma<float> {
     }
 };
 
-__device__ __forceinline__ f32x4 mfma16f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 // Row of 32x32 accumulator register r for half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -251,7 +247,11 @@ template <typename IO> struct Smem {
     static constexpr int P_OFF = Q_OFF + KB;
     static constexpr int T_OFF = P_OFF + C * OLD * (int)sizeof(IO);
     static constexpr int AF_OFF = T_OFF + C * OLD * (int)sizeof(IO);
-    static constexpr int ROW_OFF = AF_OFF + C * FLD * 4;
+    // diagonal 16x16 blocks of A, transposed (NT[b][m][i] = A[16b + i][16b + m]),
+    // block stride padded so the four blocks' broadcast reads use different banks
+    static constexpr int NTS = 16 * 16 + 4;
+    static constexpr int NT_OFF = AF_OFF + C * FLD * 4;
+    static constexpr int ROW_OFF = NT_OFF + 4 * NTS * 4;
     static constexpr int BYTES = ROW_OFF + (NROWF * C + 4) * 4;
     static_assert(!BF || BYTES <= 80 * 1024, "two workgroups per CU");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
@@ -517,6 +517,7 @@ fused_scan_kernel(const ScanParams p) {
     IO *Ts = reinterpret_cast<IO *>(smem + L::T_OFF);
     float *Af = reinterpret_cast<float *>(smem + L::AF_OFF);
     float *RF = reinterpret_cast<float *>(smem + L::ROW_OFF);     // per-row factors
+    float *NT = reinterpret_cast<float *>(smem + L::NT_OFF);      // transposed diagonal blocks of A
     auto rf = [&](int which) { return RF + which * C; };
 
     // ---- work item: XCD-aware so the r value heads of one q/k head meet in one L2
@@ -779,6 +780,15 @@ fused_scan_kernel(const ScanParams p) {
                     mask_row(v[jj], i, jb + 8 * jj, 0);
                     *reinterpret_cast<f32x4 *>(Af + i * L::FLD + jb + 8 * jj) = v[jj];
                 }
+                if (bi == bj) {   // this lane's row lies in diagonal block 2 bi + (l32 >= 16)
+                    const int hi = l32 >= 16;
+                    float *nt = NT + (2 * bi + hi) * L::NTS + (l32 & 15);
+#pragma unroll
+                    for (int jr = 0; jr < 2; ++jr)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            nt[(8 * jr + 4 * h32 + t) * 16] = hi ? v[2 + jr][t] : v[jr][t];
+                }
             };
             auto p_tile = [&](const f32x16 &acc, int bi, int bj) {
                 const int i = 32 * bi + l32, jb = 32 * bj + 4 * h32;
@@ -827,8 +837,8 @@ fused_scan_kernel(const ScanParams p) {
         }
         __syncthreads();
 
-        // ---- [C] this chunk's V in flight (first read in [D]); T' = (I + A)^-1:
-        // each wave inverts one 16x16 diagonal block, then one wave merges them
+        // ---- [C] this chunk's V in flight (first read in [D]); wave 0: T' = (I + A)^-1
+        // (diagonal 16x16 blocks by forward substitution, then 16->32->64 merges)
         VRegs vcur;       // fp32: one element per register, accumulator layout
         VWide vwide;      // bf16: 16-byte loads, moved to the accumulator layout through LDS in [D]
         if constexpr (HASV) {
@@ -838,56 +848,46 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
             for (int e = 0; e < 32; ++e) vcur.x[e] = 0u;
         }
-        {
-            // (1) D = (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly
-            // lower block N (N^16 = 0), on fp32 16x16x4 MFMAs.  An accumulator X
-            // (register r of lane group g holds X[4g + r][lane % 16]) serves as the B
-            // operand X, or as the A operand X^T, with contraction index 4g + s at
-            // step s; the transposed powers are carried so every product reads
-            // operands straight from accumulators.
-            const int g = lane >> 4, nn = lane & 15;
-            float *blk = Af + (16 * ws) * L::FLD + 16 * ws;
-            const float bcol = rf(FB_)[16 * ws + nn];
-            const f32x4 nrow = ld4(blk + nn * L::FLD + 4 * g);      // N[nn][4g + s]
-            f32x4 ncol;                                              // N[4g + s][nn]
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ncol[q] = blk[(4 * g + q) * L::FLD + nn];
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            f32x4 n2 = z4, n2t = z4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                n2 = mfma16f32(nrow[q], ncol[q], n2);      // N N
-                n2t = mfma16f32(ncol[q], nrow[q], n2t);    // N^T N^T
-            }
-            f32x4 m2 = n2;                                 // I + N^2
-#pragma unroll
-            for (int q = 0; q < 4; ++q) m2[q] += (4 * g + q == nn) ? 1.f : 0.f;
-            f32x4 n4 = z4, n4t = z4, r1 = m2;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                n4 = mfma16f32(n2t[q], n2[q], n4);         // N^2 N^2
-                n4t = mfma16f32(n2[q], n2t[q], n4t);       // (N^2)^T (N^2)^T
-                r1 = mfma16f32(-nrow[q], m2[q], r1);       // (I + N^2) - N (I + N^2)
-            }
-            f32x4 n8t = z4, r2 = r1;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                n8t = mfma16f32(n4[q], n4t[q], n8t);       // (N^4)^T (N^4)^T
-                r2 = mfma16f32(n4t[q], r1[q], r2);         // R1 + N^4 R1
-            }
-            f32x4 dinv = r2;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dinv = mfma16f32(n8t[q], r2[q], dinv);   // R2 + N^8 R2
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i = 4 * g + q;
-                blk[i * L::FLD + nn] = dinv[q];
-                Ts[(16 * ws + i) * L::OLD + 16 * ws + nn] = (IO)(dinv[q] * bcol);
-                if ((ws & 1) == 0) Ts[(16 * ws + i) * L::OLD + 16 * ws + 16 + nn] = (IO)0.f;
-            }
-        }
-        __syncthreads();
         if (ws == 0) {
+            // (1) D = (I + N)^-1 for the four strictly lower 16x16 diagonal blocks N,
+            // by right-looking forward substitution: lane = (block bk, column cc)
+            // holds column cc of D; step m subtracts N[i][m] x_m from every later
+            // row i (independent FMAs), with column m of N read from the transposed
+            // copy (one broadcast read per block) one step ahead.
+            {
+                const int bk = lane >> 4, cc = lane & 15;
+                float x[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) x[i] = i == cc ? 1.f : 0.f;
+                // only the 4-row groups below the diagonal are read; the read offset and
+                // the column pass through an opaque copy each step so that the compiler
+                // keeps the reads one step ahead instead of hoisting all of them
+                f32x4 col[2][4];
+                int ofs = bk * L::NTS;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) col[0][q] = ld4(NT + ofs + 4 * q);
+#pragma unroll
+                for (int m = 0; m < 15; ++m) {
+                    asm volatile("" : "+v"(ofs), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]),
+                                 "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]),
+                                 "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+                    if (m + 1 < 15) {
+#pragma unroll
+                        for (int q = (m + 2) >> 2; q < 4; ++q) col[(m + 1) & 1][q] = ld4(NT + ofs + (m + 1) * 16 + 4 * q);
+                    }
+                    const float xm = x[m];
+#pragma unroll
+                    for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-col[m & 1][i >> 2][i & 3], xm, x[i]);
+                }
+                const float bcol = rf(FB_)[16 * bk + cc];
+                float *blk = Af + (16 * bk) * L::FLD + 16 * bk;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    blk[i * L::FLD + cc] = x[i];
+                    Ts[(16 * bk + i) * L::OLD + 16 * bk + cc] = (IO)(x[i] * bcol);
+                    if ((bk & 1) == 0) Ts[(16 * bk + i) * L::OLD + 16 * bk + 16 + cc] = (IO)0.f;
+                }
+            }
             // (2) 16 -> 32: T'_{2x+1,2x} = -D_{2x+1} A_{2x+1,2x} D_{2x}, x = 0, 1
             {
                 const int g = lane >> 4, nn = lane & 15;
