@@ -247,8 +247,8 @@ template <typename IO> struct Smem {
     static constexpr int P_OFF = Q_OFF + KB;
     static constexpr int T_OFF = P_OFF + C * OLD * (int)sizeof(IO);
     static constexpr int AF_OFF = T_OFF + C * OLD * (int)sizeof(IO);
-    // diagonal 16x16 blocks of A, transposed (NT[b][m][i] = A[16b + i][16b + m]),
-    // block stride padded so the four blocks' broadcast reads use different banks
+    // diagonal 16x16 blocks of A, transposed: NT[b][m][4 (i % 4) + i / 4] = A[16b + i][16b + m]
+    // (column m, rows grouped by i % 4); block stride padded against bank conflicts
     static constexpr int NTS = 16 * 16 + 4;
     static constexpr int NT_OFF = AF_OFF + C * FLD * 4;
     static constexpr int ROW_OFF = NT_OFF + 4 * NTS * 4;
@@ -258,6 +258,17 @@ template <typename IO> struct Smem {
     static_assert(Q_OFF % 16 == 0 && AF_OFF % 16 == 0 && T_OFF % 16 == 0 &&
                   ROW_OFF % 16 == 0, "align");
 };
+
+// Element e of each lane quad, broadcast to the quad (DPP quad_perm [e, e, e, e]).
+__device__ __forceinline__ float quad_bcast(float v, int e) {
+    const int b = __builtin_bit_cast(int, v);
+    switch (e) {
+        case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x00, 0xf, 0xf, false));
+        case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x55, 0xf, 0xf, false));
+        case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xaa, 0xf, 0xf, false));
+        default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xff, 0xf, 0xf, false));
+    }
+}
 
 // Sum over the 16 lanes of a DPP row (every lane gets the total).
 __device__ __forceinline__ __attribute__((unused)) float row_sum16(float x) {
@@ -782,7 +793,8 @@ fused_scan_kernel(const ScanParams p) {
                 }
                 if (bi == bj) {   // this lane's row lies in diagonal block 2 bi + (l32 >= 16)
                     const int hi = l32 >= 16;
-                    float *nt = NT + (2 * bi + hi) * L::NTS + (l32 & 15);
+                    const int ir = l32 & 15;
+                    float *nt = NT + (2 * bi + hi) * L::NTS + 4 * (ir & 3) + (ir >> 2);
 #pragma unroll
                     for (int jr = 0; jr < 2; ++jr)
 #pragma unroll
@@ -837,8 +849,8 @@ fused_scan_kernel(const ScanParams p) {
         }
         __syncthreads();
 
-        // ---- [C] this chunk's V in flight (first read in [D]); wave 0: T' = (I + A)^-1
-        // (diagonal 16x16 blocks by forward substitution, then 16->32->64 merges)
+        // ---- [C] this chunk's V in flight (first read in [D]); T' = (I + A)^-1: each
+        // wave solves one 16x16 diagonal block, then wave 0 merges them (16->32->64)
         VRegs vcur;       // fp32: one element per register, accumulator layout
         VWide vwide;      // bf16: 16-byte loads, moved to the accumulator layout through LDS in [D]
         if constexpr (HASV) {
@@ -848,46 +860,39 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
             for (int e = 0; e < 32; ++e) vcur.x[e] = 0u;
         }
-        if (ws == 0) {
-            // (1) D = (I + N)^-1 for the four strictly lower 16x16 diagonal blocks N,
-            // by right-looking forward substitution: lane = (block bk, column cc)
-            // holds column cc of D; step m subtracts N[i][m] x_m from every later
-            // row i (independent FMAs), with column m of N read from the transposed
-            // copy (one broadcast read per block) one step ahead.
-            {
-                const int bk = lane >> 4, cc = lane & 15;
-                float x[16];
+        {
+            // (1) wave w: D = (I + N)^-1 for the strictly lower 16x16 diagonal block N
+            // of rows 16w .. 16w+15, by right-looking forward substitution.  Lane =
+            // (column c, row class r): it holds D[r + 4k][c], k = 0..3.  Step m
+            // broadcasts x_m = D[m][c] inside the lane quad (DPP) and subtracts
+            // N[r + 4k][m] x_m (zero for rows at or above m, as N is strictly lower),
+            // with N[r + 4k][m] read from the transposed copy one step ahead.
+            const int c = lane >> 2, rq = lane & 3;
+            const float *nt = NT + ws * L::NTS + 4 * rq;
+            float x[4];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) x[i] = i == cc ? 1.f : 0.f;
-                // only the 4-row groups below the diagonal are read; the read offset and
-                // the column pass through an opaque copy each step so that the compiler
-                // keeps the reads one step ahead instead of hoisting all of them
-                f32x4 col[2][4];
-                int ofs = bk * L::NTS;
+            for (int k = 0; k < 4; ++k) x[k] = rq + 4 * k == c ? 1.f : 0.f;
+            f32x4 ncol[2];
+            ncol[0] = ld4(nt);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) col[0][q] = ld4(NT + ofs + 4 * q);
+            for (int m = 0; m < 15; ++m) {
+                if (m + 1 < 15) ncol[(m + 1) & 1] = ld4(nt + (m + 1) * 16);
+                const float xm = quad_bcast(x[m >> 2], m & 3);
 #pragma unroll
-                for (int m = 0; m < 15; ++m) {
-                    asm volatile("" : "+v"(ofs), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]),
-                                 "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]),
-                                 "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
-                    if (m + 1 < 15) {
-#pragma unroll
-                        for (int q = (m + 2) >> 2; q < 4; ++q) col[(m + 1) & 1][q] = ld4(NT + ofs + (m + 1) * 16 + 4 * q);
-                    }
-                    const float xm = x[m];
-#pragma unroll
-                    for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-col[m & 1][i >> 2][i & 3], xm, x[i]);
-                }
-                const float bcol = rf(FB_)[16 * bk + cc];
-                float *blk = Af + (16 * bk) * L::FLD + 16 * bk;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    blk[i * L::FLD + cc] = x[i];
-                    Ts[(16 * bk + i) * L::OLD + 16 * bk + cc] = (IO)(x[i] * bcol);
-                    if ((bk & 1) == 0) Ts[(16 * bk + i) * L::OLD + 16 * bk + 16 + cc] = (IO)0.f;
-                }
+                for (int k = 0; k < 4; ++k) x[k] = fmaf(-ncol[m & 1][k], xm, x[k]);
             }
+            const float bcol = rf(FB_)[16 * ws + c];
+            float *blk = Af + (16 * ws) * L::FLD + 16 * ws;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = rq + 4 * k;
+                blk[i * L::FLD + c] = x[k];
+                Ts[(16 * ws + i) * L::OLD + 16 * ws + c] = (IO)(x[k] * bcol);
+                if ((ws & 1) == 0) Ts[(16 * ws + i) * L::OLD + 16 * ws + 16 + c] = (IO)0.f;
+            }
+        }
+        __syncthreads();
+        if (ws == 0) {
             // (2) 16 -> 32: T'_{2x+1,2x} = -D_{2x+1} A_{2x+1,2x} D_{2x}, x = 0, 1
             {
                 const int g = lane >> 4, nn = lane & 15;
