@@ -313,10 +313,12 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // ld_acc: tokens cb + 16s + 4h + {0..3} and the same + 8.  Operand row m holds
 // K column m0 + m with bits 2 and 3 of m swapped, so that the product's
 // accumulator register r of half h is column m0 + 16 (r/8) + 8h + r%8: the
-// state's natural operand order.
+// state's natural operand order.  With PERM = false operand row m is column
+// m0 + m (a plain operand of a column-major read).
+template <bool PERM = true>
 __device__ __forceinline__ bf16x8 ld_acc_tr(const bf16 *Ks, int ld, int m0, int cb, int s, int lane) {
     const int i = lane & 15, h = lane >> 5, g16 = (lane >> 4) & 1;
-    const int q = i & 3, qs = ((q & 1) << 1) | (q >> 1);
+    const int q = i & 3, qs = PERM ? ((q & 1) << 1) | (q >> 1) : q;
     const bf16 *p = Ks + (cb + 16 * s + 4 * h + (i >> 2)) * ld + m0 + 16 * g16 + 4 * qs;
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
@@ -922,18 +924,23 @@ fused_scan_kernel(const ScanParams p) {
                     }
                 }
             }
-            // (3) 32 -> 64: T'_21 = -T'_22 A_21 T'_11
+            // (3) 32 -> 64: T'_21 = -T'_22 A_21 T'_11.  bf16: T'_11 is read as its
+            // column-scaled copy T'_11 diag(b) from Ts (transposing loads), so the
+            // product already carries the column scale that Ts holds.
             {
                 f32x16 R2 = zero16();
 #pragma unroll
-                for (int s = 0; s < S32; ++s)        // R2 = A_21 T'_11 (contraction order as in ld_acc)
-                    R2 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 0, s, h32),
-                                ld_acc_t<IO>(Af, L::FLD, l32, 0, s, h32), R2);
+                for (int s = 0; s < S32; ++s) {      // R2 = A_21 T'_11 (contraction order as in ld_acc)
+                    frag b;
+                    if constexpr (BF) b = ld_acc_tr<false>(Ts, L::OLD, 0, 0, s, lane);
+                    else b = ld_acc_t<IO>(Af, L::FLD, l32, 0, s, h32);
+                    R2 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 0, s, h32), b, R2);
+                }
                 f32x16 T21 = zero16();
 #pragma unroll
                 for (int s = 0; s < S32; ++s)
                     T21 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 32, s, h32), acc_frag<IO>(R2, s), T21);
-                const float bcol = rf(FB_)[l32];
+                const float bcol = BF ? 1.f : rf(FB_)[l32];
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) Ts[(32 + acc_row(rr, h32)) * L::OLD + l32] = (IO)(-T21[rr] * bcol);
             }
