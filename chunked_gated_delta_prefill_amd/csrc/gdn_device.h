@@ -1,0 +1,454 @@
+// Device helpers shared by the scan kernels (gdn_scan.hip, gdn_pair.hip):
+// MFMA operand layouts, LDS operand reads, buffer loads of one chunk, gate
+// decoding, DPP reductions and state I/O.  Internal; included by .hip files only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace dev {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = kChunk;
+constexpr int D = kHeadDim;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9-family data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcWord3);
+}
+
+// ----------------------------------------------------------------- MFMA ----
+// 32x32 MFMA lane layout (wave64): lane l, index l % 32, half h = l / 32.
+//   A operand: row m = l % 32; B operand: col n = l % 32; contraction slots
+//   owned by half h.  Accumulator (16 fp32): col n = l % 32, row
+//   8*(r/4) + 4*h + r%4 for register r.
+// 16x16 MFMA: lane l, index l % 16, group g = l / 16.  Accumulator (4 fp32):
+//   col n = l % 16, row 4*g + r.
+template <typename OT> struct Mma;
+template <> struct Mma<bf16> {
+    static constexpr int E = 8;                     // 32x32 operand elements per lane
+    static constexpr int E16 = 4;                   // 16x16 operand elements per lane
+    typedef bf16x8 frag;
+    typedef bf16x4 frag16;
+    __device__ static f32x16 run(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static f32x4 run16(frag16 a, frag16 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma<float> {
+    static constexpr int E = 1;
+    static constexpr int E16 = 1;
+    typedef float frag;
+    typedef float frag16;
+    __device__ static f32x16 run(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static f32x4 run16(frag16 a, frag16 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// Row of 32x32 accumulator register r for half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+template <typename T> struct is_bf : std::is_same<T, bf16> {};
+
+// 32x32 operand, accumulator order: step s of a 32-wide contraction block at
+// cb; slot e of half h holds index cb + acc_row(s*E + e, h).  Row-major LDS.
+template <typename OT, typename ST>
+__device__ __forceinline__ typename Mma<OT>::frag ld_acc(const ST *M, int ld, int row, int cb, int s, int h) {
+    if constexpr (is_bf<OT>::value && is_bf<ST>::value) {
+        const bf16 *p = M + row * ld + cb + 16 * s + 4 * h;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(p);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(p + 8);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else if constexpr (is_bf<OT>::value) {        // fp32 LDS -> bf16 operand
+        const float *p = M + row * ld + cb + 16 * s + 4 * h;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 8);
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f[e] = (bf16)lo[e]; f[4 + e] = (bf16)hi[e]; }
+        return f;
+    } else {
+        return M[row * ld + cb + acc_row(s, h)];
+    }
+}
+
+// Same order, element (row, idx) stored at M[idx * ld + row] (column read).
+template <typename OT, typename ST>
+__device__ __forceinline__ typename Mma<OT>::frag ld_acc_t(const ST *M, int ld, int row, int cb, int s, int h) {
+    if constexpr (is_bf<OT>::value) {
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (bf16)(float)M[(cb + acc_row(8 * s + e, h)) * ld + row];
+        return f;
+    } else {
+        return M[(cb + acc_row(s, h)) * ld + row];
+    }
+}
+
+// 32x32 operand, natural order: step s covers [2E*s, 2E*s + 2E), half h holds
+// E consecutive indices.  Row-major LDS in the operand type.
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::frag ld_nat(const OT *M, int ld, int row, int s, int h) {
+    if constexpr (is_bf<OT>::value) {
+        return *reinterpret_cast<const bf16x8 *>(M + row * ld + 16 * s + 8 * h);
+    } else {
+        return M[row * ld + 2 * s + h];
+    }
+}
+
+// Accumulator registers of step s as a 32x32 operand (accumulator order).
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::frag acc_frag(const f32x16 &a, int s) {
+    if constexpr (is_bf<OT>::value) {
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (bf16)a[8 * s + e];
+        return f;
+    } else {
+        return a[s];
+    }
+}
+
+// 16x16 operands, accumulator order: step s, slot e of group g holds index
+// 4*g + s*E16 + e.  Row read (row-major) and column read variants, from fp32 LDS.
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::frag16 ld16_row(const float *M, int ld, int row, int cb, int s, int g) {
+    if constexpr (is_bf<OT>::value) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(M + row * ld + cb + 4 * g);
+        return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    } else {
+        return M[row * ld + cb + 4 * g + s];
+    }
+}
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::frag16 ld16_col(const float *M, int ld, int col, int rb, int s, int g) {
+    if constexpr (is_bf<OT>::value) {
+        bf16x4 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = (bf16)M[(rb + 4 * g + e) * ld + col];
+        return f;
+    } else {
+        return M[(rb + 4 * g + s) * ld + col];
+    }
+}
+template <typename OT>
+__device__ __forceinline__ typename Mma<OT>::frag16 acc16_frag(const f32x4 &a, int s) {
+    if constexpr (is_bf<OT>::value) {
+        return bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    } else {
+        return a[s];
+    }
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    return z;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ int64_t load_cu(const void *cu, int i, int is64) {
+    return is64 ? static_cast<const int64_t *>(cu)[i] : (int64_t) static_cast<const int32_t *>(cu)[i];
+}
+
+// Gate loads keep the raw bits; they are converted when first used, so the
+// load is not waited for when it is issued.
+__device__ __forceinline__ uint32_t gate_bits(__amdgpu_buffer_rsrc_t r, int off, int dt) {
+    return dt == GDN_F32 ? __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)
+                         : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float gate_value(uint32_t bits, int dt) {
+    if (dt == GDN_F32) return __builtin_bit_cast(float, bits);
+    if (dt == GDN_BF16) return bf16_bits_to_float(bits & 0xffffu);
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xffffu));
+}
+
+// ---------------------------------------------------------- LDS layout ----
+// Per-row factor arrays (64 floats each), written once per chunk.  The state
+// is held as S = sigma * S~ (sigma a per-sequence scalar, see the kernel); c
+// is the query scale:
+//   RG  in-chunk log-gate cumsum G_i   GM gamma_i = exp(G_i)   IG 1 / gamma_i
+//   DC  exp(G_L - G_i)                 FB b_i                  (b also scales T' columns)
+//   RK  rk_i, RQ rq_i  (1 without L2 norm; computed with the Gram tiles)
+//   FZ  sigma gamma_i rk_i   (rows of K S~^T)     FY  c sigma gamma_i rq_i  (output rows)
+//   FU  rk_i exp(G_L - G_i) / sigma'   (state update; without / sigma' on renorm)
+// followed by gamma_L.
+enum { RG_ = 0, GM_ = 1, IG_ = 2, DC_ = 3, FB_ = 4, RK_ = 5, RQ_ = 6, FZ_ = 7, FY_ = 8, FU_ = 9, NROWF = 10 };
+constexpr float kFastDecay = -60.f;   // G_L above this: exp(G_i - G_j) = gamma_i / gamma_j is safe
+constexpr float kRenorm = 0x1p-40f;   // sigma below this is folded back into the state
+
+
+// Element e of each lane quad, broadcast to the quad (DPP quad_perm [e, e, e, e]).
+__device__ __forceinline__ float quad_bcast(float v, int e) {
+    const int b = __builtin_bit_cast(int, v);
+    switch (e) {
+        case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x00, 0xf, 0xf, false));
+        case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x55, 0xf, 0xf, false));
+        case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xaa, 0xf, 0xf, false));
+        default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xff, 0xf, 0xf, false));
+    }
+}
+
+// Sum over the 16 lanes of a DPP row (every lane gets the total).
+__device__ __forceinline__ __attribute__((unused)) float row_sum16(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    return x;
+}
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// Sum of squares of 8 bf16 values (products exact in fp32, fp32 accumulation).
+__device__ __forceinline__ float sumsq8(bf16x8 x) {
+    const bf16x2 x0 = __builtin_shufflevector(x, x, 0, 1), x1 = __builtin_shufflevector(x, x, 2, 3);
+    const bf16x2 x2 = __builtin_shufflevector(x, x, 4, 5), x3 = __builtin_shufflevector(x, x, 6, 7);
+    const float a = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, __builtin_amdgcn_fdot2_f32_bf16(x0, x0, 0.f, false), false);
+    const float b = __builtin_amdgcn_fdot2_f32_bf16(x3, x3, __builtin_amdgcn_fdot2_f32_bf16(x1, x1, 0.f, false), false);
+    return a + b;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts of 1, 2, 4, 8 inside
+// each 16-lane row, then the row totals carried across rows.
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_add(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// 32x32 bf16 A operand of a product contracting over tokens, rows = K columns
+// [m0, m0 + 32), read straight from row-major K with the transposing LDS load
+// (within 16 lanes, output lane i element e comes from source lane i/4 + 4e,
+// element i%4; source lane j points at token t0 + j/4 and at the 4 columns of
+// output lanes 4 (j%4) .. 4 (j%4) + 3).  Slots follow the accumulator order of
+// ld_acc: tokens cb + 16s + 4h + {0..3} and the same + 8.  Operand row m holds
+// K column m0 + m with bits 2 and 3 of m swapped, so that the product's
+// accumulator register r of half h is column m0 + 16 (r/8) + 8h + r%8: the
+// state's natural operand order.  With PERM = false operand row m is column
+// m0 + m (a plain operand of a column-major read).
+template <bool PERM = true>
+__device__ __forceinline__ bf16x8 ld_acc_tr(const bf16 *Ks, int ld, int m0, int cb, int s, int lane) {
+    const int i = lane & 15, h = lane >> 5, g16 = (lane >> 4) & 1;
+    const int q = i & 3, qs = PERM ? ((q & 1) << 1) | (q >> 1) : q;
+    const bf16 *p = Ks + (cb + 16 * s + 4 * h + (i >> 2)) * ld + m0 + 16 * g16 + 4 * qs;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * ld));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// K, Q and the gates of the next chunk, loaded while the current chunk runs
+// (consumed only after the chunk's last barrier, so no wait is forced early).
+template <typename IO> struct Prefetch;
+template <> struct Prefetch<bf16> {
+    i32x4 kq[2][4];      // K and Q: 4 rows x 8 columns per thread
+    uint32_t g, b;       // raw gate bits of token `lane` (wave 0)
+};
+template <> struct Prefetch<float> {
+    f32x4 kq[2][8];      // K and Q: 8 rows x 4 columns per thread
+    uint32_t g, b;
+};
+// This chunk's V in accumulator layout (rows 32*ib + acc_row(r, h32), column
+// v0), one element per register; loaded at the start of the chunk and first
+// read in the last phase.
+struct VRegs {
+    uint32_t x[32];
+};
+__device__ __forceinline__ float vreg_at(const VRegs &v, int e, bool bf) {
+    return bf ? bf16_bits_to_float(v.x[e] & 0xffffu) : __builtin_bit_cast(float, v.x[e]);
+}
+
+struct ChunkRef {
+    int64_t t0;
+    int L;
+};
+
+// Loads one chunk's inputs into registers.  Each lane keeps one VGPR offset;
+// for full chunks the per-row offsets go in the scalar offset operand, for
+// the ragged last chunk they go in the (range-checked) vector offset so rows
+// past the end load zeros.
+template <typename IO>
+__device__ __forceinline__ void issue_loads(Prefetch<IO> &pf, const ScanParams &p, ChunkRef ch, int hq, int h,
+                                            int tid, int lane, int ws) {
+    constexpr bool BF = is_bf<IO>::value;
+    constexpr int ES = (int)sizeof(IO);
+    const int L = ch.L;
+    const auto rk = rsrc(p.k + ch.t0 * p.k_st + hq * p.k_sh, L > 0 ? (L - 1) * p.k_st + D * ES : 0);
+    const auto rq = rsrc(p.q + ch.t0 * p.q_st + hq * p.q_sh, L > 0 ? (L - 1) * p.q_st + D * ES : 0);
+    if constexpr (BF) {
+        const int rq4 = tid >> 4, cg = tid & 15;
+        const int vk = 4 * rq4 * p.k_st + 16 * cg, vq = 4 * rq4 * p.q_st + 16 * cg;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            pf.kq[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rk, vk + t * p.k_st, 0, 0);
+            pf.kq[1][t] = __builtin_amdgcn_raw_buffer_load_b128(rq, vq + t * p.q_st, 0, 0);
+        }
+    } else {
+        const int r0 = tid >> 5, cg = tid & 31;
+        const int vk = r0 * p.k_st + 16 * cg, vq = r0 * p.q_st + 16 * cg;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pf.kq[0][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, vk + 8 * j * p.k_st, 0, 0));
+            pf.kq[1][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vq + 8 * j * p.q_st, 0, 0));
+        }
+    }
+    if (ws == 0) {   // gates of token `lane`
+        pf.g = 0;
+        pf.b = 0;
+        if (p.g) {
+            const auto rg = rsrc(p.g + ch.t0 * p.g_st + h * p.g_sh, L > 0 ? (L - 1) * p.g_st + 4 : 0);
+            pf.g = gate_bits(rg, lane * p.g_st, p.g_dt);
+        }
+        if (p.beta) {
+            const auto rb = rsrc(p.beta + ch.t0 * p.b_st + h * p.b_sh, L > 0 ? (L - 1) * p.b_st + 4 : 0);
+            pf.b = gate_bits(rb, lane * p.b_st, p.b_dt);
+        }
+    }
+}
+
+template <typename IO>
+__device__ __forceinline__ void issue_v(VRegs &vr, const ScanParams &p, ChunkRef ch, int h, int h32, int v0) {
+    constexpr bool BF = is_bf<IO>::value;
+    constexpr int ES = (int)sizeof(IO);
+    const int L = ch.L;
+    const bool full = L == C;
+    const auto rv = rsrc(p.v + ch.t0 * p.v_st + h * p.v_sh, L > 0 ? (L - 1) * p.v_st + D * ES : 0);
+    const int vv = 4 * h32 * p.v_st + v0 * ES;
+    auto vall = [&](bool in_soffset) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const int ro = (32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3)) * p.v_st;
+            if constexpr (BF)
+                vr.x[e] = in_soffset ? __builtin_amdgcn_raw_buffer_load_b16(rv, vv, ro, 0)
+                                     : __builtin_amdgcn_raw_buffer_load_b16(rv, vv + ro, 0, 0);
+            else
+                vr.x[e] = in_soffset ? __builtin_amdgcn_raw_buffer_load_b32(rv, vv, ro, 0)
+                                     : __builtin_amdgcn_raw_buffer_load_b32(rv, vv + ro, 0, 0);
+        }
+    };
+    if (full) vall(true);
+    else vall(false);
+}
+
+// bf16 V: each wave loads the 64 x 32 block of its own state columns with
+// 16-byte loads (token 16 j + lane / 4, columns 32 ws + 8 (lane % 4) .. + 8);
+// rows past the chunk end fall outside the buffer range and load zeros.
+struct VWide {
+    i32x4 x[4];
+};
+__device__ __forceinline__ void issue_v_wide(VWide &vw, const ScanParams &p, ChunkRef ch, int h, int ws, int lane) {
+    const int L = ch.L;
+    const auto rv = rsrc(p.v + ch.t0 * p.v_st + h * p.v_sh, L > 0 ? (L - 1) * p.v_st + D * 2 : 0);
+    const int vo = (lane >> 2) * p.v_st + (32 * ws + 8 * (lane & 3)) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vw.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * j * p.v_st, 0, 0);
+}
+
+__device__ __forceinline__ ChunkRef chunk_at(int64_t bos, int64_t eos, int c) {
+    ChunkRef ch;
+    ch.t0 = bos + (int64_t)c * C;
+    const int64_t rem = eos - ch.t0;
+    ch.L = rem <= 0 ? 0 : (rem >= C ? C : (int)rem);
+    return ch;
+}
+
+// ---- state I/O: accumulator tiles S[b] (S^T rows k, column v0) <-> a V-major
+// [128][128] block at `base` with row stride `rs` bytes.  Register r of half h32
+// holds k = 32 b + acc_row(r, h32) in accumulator order (NAT = false) or
+// k = 32 b + 16 (r / 8) + 8 h32 + r % 8 in natural operand order (NAT = true).
+template <bool NAT> __device__ __forceinline__ int state_k(int bb, int r, int h32) {
+    return NAT ? 32 * bb + 16 * (r >> 3) + 8 * h32 + (r & 7) : 32 * bb + acc_row(r, h32);
+}
+
+template <bool NAT>
+__device__ __forceinline__ void load_state(f32x16 (&S)[4], const char *base, int rs, int dt, int v0, int h32) {
+    const auto r = rsrc(base, (int64_t)D * rs);
+    if (dt == GDN_F32) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {     // registers 4j .. 4j+3 hold 4 consecutive k
+                const f32x4 x = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, v0 * rs + 4 * state_k<NAT>(bb, 4 * j, h32), 0, 0));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = x[t];
+            }
+    } else {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x4 x = __builtin_bit_cast(
+                    bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, v0 * rs + 2 * state_k<NAT>(bb, 4 * j, h32), 0, 0));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = (float)x[t];
+            }
+    }
+}
+
+template <bool NAT>
+__device__ __forceinline__ void store_state(const f32x16 (&S)[4], char *base, int rs, int dt, int v0, int h32) {
+    const auto r = rsrc(base, (int64_t)D * rs);
+    if (dt == GDN_F32) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f32x4 x;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = S[bb][4 * j + t];
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r,
+                                                       v0 * rs + 4 * state_k<NAT>(bb, 4 * j, h32), 0, 0);
+            }
+    } else {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 x;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = (bf16)S[bb][4 * j + t];
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r,
+                                                      v0 * rs + 2 * state_k<NAT>(bb, 4 * j, h32), 0, 0);
+            }
+    }
+}
+
+constexpr int64_t kMapBytes = (int64_t)D * D * 4;   // one fp32 [128][128] block of the workspace
+// s_waitcnt operand for vmcnt(0) alone (expcnt and lgkmcnt at their maximum)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+
+}  // namespace dev
+}  // namespace gdn
