@@ -294,27 +294,45 @@ struct ChunkRef {
     int L;
 };
 
-// Loads one chunk's inputs into registers.  Each lane keeps one VGPR offset;
-// for full chunks the per-row offsets go in the scalar offset operand, for
-// the ragged last chunk they go in the (range-checked) vector offset so rows
-// past the end load zeros.
+// bf16 K and Q, part t of four: rows 4 (tid / 16) + t, 16 bytes at column 8 (tid % 16)
+// (four full rows per wave and instruction).
+__device__ __forceinline__ void issue_kq_part(Prefetch<bf16> &pf, const ScanParams &p, ChunkRef ch, int hq, int tid,
+                                              int t) {
+    const int L = ch.L;
+    const auto rk = rsrc(p.k + ch.t0 * p.k_st + hq * p.k_sh, L > 0 ? (L - 1) * p.k_st + D * 2 : 0);
+    const auto rq = rsrc(p.q + ch.t0 * p.q_st + hq * p.q_sh, L > 0 ? (L - 1) * p.q_st + D * 2 : 0);
+    const int rq4 = tid >> 4, cg = tid & 15;
+    pf.kq[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rk, (4 * rq4 + t) * p.k_st + 16 * cg, 0, 0);
+    pf.kq[1][t] = __builtin_amdgcn_raw_buffer_load_b128(rq, (4 * rq4 + t) * p.q_st + 16 * cg, 0, 0);
+}
+
+// gate and beta of token `lane` (raw bits; 0 when the input is absent)
+template <typename IO>
+__device__ __forceinline__ void issue_gates(Prefetch<IO> &pf, const ScanParams &p, ChunkRef ch, int h, int lane) {
+    const int L = ch.L;
+    pf.g = 0;
+    pf.b = 0;
+    if (p.g) {
+        const auto rg = rsrc(p.g + ch.t0 * p.g_st + h * p.g_sh, L > 0 ? (L - 1) * p.g_st + 4 : 0);
+        pf.g = gate_bits(rg, lane * p.g_st, p.g_dt);
+    }
+    if (p.beta) {
+        const auto rb = rsrc(p.beta + ch.t0 * p.b_st + h * p.b_sh, L > 0 ? (L - 1) * p.b_st + 4 : 0);
+        pf.b = gate_bits(rb, lane * p.b_st, p.b_dt);
+    }
+}
+
+// Loads one chunk's K, Q (and, on wave 0, gates) into registers.
 template <typename IO>
 __device__ __forceinline__ void issue_loads(Prefetch<IO> &pf, const ScanParams &p, ChunkRef ch, int hq, int h,
                                             int tid, int lane, int ws) {
-    constexpr bool BF = is_bf<IO>::value;
-    constexpr int ES = (int)sizeof(IO);
-    const int L = ch.L;
-    const auto rk = rsrc(p.k + ch.t0 * p.k_st + hq * p.k_sh, L > 0 ? (L - 1) * p.k_st + D * ES : 0);
-    const auto rq = rsrc(p.q + ch.t0 * p.q_st + hq * p.q_sh, L > 0 ? (L - 1) * p.q_st + D * ES : 0);
-    if constexpr (BF) {
-        const int rq4 = tid >> 4, cg = tid & 15;
-        const int vk = 4 * rq4 * p.k_st + 16 * cg, vq = 4 * rq4 * p.q_st + 16 * cg;
+    if constexpr (is_bf<IO>::value) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            pf.kq[0][t] = __builtin_amdgcn_raw_buffer_load_b128(rk, vk + t * p.k_st, 0, 0);
-            pf.kq[1][t] = __builtin_amdgcn_raw_buffer_load_b128(rq, vq + t * p.q_st, 0, 0);
-        }
+        for (int t = 0; t < 4; ++t) issue_kq_part(pf, p, ch, hq, tid, t);
     } else {
+        const int L = ch.L;
+        const auto rk = rsrc(p.k + ch.t0 * p.k_st + hq * p.k_sh, L > 0 ? (L - 1) * p.k_st + D * 4 : 0);
+        const auto rq = rsrc(p.q + ch.t0 * p.q_st + hq * p.q_sh, L > 0 ? (L - 1) * p.q_st + D * 4 : 0);
         const int r0 = tid >> 5, cg = tid & 31;
         const int vk = r0 * p.k_st + 16 * cg, vq = r0 * p.q_st + 16 * cg;
 #pragma unroll
@@ -323,18 +341,7 @@ __device__ __forceinline__ void issue_loads(Prefetch<IO> &pf, const ScanParams &
             pf.kq[1][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vq + 8 * j * p.q_st, 0, 0));
         }
     }
-    if (ws == 0) {   // gates of token `lane`
-        pf.g = 0;
-        pf.b = 0;
-        if (p.g) {
-            const auto rg = rsrc(p.g + ch.t0 * p.g_st + h * p.g_sh, L > 0 ? (L - 1) * p.g_st + 4 : 0);
-            pf.g = gate_bits(rg, lane * p.g_st, p.g_dt);
-        }
-        if (p.beta) {
-            const auto rb = rsrc(p.beta + ch.t0 * p.b_st + h * p.b_sh, L > 0 ? (L - 1) * p.b_st + 4 : 0);
-            pf.b = gate_bits(rb, lane * p.b_st, p.b_dt);
-        }
-    }
+    if (ws == 0) issue_gates(pf, p, ch, h, lane);
 }
 
 template <typename IO>
@@ -367,12 +374,16 @@ __device__ __forceinline__ void issue_v(VRegs &vr, const ScanParams &p, ChunkRef
 struct VWide {
     i32x4 x[4];
 };
-__device__ __forceinline__ void issue_v_wide(VWide &vw, const ScanParams &p, ChunkRef ch, int h, int ws, int lane) {
+__device__ __forceinline__ void issue_v_wide_part(VWide &vw, const ScanParams &p, ChunkRef ch, int h, int ws, int lane,
+                                                  int j) {
     const int L = ch.L;
     const auto rv = rsrc(p.v + ch.t0 * p.v_st + h * p.v_sh, L > 0 ? (L - 1) * p.v_st + D * 2 : 0);
     const int vo = (lane >> 2) * p.v_st + (32 * ws + 8 * (lane & 3)) * 2;
+    vw.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * j * p.v_st, 0, 0);
+}
+__device__ __forceinline__ void issue_v_wide(VWide &vw, const ScanParams &p, ChunkRef ch, int h, int ws, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vw.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * j * p.v_st, 0, 0);
+    for (int j = 0; j < 4; ++j) issue_v_wide_part(vw, p, ch, h, ws, lane, j);
 }
 
 __device__ __forceinline__ ChunkRef chunk_at(int64_t bos, int64_t eos, int c) {

@@ -232,6 +232,7 @@ fused_scan_kernel(const ScanParams p) {
         // this step's MFMAs run.
         f32x16 gt[2] = {zero16(), zero16()};
         f32x16 X[2] = {zero16(), zero16()}, Y[2] = {zero16(), zero16()};
+        const ChunkRef next = chunk_at(bos, eos, c + 1);
         {
             constexpr int NK = 4 * S32;
             auto frag_at = [&](const IO *M, int blk, int k) -> frag {
@@ -306,8 +307,15 @@ fused_scan_kernel(const ScanParams p) {
         }
         __syncthreads();
 
-        // ---- [B] next chunk's K, Q, gates in flight; A (fp32) and P into LDS
-        issue_loads<IO>(pf, p, chunk_at(bos, eos, c + 1), hq, h, tid, lane, ws);
+        // ---- [B] next chunk's K, Q, gates in flight; A (fp32) and P into LDS.  bf16:
+        // half of the K, Q loads go out here, the rest after the tiles are formed, so
+        // that a wave does not stall on a long run of load issues
+        if constexpr (BF) {
+            issue_kq_part(pf, p, next, hq, tid, 0);
+            issue_kq_part(pf, p, next, hq, tid, 1);
+        } else {
+            issue_loads<IO>(pf, p, next, hq, h, tid, lane, ws);
+        }
         {
             // Lane row i = 32 bi + l32; register 4 jj + t is column j = 32 bj + 8 jj + 4 h32 + t.
             //   A = b_i rk_i rk_j (k_i . k_j) exp(G_i - G_j)   for j < i   (fp32)
@@ -407,6 +415,11 @@ fused_scan_kernel(const ScanParams p) {
                 if (ws == 3) p_tile(gt[0], 0, 0);
                 if (ws < 2) p_tile(gt[1], 1, ws);
             }
+            if constexpr (BF) {
+                issue_kq_part(pf, p, next, hq, tid, 2);
+                issue_kq_part(pf, p, next, hq, tid, 3);
+                if (ws == 0) issue_gates(pf, p, next, h, lane);
+            }
             if (ws == 2) {   // row factors of [D], lane = token
                 const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
                 rf(FZ_)[lane] = sigma * gam * rk;
@@ -421,8 +434,7 @@ fused_scan_kernel(const ScanParams p) {
         VRegs vcur;       // fp32: one element per register, accumulator layout
         VWide vwide;      // bf16: 16-byte loads, moved to the accumulator layout through LDS in [D]
         if constexpr (HASV) {
-            if constexpr (BF) issue_v_wide(vwide, p, ch, h, ws, lane);
-            else issue_v<IO>(vcur, p, ch, h, h32, v0);
+            if constexpr (!BF) issue_v<IO>(vcur, p, ch, h, h32, v0);   // bf16: inside the solve below
         } else {
 #pragma unroll
             for (int e = 0; e < 32; ++e) vcur.x[e] = 0u;
@@ -444,6 +456,10 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
             for (int m = 0; m < 15; ++m) {
                 if (m + 1 < 15) ncol[(m + 1) & 1] = ld4(nt + (m + 1) * 16);
+                // bf16 V: one of the four 16-byte loads every fourth step
+                if constexpr (BF && HASV) {
+                    if (m % 4 == 0) issue_v_wide_part(vwide, p, ch, h, ws, lane, m / 4);
+                }
                 const float xm = quad_bcast(x[m >> 2], m & 3);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) x[k] = fmaf(-ncol[m & 1][k], xm, x[k]);
@@ -612,20 +628,31 @@ fused_scan_kernel(const ScanParams p) {
                     for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
                 }
             }
-            // store: lane = token 32 ib + l32 (rows past the chunk end fall outside the
-            // buffer range), registers 4q..4q+3 = v 32 ws + 8q + 4 h32 + 0..3
-            constexpr int ES = (int)sizeof(IO);
-            const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * ES);
+            // store (rows past the chunk end fall outside the buffer range)
+            if constexpr (BF) {
+                // through this wave's 4 KB of the A area (free again): rows t of its 32
+                // columns (64 B), the 16-byte granules of row t rotated by (t / 4) % 4 so
+                // that the 8-byte writes spread over the banks; then 16 rows of 64 B per
+                // store instruction instead of 32 rows of 16 B
+                bf16 *Ow = reinterpret_cast<bf16 *>(smem + L::AF_OFF) + ws * (C * 32);
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int base = (32 * ib + l32) * p.o_st + (32 * ws + 4 * h32) * ES;
+                for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if constexpr (BF) {
+                    for (int q = 0; q < 4; ++q) {
                         const bf16x4 b4 = {(bf16)Y[ib][4 * q], (bf16)Y[ib][4 * q + 1], (bf16)Y[ib][4 * q + 2],
                                            (bf16)Y[ib][4 * q + 3]};
-                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b4), ro, base + 8 * q * ES, 0, 0);
-                    } else {
+                        *reinterpret_cast<bf16x4 *>(Ow + (32 * ib + l32) * 32 + 8 * (q ^ ((l32 >> 2) & 3)) + 4 * h32) = b4;
+                    }
+                // (read back and stored one 16-row group per step of the state update)
+            } else {
+                // lane = token 32 ib + l32, registers 4q..4q+3 = v 32 ws + 8q + 4 h32 + 0..3
+                constexpr int ES = (int)sizeof(IO);
+                const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * ES);
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const int base = (32 * ib + l32) * p.o_st + (32 * ws + 4 * h32) * ES;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
                         const f32x4 f4 = {Y[ib][4 * q], Y[ib][4 * q + 1], Y[ib][4 * q + 2], Y[ib][4 * q + 3]};
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, f4), ro, base + 8 * q * ES, 0, 0);
                     }
@@ -658,6 +685,13 @@ fused_scan_kernel(const ScanParams p) {
             for (int k = 0; k < NU; ++k) {
                 const int cur = k & 1;
                 if (k + 1 < NU) load_kt(k + 1, kt[cur ^ 1]);
+                if constexpr (OUT && BF) {   // output rows 16k .. 16k+15 of this wave's columns
+                    const bf16 *Ow = reinterpret_cast<const bf16 *>(smem + L::AF_OFF) + ws * (C * 32);
+                    const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * 2);
+                    const int gq = lane & 3, t = 16 * k + (lane >> 2);
+                    const i32x4 o16 = *reinterpret_cast<const i32x4 *>(Ow + t * 32 + 8 * (gq ^ ((t >> 2) & 3)));
+                    __builtin_amdgcn_raw_buffer_store_b128(o16, ro, t * p.o_st + (32 * ws + 8 * gq) * 2, 0, 0);
+                }
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) S[bb] = M::run(kt[cur][bb], ub[k / S32][k % S32], S[bb]);
             }
