@@ -25,12 +25,13 @@
 //   * Accumulators are reused directly as B operands (S0^T, Z, Vnew): the
 //     contraction index of those products is permuted to the accumulator's
 //     row order and the LDS-side operand is read with the same permutation.
-//   * Per chunk: [L] stage K, K^T, Q and gates in LDS; [A] K S0^T and Q S0^T
-//     (each wave its own state rows) plus the Gram tiles; [B] A and P into
-//     LDS (P reuses Q's space) and the next chunk's loads are issued into
-//     registers; [C] one wave forms T' (16-row diagonal blocks by forward
-//     substitution, then 16->32->64 block merges on MFMA); [D] Vnew, O and
-//     the state update.
+//   * Per chunk: [L] stage K and Q in LDS, gate prefix sums and decay rows;
+//     [A] one pass over the 128-wide contraction gives K S~^T and S~ Q^T for
+//     the wave's own state rows plus its Gram tiles and row norms; [B] A (fp32)
+//     and P into LDS while the next chunk's K, Q loads are in flight; [C] the
+//     four 16x16 diagonal inverses by forward substitution (one per wave), the
+//     16->32 merges and the 32->64 merge on MFMA; [D] Vnew, O and the state
+//     update.
 //   * Global accesses go through buffer resources whose range ends at the
 //     chunk's last valid token, so ragged tails load zeros and drop stores
 //     without branches.
@@ -430,7 +431,7 @@ fused_scan_kernel(const ScanParams p) {
         __syncthreads();
 
         // ---- [C] this chunk's V in flight (first read in [D]); T' = (I + A)^-1: each
-        // wave solves one 16x16 diagonal block, then wave 0 merges them (16->32->64)
+        // wave solves one 16x16 diagonal block, then the blocks are merged (16->32->64)
         VRegs vcur;       // fp32: one element per register, accumulator layout
         VWide vwide;      // bf16: 16-byte loads, moved to the accumulator layout through LDS in [D]
         if constexpr (HASV) {
@@ -475,56 +476,75 @@ fused_scan_kernel(const ScanParams p) {
             }
         }
         __syncthreads();
-        if (ws == 0) {
-            // (2) 16 -> 32: T'_{2x+1,2x} = -D_{2x+1} A_{2x+1,2x} D_{2x}, x = 0, 1
-            {
-                const int g = lane >> 4, nn = lane & 15;
-                f32x4 R[2];
+        // (2) 16 -> 32: T'_{2x+1,2x} = -D_{2x+1} A_{2x+1,2x} D_{2x}, x = 0, 1
+        auto merge16 = [&](int x2) {
+            const int g = lane >> 4, nn = lane & 15;
+            const int lo = 32 * x2, hi = 32 * x2 + 16;
+            f32x4 R = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int x2 = 0; x2 < 2; ++x2) {
-                    const int lo = 32 * x2, hi = 32 * x2 + 16;
-                    R[x2] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < S16; ++s)
+                R = M::run16(ld16_row<IO>(Af, L::FLD, hi + nn, lo, s, g), ld16_col<IO>(Af, L::FLD, lo + nn, lo, s, g), R);
+            const float bcol = rf(FB_)[lo + nn];
+            f32x4 Tq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < S16; ++s)
-                        R[x2] = M::run16(ld16_row<IO>(Af, L::FLD, hi + nn, lo, s, g),
-                                         ld16_col<IO>(Af, L::FLD, lo + nn, lo, s, g), R[x2]);
-                }
+            for (int s = 0; s < S16; ++s)
+                Tq = M::run16(ld16_row<IO>(Af, L::FLD, hi + nn, hi, s, g), acc16_frag<IO>(R, s), Tq);
 #pragma unroll
-                for (int x2 = 0; x2 < 2; ++x2) {
-                    const int lo = 32 * x2, hi = 32 * x2 + 16;
-                    const float bcol = rf(FB_)[lo + nn];
-                    f32x4 Tq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < S16; ++s)
-                        Tq = M::run16(ld16_row<IO>(Af, L::FLD, hi + nn, hi, s, g), acc16_frag<IO>(R[x2], s), Tq);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int i = hi + 4 * g + rr;
-                        Af[i * L::FLD + lo + nn] = -Tq[rr];
-                        Ts[i * L::OLD + lo + nn] = (IO)(-Tq[rr] * bcol);
-                    }
-                }
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = hi + 4 * g + rr;
+                Af[i * L::FLD + lo + nn] = -Tq[rr];
+                Ts[i * L::OLD + lo + nn] = (IO)(-Tq[rr] * bcol);
             }
-            // (3) 32 -> 64: T'_21 = -T'_22 A_21 T'_11.  bf16: T'_11 is read as its
-            // column-scaled copy T'_11 diag(b) from Ts (transposing loads), so the
-            // product already carries the column scale that Ts holds.
-            {
-                f32x16 R2 = zero16();
+        };
+        if constexpr (BF) {
+            // the two 16 -> 32 merges on waves 0 and 1; then the four 16x16 blocks
+            // (r, c) of T''_21 = -T'_22 A_21 T''_11 on the four waves: wave (r, c) forms
+            // R = A_21 T''_11[:, c] (both 16-row halves) and -T'_22[r, :] R.  T''_11 is
+            // read as its column-scaled copy from Ts (transposing loads), so the
+            // product carries the column scale that Ts holds.
+            if (ws < 2) merge16(ws);
+            __syncthreads();
+            const int r = ws >> 1, cc = ws & 1;
+            const int g = lane >> 4, n = lane & 15;
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            // T''_11 rows 8g .. 8g+7 of column 16 cc + n: source lane j points at row
+            // 8g + j/4 (+4), columns 16 cc + 4 (j%4) .. +3
+            const bf16 *tp = Ts + (8 * g + (n >> 2)) * L::OLD + 16 * cc + 4 * (n & 3);
+            const s16x4 t_lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)tp);
+            const s16x4 t_hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tp + 4 * L::OLD));
+            const bf16x8 tb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t_lo, t_hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            auto row8 = [&](int row, int c0, int c1) {   // Af[row][c0 .. c0+3], Af[row][c1 .. c1+3] as bf16
+                const f32x4 a = ld4(Af + row * L::FLD + c0), b = ld4(Af + row * L::FLD + c1);
+                return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+            };
+            f32x4 R[2];
 #pragma unroll
-                for (int s = 0; s < S32; ++s) {      // R2 = A_21 T'_11 (contraction order as in ld_acc)
-                    frag b;
-                    if constexpr (BF) b = ld_acc_tr<false>(Ts, L::OLD, 0, 0, s, lane);
-                    else b = ld_acc_t<IO>(Af, L::FLD, l32, 0, s, h32);
-                    R2 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 0, s, h32), b, R2);
-                }
-                f32x16 T21 = zero16();
+            for (int rp = 0; rp < 2; ++rp)
+                R[rp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row8(32 + 16 * rp + n, 8 * g, 8 * g + 4), tb,
+                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            // contraction over the 32 rows of R in the order the accumulators hold
+            // them: slots 0..3 of group g are rows 4g .. 4g+3, slots 4..7 rows 16 + 4g ..
+            const bf16x8 rb = {(bf16)R[0][0], (bf16)R[0][1], (bf16)R[0][2], (bf16)R[0][3],
+                               (bf16)R[1][0], (bf16)R[1][1], (bf16)R[1][2], (bf16)R[1][3]};
+            const f32x4 T21 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row8(32 + 16 * r + n, 32 + 4 * g, 48 + 4 * g), rb,
+                                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-                for (int s = 0; s < S32; ++s)
-                    T21 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 32, s, h32), acc_frag<IO>(R2, s), T21);
-                const float bcol = BF ? 1.f : rf(FB_)[l32];
+            for (int rr = 0; rr < 4; ++rr) Ts[(32 + 16 * r + 4 * g + rr) * L::OLD + 16 * cc + n] = (IO)(-T21[rr]);
+        } else if (ws == 0) {
+            merge16(0);
+            merge16(1);
+            // (3) 32 -> 64: T'_21 = -T'_22 A_21 T'_11, then the column scale b
+            f32x16 R2 = zero16();
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) Ts[(32 + acc_row(rr, h32)) * L::OLD + l32] = (IO)(-T21[rr] * bcol);
-            }
+            for (int s = 0; s < S32; ++s)       // R2 = A_21 T'_11 (contraction order as in ld_acc)
+                R2 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 0, s, h32), ld_acc_t<IO>(Af, L::FLD, l32, 0, s, h32), R2);
+            f32x16 T21 = zero16();
+#pragma unroll
+            for (int s = 0; s < S32; ++s)
+                T21 = M::run(ld_acc<IO>(Af, L::FLD, 32 + l32, 32, s, h32), acc_frag<IO>(R2, s), T21);
+            const float bcol = rf(FB_)[l32];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) Ts[(32 + acc_row(rr, h32)) * L::OLD + l32] = (IO)(-T21[rr] * bcol);
         }
         __syncthreads();
 
