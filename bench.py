@@ -35,7 +35,9 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 D, C = 128, 64
 KERNEL = "fused_scan_kernel"
-KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_prefill_amd", "csrc", "gdn_scan.hip")
+# sources of the scan kernel: traffic counters count only while these are unchanged
+KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_prefill_amd", "csrc", f)
+               for f in ("gdn_scan.hip", "gdn_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_scan_large_batch.txt")
 
 
@@ -53,7 +55,10 @@ def algorithmic(w):
 
 
 def kernel_source_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
