@@ -5,11 +5,13 @@ Argument marshalling only: every step of the scan runs in the HIP library
 ``include/gdn.h``.  There is no other implementation here and no fallback: if
 the library is missing or refuses a call, an exception is raised.
 
-The single entry point mirrors the C function::
+The entry points mirror the C functions::
 
     gdn_chunk_prefill(q, k, v, g, beta, scale, cu_seqlens, initial_state,
                       output_state, use_qk_l2norm, batch_invariant, out,
                       stream=None)
+    gdn_decode_step(q, k, v, g, beta, scale, state_in, state_out,
+                    use_qk_l2norm, out, stream=None)
 
 All tensors are torch CUDA (HIP) tensors; ``out`` and ``output_state`` are
 written in place.  See include/gdn.h for shapes, dtypes and error codes.
@@ -51,6 +53,8 @@ def load():
         lib.gdn_chunk_prefill.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int,
                                           ctypes.c_int, P, ctypes.c_void_p]
         lib.gdn_chunk_prefill.restype = ctypes.c_int
+        lib.gdn_decode_step.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_int, P, ctypes.c_void_p]
+        lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_last_error.argtypes = []
         lib.gdn_last_error.restype = ctypes.c_char_p
         lib.gdn_release_workspace.argtypes = []
@@ -95,18 +99,42 @@ def call_raw(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, u
     return rc, (lib.gdn_last_error() or b"").decode()
 
 
+def _stream_handle(stream, q):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else None
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return stream
+
+
 def gdn_chunk_prefill(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state,
                       use_qk_l2norm, batch_invariant, out, stream=None):
     """Enqueues the scan on ``stream`` (default: torch's current stream of q's device)."""
-    if stream is None:
-        import torch
-        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else None
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = _stream_handle(stream, q)
     rc, msg = call_raw(describe(q), describe(k), describe(v), describe(g), describe(beta),
                        0.0 if scale is None else float(scale), describe(cu_seqlens),
                        describe(initial_state), describe(output_state), use_qk_l2norm,
                        batch_invariant, describe(out), stream)
+    if rc != 0:
+        raise GdnError(rc, msg)
+
+
+def call_decode_raw(q, k, v, g, beta, scale, state_in, state_out, use_qk_l2norm, out, stream):
+    """Calls gdn_decode_step on descriptors; returns the status code and message."""
+    lib = load()
+    ref = lambda d: None if d is None else ctypes.byref(d)
+    rc = lib.gdn_decode_step(ref(q), ref(k), ref(v), ref(g), ref(beta), ctypes.c_float(scale), ref(state_in),
+                             ref(state_out), int(bool(use_qk_l2norm)), ref(out), stream)
+    return rc, (lib.gdn_last_error() or b"").decode()
+
+
+def gdn_decode_step(q, k, v, g, beta, scale, state_in, state_out, use_qk_l2norm, out, stream=None):
+    """Enqueues one decode step on ``stream``; ``state_out`` may be ``state_in`` (in place)."""
+    stream = _stream_handle(stream, q)
+    rc, msg = call_decode_raw(describe(q), describe(k), describe(v), describe(g), describe(beta),
+                              0.0 if scale is None else float(scale), describe(state_in), describe(state_out),
+                              use_qk_l2norm, describe(out), stream)
     if rc != 0:
         raise GdnError(rc, msg)
 

@@ -383,3 +383,108 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
         return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return GDN_OK;
 }
+
+extern "C" int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                               const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                               const gdn_tensor *state_in, const gdn_tensor *state_out, int use_qk_l2norm,
+                               const gdn_tensor *out, void *stream) {
+    g_last_error.clear();
+    std::string msg;
+    int rc;
+    if (!q || !k || !v || !out) return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v and out are required");
+    if ((rc = check_basic(q, "q", 3, msg))) return fail(rc, msg);
+    if ((rc = check_basic(k, "k", 3, msg))) return fail(rc, msg);
+    if ((rc = check_basic(v, "v", 3, msg))) return fail(rc, msg);
+    if ((rc = check_basic(out, "out", 3, msg))) return fail(rc, msg);
+    const int io = q->dtype;
+    if (io == GDN_F16) return fail(GDN_ERR_UNSUPPORTED, "q/k/v in f16 are not supported (f32 or bf16)");
+    if (io != GDN_F32 && io != GDN_BF16)
+        return fail(GDN_ERR_INVALID_ARGUMENT, std::string("q: dtype ") + dt_name(io) + " is not a float type");
+    if (k->dtype != io || v->dtype != io || out->dtype != io)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v and out must share one dtype");
+    const int64_t N = q->sizes[0], Hqk = q->sizes[1], Hv = v->sizes[1];
+    if (q->sizes[2] != gdn::kHeadDim || k->sizes[2] != gdn::kHeadDim || v->sizes[2] != gdn::kHeadDim ||
+        out->sizes[2] != gdn::kHeadDim)
+        return fail(GDN_ERR_UNSUPPORTED, "head_dim must be 128 for q, k, v and out");
+    if (k->sizes[0] != N || k->sizes[1] != Hqk) return fail(GDN_ERR_INVALID_ARGUMENT, "k must have the shape of q");
+    if (v->sizes[0] != N || out->sizes[0] != N || out->sizes[1] != Hv)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "v and out must be [N, Hv, 128] with q's N");
+    if (Hqk < 1 || Hv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "head counts must be positive");
+    if (Hv % Hqk != 0)
+        return fail(GDN_ERR_UNSUPPORTED, "Hv must be a multiple of Hqk (each q/k head serves Hv/Hqk value heads)");
+    if (N > ((int64_t)1 << 24) || Hv > 65536) return fail(GDN_ERR_UNSUPPORTED, "problem too large");
+    const size_t esz = dt_size(io);
+    if (N > 0 && (!aligned16(q->data, esz, q->strides, 2) || !aligned16(k->data, esz, k->strides, 2)))
+        return fail(GDN_ERR_UNSUPPORTED, "q and k rows must be 16-byte aligned (pointer and sequence/head strides)");
+    if (g) {
+        if ((rc = check_basic(g, "g", 2, msg, false))) return fail(rc, msg);
+        if (g->sizes[0] != N || g->sizes[1] != Hv) return fail(GDN_ERR_INVALID_ARGUMENT, "g must be [N, Hv]");
+        if (g->dtype != GDN_F32 && g->dtype != GDN_BF16 && g->dtype != GDN_F16)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "g must be f32, bf16 or f16");
+    }
+    if (beta) {
+        if ((rc = check_basic(beta, "beta", 2, msg, false))) return fail(rc, msg);
+        if (beta->sizes[0] != N || beta->sizes[1] != Hv) return fail(GDN_ERR_INVALID_ARGUMENT, "beta must be [N, Hv]");
+        if (beta->dtype != GDN_F32 && beta->dtype != io)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "beta must be f32 or q's dtype");
+    }
+    const gdn_tensor *st[2] = {state_in, state_out};
+    const char *st_name[2] = {"state_in", "state_out"};
+    for (int i = 0; i < 2; ++i) {
+        if (!st[i]) continue;
+        if ((rc = check_basic(st[i], st_name[i], 4, msg))) return fail(rc, msg);
+        if (st[i]->dtype != GDN_F32 && st[i]->dtype != GDN_BF16)
+            return fail(GDN_ERR_INVALID_ARGUMENT, std::string(st_name[i]) + " must be f32 or bf16");
+        if (st[i]->sizes[0] != N || st[i]->sizes[1] != Hv || st[i]->sizes[2] != gdn::kHeadDim ||
+            st[i]->sizes[3] != gdn::kHeadDim)
+            return fail(GDN_ERR_INVALID_ARGUMENT, std::string(st_name[i]) + " must be [N, Hv, 128, 128]");
+        if (N > 0 && !aligned16(st[i]->data, dt_size(st[i]->dtype), st[i]->strides, 3))
+            return fail(GDN_ERR_UNSUPPORTED, std::string(st_name[i]) + ": rows must be 16-byte aligned (pointer and strides)");
+    }
+    if (state_in && state_out && state_in->data == state_out->data && N > 0) {
+        bool same = state_in->dtype == state_out->dtype;
+        for (int i = 0; i < 4; ++i) same = same && state_in->strides[i] == state_out->strides[i];
+        if (!same)
+            return fail(GDN_ERR_ALIAS, "state_out may share state_in's buffer only as the identical view (in-place update)");
+    }
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale must be finite");
+    int dev = 0, cus = 256;
+    if ((rc = check_device(msg, &dev, &cus))) return fail(rc, msg);
+    if (N == 0) return GDN_OK;
+
+    gdn::DecodeParams p{};
+    const int64_t es = (int64_t)esz;
+    p.q = static_cast<const char *>(q->data); p.q_sn = q->strides[0] * es; p.q_sh = q->strides[1] * es;
+    p.k = static_cast<const char *>(k->data); p.k_sn = k->strides[0] * es; p.k_sh = k->strides[1] * es;
+    p.v = static_cast<const char *>(v->data); p.v_sn = v->strides[0] * es; p.v_sh = v->strides[1] * es;
+    p.io_dt = io;
+    if (g) {
+        const int64_t ge = (int64_t)dt_size(g->dtype);
+        p.g = static_cast<const char *>(g->data); p.g_sn = g->strides[0] * ge; p.g_sh = g->strides[1] * ge;
+        p.g_dt = g->dtype;
+    }
+    if (beta) {
+        const int64_t be = (int64_t)dt_size(beta->dtype);
+        p.beta = static_cast<const char *>(beta->data); p.b_sn = beta->strides[0] * be; p.b_sh = beta->strides[1] * be;
+        p.b_dt = beta->dtype;
+    }
+    if (state_in) {
+        const int64_t se = (int64_t)dt_size(state_in->dtype);
+        p.s_in = static_cast<const char *>(state_in->data);
+        p.si_n = state_in->strides[0] * se; p.si_h = state_in->strides[1] * se; p.si_v = state_in->strides[2] * se;
+        p.si_dt = state_in->dtype;
+    }
+    if (state_out) {
+        const int64_t se = (int64_t)dt_size(state_out->dtype);
+        p.s_out = static_cast<char *>(state_out->data);
+        p.so_n = state_out->strides[0] * se; p.so_h = state_out->strides[1] * se; p.so_v = state_out->strides[2] * se;
+        p.so_dt = state_out->dtype;
+    }
+    p.out = static_cast<char *>(out->data); p.o_sn = out->strides[0] * es; p.o_sh = out->strides[1] * es;
+    p.scale = scale == 0.0f ? 1.0f / std::sqrt((float)gdn::kHeadDim) : scale;
+    p.l2norm = use_qk_l2norm != 0;
+    p.N = (int32_t)N; p.Hv = (int32_t)Hv; p.r = (int32_t)(Hv / Hqk);
+    const hipError_t e = gdn::launch_decode(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return GDN_OK;
+}

@@ -72,6 +72,25 @@ struct FixParams {
     int32_t N, Hv;
 };
 
+// One decode step (gdn_decode_step): byte strides over (sequence, head).
+struct DecodeParams {
+    const char *q, *k, *v, *g, *beta;
+    int64_t q_sn, q_sh, k_sn, k_sh, v_sn, v_sh;
+    int64_t g_sn, g_sh, b_sn, b_sh;
+    int32_t io_dt, g_dt, b_dt;
+    const char *s_in;
+    int64_t si_n, si_h, si_v;
+    int32_t si_dt;
+    char *s_out;
+    int64_t so_n, so_h, so_v;
+    int32_t so_dt;
+    char *out;
+    int64_t o_sn, o_sh;
+    float scale;
+    int32_t l2norm, N, Hv, r;
+};
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+
 // Fused chunked scan: one workgroup per (sequence or segment, value head).
 // io_bf16 selects bf16 q/k/v/out (bf16 MFMA) or fp32 (fp32 MFMA).
 hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, int mode, hipStream_t stream);

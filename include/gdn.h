@@ -1,5 +1,6 @@
 /*
- * gdn.h - C ABI of the MI355X (gfx950) chunked gated delta rule prefill scan.
+ * gdn.h - C ABI of the MI355X (gfx950) chunked gated delta rule prefill scan
+ * (and the single-token decode step that continues from its state).
  *
  * The operation ("flashinfer.gdn_prefill": chunk_gated_delta_rule is the
  * chunked GDN scan that builds the recurrent state from a whole prompt before
@@ -109,6 +110,42 @@ int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor
                       const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
                       const gdn_tensor *output_state, int use_qk_l2norm,
                       int batch_invariant, const gdn_tensor *out, void *stream);
+
+/*
+ * gdn_decode_step - one recurrent step for a batch of N sequences, one new
+ * token each: the decode-side update that continues from the state a prefill
+ * hands over ("flashinfer.gdn_prefill": the chunked scan initialises the
+ * recurrent state before the decode loop takes over; "flashinfer.cudnn",
+ * Linear attention: the state crosses V-major, float32 or bfloat16).  Per
+ * sequence n and value head h it applies the same recurrence as above to the
+ * single token:
+ *
+ *     S' = a S (I - b k k^T) + b v k^T,   o = scale S' q
+ *
+ *   q, k            [N, Hqk, 128], F32 or BF16 (both the same), innermost
+ *                   contiguous, rows 16-byte aligned.
+ *   v               [N, Hv, 128], q's dtype; Hv % Hqk == 0.
+ *   g, beta         NULL (ones) or [N, Hv]; g F32, BF16 or F16, beta F32 or
+ *                   q's dtype (as for gdn_chunk_prefill).
+ *   scale           as for gdn_chunk_prefill (0.0 means 1/sqrt(128)).
+ *   state_in        NULL (zero state) or [N, Hv, 128, 128] F32 or BF16,
+ *                   V-major, rows 16-byte aligned.
+ *   state_out       NULL (no state written) or the same shape, F32 or BF16.
+ *                   It may be state_in itself (the identical view: same
+ *                   pointer, dtype and strides) for an in-place update; the
+ *                   same pointer with another dtype or strides is rejected
+ *                   with GDN_ERR_ALIAS, other overlap is an unchecked
+ *                   precondition.
+ *   use_qk_l2norm   as for gdn_chunk_prefill.
+ *   out             [N, Hv, 128], q's dtype.
+ *   stream          as for gdn_chunk_prefill (asynchronous).
+ *
+ * Ownership and errors as for gdn_chunk_prefill; no workspace is used.
+ */
+int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                    const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                    const gdn_tensor *state_in, const gdn_tensor *state_out,
+                    int use_qk_l2norm, const gdn_tensor *out, void *stream);
 
 /* Message for the last non-zero return of a gdn_* call on this thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["gdn_chunk_prefill", "gdn_last_error", "gdn_release_workspace"]
+    assert names == ["gdn_chunk_prefill", "gdn_decode_step", "gdn_last_error", "gdn_release_workspace"]
     L = lib.load()
     for n in names:
         assert hasattr(L, n), n
@@ -130,3 +130,59 @@ def test_optional_arguments_may_be_null():
 
 def test_release_workspace_without_gpu():
     lib.load().gdn_release_workspace()
+
+
+# ---- gdn_decode_step (one token per sequence: q, k [N, Hqk, 128], v, out [N, Hv, 128])
+
+def _dargs(N=3, Hqk=2, Hv=4, dt=GDN_BF16, **over):
+    a = dict(q=_t([N, Hqk, 128], dt), k=_t([N, Hqk, 128], dt), v=_t([N, Hv, 128], dt),
+             g=_t([N, Hv], GDN_F32), beta=_t([N, Hv], GDN_F32), scale=0.0,
+             s0=_t([N, Hv, 128, 128], GDN_F32, FAKE + (1 << 30)),
+             s1=_t([N, Hv, 128, 128], GDN_F32, FAKE + (1 << 31)), l2=1,
+             out=_t([N, Hv, 128], dt, FAKE + (1 << 32)))
+    a.update(over)
+    return a
+
+
+def _dcall(a):
+    return lib.call_decode_raw(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["s0"], a["s1"],
+                               a["l2"], a["out"], None)
+
+
+DECODE_CASES = {
+    "q_missing": (dict(q=None), INVALID),
+    "out_missing": (dict(out=None), INVALID),
+    "head_dim_64": (dict(q=_t([3, 2, 64]), k=_t([3, 2, 64])), UNSUPPORTED),
+    "head_ratio": (dict(v=_t([3, 3, 128]), out=_t([3, 3, 128]), g=None, beta=None, s0=None, s1=None),
+                   UNSUPPORTED),
+    "f16_inputs": (dict(q=_t([3, 2, 128], GDN_F16), k=_t([3, 2, 128], GDN_F16), v=_t([3, 4, 128], GDN_F16),
+                        out=_t([3, 4, 128], GDN_F16)), UNSUPPORTED),
+    "v_batch": (dict(v=_t([4, 4, 128])), INVALID),
+    "g_shape": (dict(g=_t([3, 2], GDN_F32)), INVALID),
+    "beta_dtype": (dict(beta=_t([3, 4], GDN_F16)), INVALID),
+    "state_shape": (dict(s0=_t([3, 4, 128, 64], GDN_F32)), INVALID),
+    "state_dtype": (dict(s1=_t([3, 4, 128, 128], GDN_I32, FAKE + (1 << 31))), INVALID),
+    "alias_other_dtype": (dict(s1=_t([3, 4, 128, 128], GDN_BF16, FAKE + (1 << 30))), ALIAS),
+    "alias_other_strides": (dict(s1=_t([3, 4, 128, 128], GDN_F32, FAKE + (1 << 30),
+                                       strides=[4 * 128 * 256, 128 * 256, 256, 1])), ALIAS),
+    "misaligned_state": (dict(s0=_t([3, 4, 128, 128], GDN_F32, FAKE + 4)), UNSUPPORTED),
+    "scale_inf": (dict(scale=math.inf), INVALID),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_CASES))
+def test_decode_rejected_before_any_device_access(name):
+    over, code = DECODE_CASES[name]
+    rc, msg = _dcall(_dargs(**over))
+    assert rc == code, (rc, msg)
+    assert msg
+
+
+def test_decode_in_place_view_is_accepted():
+    if _has_gpu():
+        pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
+    a = _dargs(s1=_t([3, 4, 128, 128], GDN_F32, FAKE + (1 << 30)))
+    rc, msg = _dcall(a)
+    assert rc == NO_DEVICE, (rc, msg)
+    rc, _ = _dcall(_dargs(g=None, beta=None, s0=None, s1=None))
+    assert rc == NO_DEVICE
