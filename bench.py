@@ -14,6 +14,11 @@ Algorithmic work (chunk length 64, whatever the kernels use internally):
   bytes/token = q, k (2 Hqk d 2B) + v, out (2 Hv d 2B) + g, beta (2 Hv 4B)
   bytes/seq   = initial + final state (2 Hv d^2 4B)
 
+Decode step (gdn_decode_step): ``--decode`` times one recurrent step for 256
+sequences (Hqk 16, Hv 32, bf16, fp32 state updated in place) and prints its
+own JSON line; it reads and writes the whole state once, so its roofline is
+HBM: bytes/step = state (2 Hv d^2 4B per sequence) + q, k, v, out, g, beta.
+
 Other modes (used to produce the committed rocprofv3 summaries):
   --copy-calibration   a plain device copy of known size (for PMC scaling)
   --summarize-pmc DIR  turn rocprofv3 --pmc outputs (rocpd .db) into profiles/*.txt
@@ -167,7 +172,7 @@ def _dispatch_durations(d, name_part):
     return [dur for _, dur in sorted(out)]
 
 
-def summarize_trace(base, out_path, command, last=0):
+def summarize_trace(base, out_path, command, last=0, kernel=KERNEL):
     rows = _kernel_stats(base)
     lines = [f"# rocprofv3 --kernel-trace --stats summary (rocpd top_kernels; durations in microseconds)",
              f"# command: {command}",
@@ -176,10 +181,10 @@ def summarize_trace(base, out_path, command, last=0):
         short = name.replace("(anonymous namespace)", "anon").replace("void ", "")
         short = short[:short.rfind("(")] if "(" in short else short
         lines.append(f"{short[:100]} | {calls} | {avg:.3f} | {tot:.1f} | {pct:.2f}")
-    durs = _dispatch_durations(base, KERNEL)
+    durs = _dispatch_durations(base, kernel)
     if durs and last > 0:
         tail = durs[-last:]
-        lines.append(f"# {KERNEL}: the last {len(tail)} dispatches (the timed steps, warmup excluded)")
+        lines.append(f"# {kernel}: the last {len(tail)} dispatches (the timed steps, warmup excluded)")
         lines.append(f"timed_dispatches = {len(tail)}")
         lines.append(f"timed_average_us = {statistics.fmean(tail):.3f}")
         lines.append(f"timed_median_us = {statistics.median(tail):.3f}")
@@ -250,6 +255,77 @@ def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes):
     print("\n".join(lines))
 
 
+def bench_decode(args, gdn, W):
+    """One decode step per timed step over decode_batch; one JSON line."""
+    import torch
+    import oracle
+    w = W.decode_batch(device="cuda")
+    state = w.initial_state.clone()
+    out = torch.empty(w.T, w.Hv, D, dtype=w.q.dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    io = w.q.element_size()
+    byts = w.N * (2 * w.Hqk * D * io + 2 * w.Hv * D * io + w.Hv * 8) + 2 * w.N * w.Hv * D * D * 4
+
+    def step():
+        gdn.gdn_decode_step(w.q, w.k, w.v, w.g, w.beta, w.scale, state, state, w.use_qk_l2norm, out, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_ms = statistics.mean(launch_ms)
+    ms_step = wall * 1e3 / args.steps
+    achieved = byts / (kern_ms / 1e3) / 1e9
+    # reference: a plain 1 GiB device-to-device copy (reads and writes 1 GiB each)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, dst
+    res = {
+        "metric": "GDN decode step tokens/s (one token per sequence), 1 GPU",
+        "value": round(w.N / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "sequences": w.N, "hqk": w.Hqk, "hv": w.Hv, "head_dim": D,
+                   "state": "float32", "in_place": True, "l2norm": w.use_qk_l2norm},
+        "kernel_ms": round(kern_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "decode_kernel",
+                     "algorithmic_bytes": byts, "device_copy_gbs": round(copy_gbs, 1)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        wc = W.decode_batch(device="cpu")
+        threads = oracle.default_threads()
+        t = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t < 2.0:
+            oracle.run(wc.q, wc.k, wc.v, wc.g, wc.beta, wc.scale, wc.cu_seqlens, wc.initial_state,
+                       wc.use_qk_l2norm, nthreads=threads)
+            reps += 1
+        dt = (time.perf_counter() - t) / reps
+        res["cpu_baseline"] = {"value": round(wc.N / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"the whole batch ({wc.N} sequences x {wc.Hv} v-heads), fp64 oracle, "
+                                         f"{reps} runs of {dt * 1e3:.0f} ms"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,7 +342,9 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"), default=None)
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 --pmc output dirs; the last argument is the output file")
+    ap.add_argument("--decode", action="store_true", help="time the decode step instead of the prefill")
     ap.add_argument("--trace-command", default="?")
+    ap.add_argument("--trace-kernel", default=KERNEL, help="with --summarize-trace: kernel name to average")
     ap.add_argument("--trace-last", type=int, default=0,
                     help="with --summarize-trace: also average the last N dispatches of the scan kernel")
     args = ap.parse_args()
@@ -284,7 +362,8 @@ def main():
                            json.loads(args.pmc_commands).get("commands", []))
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_command, args.trace_last)
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_command, args.trace_last,
+                        args.trace_kernel)
         return
 
     import torch
@@ -293,6 +372,9 @@ def main():
     import gdn_workloads as W
 
     gdn.load()
+    if args.decode:
+        bench_decode(args, gdn, W)
+        return
     w = W.make(args.workload, device="cuda", variant=args.variant)
     flops, byts = algorithmic(w)
     if args.summarize_pmc:

@@ -22,6 +22,10 @@ on "flashinfer.cudnn.cudnn_chunk_gated_delta_rule", Parameters):
                  255 forced empty; bf16 initial and final state; int32.
   large_batch    32 sequences x 8192 tokens (262144), int32; fp32 state.
 
+  decode_batch   256 sequences of one token each (one decode step after a
+                 prefill), Hqk = 16, Hv = 32, bf16 q/k/v, fp32 state ~ N(0, 0.01^2)
+                 updated in place; gates as varlen_bf16.
+
 Variant "alt_gates" (long_single, many_short, large_batch) draws
 g ~ U[0.9, 1) and beta ~ U(0, 1) instead.
 
@@ -173,6 +177,11 @@ def make(config, *, device="cpu", variant=None):
                      cu_dtype=torch.int32, gate="uniform" if alt else "sigmoid",
                      name=CONFIG_NAMES[4] + ("/alt_gates" if alt else ""))
     raise ValueError(config)
+
+
+def decode_batch(*, device="cpu", N=256):
+    """One token for each of N sequences: the input of one decode step."""
+    return build([1] * N, 16, 32, torch.bfloat16, seed=1100, device=device, name="decode_batch")
 
 
 def slice_item(w: Workload, n: int, heads):
