@@ -343,6 +343,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 --pmc output dirs; the last argument is the output file")
     ap.add_argument("--decode", action="store_true", help="time the decode step instead of the prefill")
+    ap.add_argument("--checkpoint-interval", type=int, default=0,
+                    help="tokens between state checkpoints (gdn_chunk_prefill_checkpointed); 0 = plain scan")
     ap.add_argument("--trace-command", default="?")
     ap.add_argument("--trace-kernel", default=KERNEL, help="with --summarize-trace: kernel name to average")
     ap.add_argument("--trace-last", type=int, default=0,
@@ -386,10 +388,20 @@ def main():
     out = torch.empty(w.T, w.Hv, D, dtype=w.q.dtype, device="cuda")
     fin = None if w.state_dtype is None else torch.empty(w.N, w.Hv, D, D, dtype=w.state_dtype, device="cuda")
     stream = torch.cuda.current_stream()
+    ck_every = args.checkpoint_interval
+    if ck_every:
+        per_seq = max(1, max(w.lengths()) // ck_every)
+        ck = torch.empty(w.N * per_seq, w.Hv, D, D, dtype=torch.float32, device="cuda")
+        byts += sum(L // ck_every for L in w.lengths()) * w.Hv * D * D * 4   # checkpoint writes
 
     def step():
-        gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin,
-                              w.use_qk_l2norm, bool(args.batch_invariant), out, stream)
+        if ck_every:
+            gdn.gdn_chunk_prefill_checkpointed(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state,
+                                               fin, w.use_qk_l2norm, bool(args.batch_invariant), ck, per_seq,
+                                               ck_every, out, stream)
+        else:
+            gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin,
+                                  w.use_qk_l2norm, bool(args.batch_invariant), out, stream)
 
     for _ in range(args.warmup):
         step()
@@ -410,7 +422,7 @@ def main():
     kern_ms = statistics.mean(launch_ms)
     value = w.T / (ms_step / 1e3)
     achieved = byts / (kern_ms / 1e3) / 1e9
-    traffic = read_traffic()
+    traffic = None if ck_every else read_traffic()
     res = {
         "metric": "GDN prefill tokens/s and TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -420,7 +432,8 @@ def main():
         "config": {"workload": w.name, "sequences": w.N, "tokens": w.T, "hqk": w.Hqk, "hv": w.Hv,
                    "head_dim": D, "state": str(w.initial_state.dtype).replace("torch.", "")
                    if w.initial_state is not None else None, "l2norm": w.use_qk_l2norm,
-                   "batch_invariant": bool(args.batch_invariant)},
+                   "batch_invariant": bool(args.batch_invariant),
+                   **({"checkpoint_interval": ck_every} if ck_every else {})},
         "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
         "mfma_frac": round(flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": round(kern_ms, 4),

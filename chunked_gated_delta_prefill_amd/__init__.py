@@ -10,6 +10,11 @@ The entry points mirror the C functions::
     gdn_chunk_prefill(q, k, v, g, beta, scale, cu_seqlens, initial_state,
                       output_state, use_qk_l2norm, batch_invariant, out,
                       stream=None)
+    gdn_chunk_prefill_checkpointed(q, k, v, g, beta, scale, cu_seqlens,
+                                   initial_state, output_state, use_qk_l2norm,
+                                   batch_invariant, checkpoints,
+                                   checkpoints_per_sequence, checkpoint_interval,
+                                   out, stream=None)
     gdn_decode_step(q, k, v, g, beta, scale, state_in, state_out,
                     use_qk_l2norm, out, stream=None)
 
@@ -53,6 +58,10 @@ def load():
         lib.gdn_chunk_prefill.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int,
                                           ctypes.c_int, P, ctypes.c_void_p]
         lib.gdn_chunk_prefill.restype = ctypes.c_int
+        lib.gdn_chunk_prefill_checkpointed.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int,
+                                                       ctypes.c_int, P, ctypes.c_int32, ctypes.c_int64, P,
+                                                       ctypes.c_void_p]
+        lib.gdn_chunk_prefill_checkpointed.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_int, P, ctypes.c_void_p]
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_last_error.argtypes = []
@@ -116,6 +125,33 @@ def gdn_chunk_prefill(q, k, v, g, beta, scale, cu_seqlens, initial_state, output
                        0.0 if scale is None else float(scale), describe(cu_seqlens),
                        describe(initial_state), describe(output_state), use_qk_l2norm,
                        batch_invariant, describe(out), stream)
+    if rc != 0:
+        raise GdnError(rc, msg)
+
+
+def call_checkpointed_raw(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, use_qk_l2norm,
+                          batch_invariant, checkpoints, per_seq, interval, out, stream):
+    """Calls gdn_chunk_prefill_checkpointed on descriptors; returns the status code and message."""
+    lib = load()
+    ref = lambda d: None if d is None else ctypes.byref(d)
+    rc = lib.gdn_chunk_prefill_checkpointed(ref(q), ref(k), ref(v), ref(g), ref(beta), ctypes.c_float(scale),
+                                            ref(cu_seqlens), ref(initial_state), ref(output_state),
+                                            int(bool(use_qk_l2norm)), int(bool(batch_invariant)), ref(checkpoints),
+                                            int(per_seq), int(interval), ref(out), stream)
+    return rc, (lib.gdn_last_error() or b"").decode()
+
+
+def gdn_chunk_prefill_checkpointed(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state,
+                                   use_qk_l2norm, batch_invariant, checkpoints, checkpoints_per_sequence,
+                                   checkpoint_interval, out, stream=None):
+    """The scan, also writing the state every ``checkpoint_interval`` tokens of each sequence into
+    ``checkpoints`` ([N * checkpoints_per_sequence, Hv, 128, 128])."""
+    stream = _stream_handle(stream, q)
+    rc, msg = call_checkpointed_raw(describe(q), describe(k), describe(v), describe(g), describe(beta),
+                                    0.0 if scale is None else float(scale), describe(cu_seqlens),
+                                    describe(initial_state), describe(output_state), use_qk_l2norm,
+                                    batch_invariant, describe(checkpoints), checkpoints_per_sequence,
+                                    checkpoint_interval, describe(out), stream)
     if rc != 0:
         raise GdnError(rc, msg)
 

@@ -188,11 +188,12 @@ extern "C" void gdn_release_workspace(void) {
     (void)hipGetLastError();
 }
 
-extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
-                                 const gdn_tensor *g, const gdn_tensor *beta, float scale,
-                                 const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
-                                 const gdn_tensor *output_state, int use_qk_l2norm,
-                                 int batch_invariant, const gdn_tensor *out, void *stream) {
+namespace {
+
+int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, const gdn_tensor *g,
+                 const gdn_tensor *beta, float scale, const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                 const gdn_tensor *output_state, int use_qk_l2norm, int batch_invariant, const gdn_tensor *ckpt,
+                 int32_t ck_per_seq, int64_t ck_interval, const gdn_tensor *out, void *stream) {
     g_last_error.clear();
     std::string msg;
     int rc;
@@ -292,6 +293,26 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
         return fail(GDN_ERR_ALIAS, "output_state must not alias initial_state");
     if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale must be finite");
 
+    // ---- state checkpoints
+    if (ckpt) {
+        if ((rc = check_basic(ckpt, "checkpoints", 4, msg))) return fail(rc, msg);
+        if (ckpt->dtype != GDN_F32 && ckpt->dtype != GDN_BF16)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "checkpoints must be f32 or bf16");
+        if (ck_per_seq < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "checkpoints_per_sequence must be >= 1");
+        if (ck_interval < gdn::kChunk || ck_interval % gdn::kChunk != 0 || ck_interval > ((int64_t)1 << 30))
+            return fail(GDN_ERR_UNSUPPORTED, "checkpoint_interval must be a positive multiple of 64 tokens");
+        if (ckpt->sizes[0] != N * ck_per_seq || ckpt->sizes[1] != Hv || ckpt->sizes[2] != gdn::kHeadDim ||
+            ckpt->sizes[3] != gdn::kHeadDim)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "checkpoints must be [N * checkpoints_per_sequence, Hv, 128, 128]");
+        const int64_t se = (int64_t)dt_size(ckpt->dtype);
+        if (N > 0 && (!aligned16(ckpt->data, (size_t)se, ckpt->strides, 3) || ckpt->strides[2] < gdn::kHeadDim ||
+                      ckpt->strides[2] * se * gdn::kHeadDim >= kRowLimit))
+            return fail(GDN_ERR_UNSUPPORTED, "checkpoints: rows must be 16-byte aligned, >= 128 elements apart");
+        if (N > 0 && ((initial_state && ckpt->data == initial_state->data) ||
+                      (output_state && ckpt->data == output_state->data)))
+            return fail(GDN_ERR_ALIAS, "checkpoints must not alias initial_state or output_state");
+    }
+
     // ---- device
     int dev = 0, cus = 256;
     if ((rc = check_device(msg, &dev, &cus))) return fail(rc, msg);
@@ -332,6 +353,13 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
     p.o_st = (int32_t)(out->strides[0] * es); p.o_sh = out->strides[1] * es;
     p.scale = scale == 0.0f ? 1.0f / std::sqrt((float)gdn::kHeadDim) : scale;
     p.N = (int32_t)N; p.Hqk = (int32_t)Hqk; p.Hv = (int32_t)Hv; p.r = (int32_t)(Hv / Hqk);
+    if (ckpt) {
+        const int64_t se = (int64_t)dt_size(ckpt->dtype);
+        p.ck = static_cast<char *>(ckpt->data);
+        p.ck_n = ckpt->strides[0] * se; p.ck_h = ckpt->strides[1] * se;
+        p.ck_v = (int32_t)(ckpt->strides[2] * se); p.ck_dt = ckpt->dtype;
+        p.ck_per_seq = ck_per_seq; p.ck_every = (int32_t)(ck_interval / gdn::kChunk);
+    }
     p.l2norm = use_qk_l2norm != 0;
     const bool bf = io == GDN_BF16;
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -382,6 +410,32 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
         (e = gdn::launch_fused_scan(p, bf, gdn::kScan, hs)) != hipSuccess)
         return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                                 const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                                 const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                                 const gdn_tensor *output_state, int use_qk_l2norm,
+                                 int batch_invariant, const gdn_tensor *out, void *stream) {
+    return prefill_impl(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, use_qk_l2norm,
+                        batch_invariant, nullptr, 0, 0, out, stream);
+}
+
+extern "C" int gdn_chunk_prefill_checkpointed(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                                              const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                                              const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                                              const gdn_tensor *output_state, int use_qk_l2norm,
+                                              int batch_invariant, const gdn_tensor *checkpoints,
+                                              int32_t checkpoints_per_sequence, int64_t checkpoint_interval,
+                                              const gdn_tensor *out, void *stream) {
+    if (!checkpoints) {
+        g_last_error = "checkpoints is required (use gdn_chunk_prefill without checkpoints)";
+        return GDN_ERR_INVALID_ARGUMENT;
+    }
+    return prefill_impl(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, use_qk_l2norm,
+                        batch_invariant, checkpoints, checkpoints_per_sequence, checkpoint_interval, out, stream);
 }
 
 extern "C" int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,

@@ -57,6 +57,12 @@ struct ScanParams {
     const int32_t *nsegs;           // number of valid entries (device)
     int32_t seg_cap;                // entries the grid covers
     float *ws_n, *ws_m, *ws_sin;    // [seg_cap][Hv][128][128] fp32, V-major
+    // state checkpoints (ck == nullptr: none): slot n * ck_per_seq + i holds the
+    // state after (i + 1) * ck_every chunks of sequence n
+    char *ck;
+    int64_t ck_n, ck_h;             // slot and head strides (bytes)
+    int32_t ck_v, ck_dt;            // row stride (bytes), dtype
+    int32_t ck_per_seq, ck_every;   // slots per sequence, chunks between checkpoints
 };
 
 // Fix-up of the split path: per (sequence, value head), serially over its

@@ -148,6 +148,8 @@ fused_scan_kernel(const ScanParams p) {
     }
 
     const int nchunks = (int)((eos - bos + C - 1) / C);
+    // chunks of the sequence before this work item (segments start on chunk bounds)
+    const int seq_chunk0 = (MODE == kScan && p.ck && p.segs) ? (int)((bos - load_cu(p.cu, n, p.cu_i64)) / C) : 0;
     float sigma = 1.f;          // true state = sigma * S (uniform across the workgroup)
     Prefetch<IO> pf;
     if (nchunks > 0) issue_loads<IO>(pf, p, chunk_at(bos, eos, 0), hq, h, threadIdx.x, threadIdx.x & 63, threadIdx.x >> 6);
@@ -714,6 +716,22 @@ fused_scan_kernel(const ScanParams p) {
                 }
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) S[bb] = M::run(kt[cur][bb], ub[k / S32][k % S32], S[bb]);
+            }
+        }
+        // ---- state checkpoint at a full chunk that ends on a checkpoint boundary:
+        // the lazy scale is folded into the state first (a renorm), then stored
+        if constexpr (MODE == kScan) {
+            const int done = seq_chunk0 + c + 1;
+            if (p.ck && Lc == C && done % p.ck_every == 0 && done / p.ck_every <= p.ck_per_seq) {
+                if (sigma != 1.f) {
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) S[bb][rr] *= sigma;
+                    sigma = 1.f;
+                }
+                const int64_t slot = (int64_t)n * p.ck_per_seq + done / p.ck_every - 1;
+                store_state<BF>(S, p.ck + slot * p.ck_n + h * p.ck_h, p.ck_v, p.ck_dt, v0, h32);
             }
         }
         __syncthreads();

@@ -112,6 +112,33 @@ int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor
                       int batch_invariant, const gdn_tensor *out, void *stream);
 
 /*
+ * gdn_chunk_prefill_checkpointed - gdn_chunk_prefill that also writes the
+ * state at fixed token intervals of every sequence (the state checkpointing
+ * that "flashinfer.cudnn", Linear attention, lists among the arguments the
+ * routing layer handles before cuDNN is called).
+ *
+ *   checkpoints               [N * P, Hv, 128, 128] F32 or BF16 (required),
+ *                             V-major like the states, rows 16-byte aligned;
+ *                             must not share its data pointer with
+ *                             initial_state or output_state.
+ *   checkpoints_per_sequence  P >= 1.
+ *   checkpoint_interval       I tokens, a positive multiple of 64.
+ *
+ * Slot n * P + i receives the state of sequence n after its first (i + 1) * I
+ * tokens, for every i < P with (i + 1) * I <= length of sequence n; other
+ * slots are left as they are (a checkpoint at the sequence end equals the
+ * final state).  All other arguments, ownership and errors as for
+ * gdn_chunk_prefill.
+ */
+int gdn_chunk_prefill_checkpointed(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                                   const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                                   const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                                   const gdn_tensor *output_state, int use_qk_l2norm,
+                                   int batch_invariant, const gdn_tensor *checkpoints,
+                                   int32_t checkpoints_per_sequence, int64_t checkpoint_interval,
+                                   const gdn_tensor *out, void *stream);
+
+/*
  * gdn_decode_step - one recurrent step for a batch of N sequences, one new
  * token each: the decode-side update that continues from the state a prefill
  * hands over ("flashinfer.gdn_prefill": the chunked scan initialises the

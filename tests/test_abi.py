@@ -25,7 +25,8 @@ def _declared_functions():
 
 def test_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["gdn_chunk_prefill", "gdn_decode_step", "gdn_last_error", "gdn_release_workspace"]
+    assert names == ["gdn_chunk_prefill", "gdn_chunk_prefill_checkpointed", "gdn_decode_step", "gdn_last_error",
+                     "gdn_release_workspace"]
     L = lib.load()
     for n in names:
         assert hasattr(L, n), n
@@ -186,3 +187,45 @@ def test_decode_in_place_view_is_accepted():
     assert rc == NO_DEVICE, (rc, msg)
     rc, _ = _dcall(_dargs(g=None, beta=None, s0=None, s1=None))
     assert rc == NO_DEVICE
+
+
+# ---- gdn_chunk_prefill_checkpointed (N = 2 sequences, P = 3 slots each)
+
+def _ccall(ck=None, per_seq=3, interval=128, **over):
+    a = _args(**over)
+    if ck is None:
+        ck = _t([6, 4, 128, 128], GDN_F32, FAKE + (1 << 33))
+    return lib.call_checkpointed_raw(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["cu"], a["s0"],
+                                     a["s1"], a["l2"], a["bi"], ck, per_seq, interval, a["out"], None)
+
+
+CKPT_CASES = {
+    "interval_not_chunk_multiple": (dict(interval=100), UNSUPPORTED),
+    "interval_zero": (dict(interval=0), UNSUPPORTED),
+    "per_seq_zero": (dict(per_seq=0, ck=_t([0, 4, 128, 128], GDN_F32, FAKE + (1 << 33))), INVALID),
+    "slots_mismatch": (dict(ck=_t([5, 4, 128, 128], GDN_F32, FAKE + (1 << 33))), INVALID),
+    "dtype": (dict(ck=_t([6, 4, 128, 128], GDN_F16, FAKE + (1 << 33))), INVALID),
+    "aliases_output_state": (dict(ck=_t([6, 4, 128, 128], GDN_F32, FAKE + (1 << 31))), ALIAS),
+    "misaligned": (dict(ck=_t([6, 4, 128, 128], GDN_F32, FAKE + (1 << 33) + 8)), UNSUPPORTED),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CKPT_CASES))
+def test_checkpointed_rejected_before_any_device_access(name):
+    rc, msg = _ccall(**CKPT_CASES[name][0])
+    assert rc == CKPT_CASES[name][1], (rc, msg)
+    assert msg
+
+
+def test_checkpointed_requires_checkpoints():
+    a = _args()
+    rc, msg = lib.call_checkpointed_raw(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["cu"], a["s0"],
+                                        a["s1"], a["l2"], a["bi"], None, 1, 64, a["out"], None)
+    assert rc == INVALID and msg
+
+
+def test_checkpointed_valid_call_without_gpu():
+    if _has_gpu():
+        pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
+    rc, msg = _ccall()
+    assert rc == NO_DEVICE, (rc, msg)
