@@ -343,6 +343,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 --pmc output dirs; the last argument is the output file")
     ap.add_argument("--decode", action="store_true", help="time the decode step instead of the prefill")
+    ap.add_argument("--pooled", action="store_true",
+                    help="states in an indexed pool (gdn_chunk_prefill_pooled, reversed index order)")
     ap.add_argument("--checkpoint-interval", type=int, default=0,
                     help="tokens between state checkpoints (gdn_chunk_prefill_checkpointed); 0 = plain scan")
     ap.add_argument("--trace-command", default="?")
@@ -394,8 +396,15 @@ def main():
         ck = torch.empty(w.N * per_seq, w.Hv, D, D, dtype=torch.float32, device="cuda")
         byts += sum(L // ck_every for L in w.lengths()) * w.Hv * D * D * 4   # checkpoint writes
 
+    if args.pooled:
+        pool = w.initial_state.clone()
+        pidx = torch.arange(w.N - 1, -1, -1, dtype=torch.int32, device="cuda")
+
     def step():
-        if ck_every:
+        if args.pooled:
+            gdn.gdn_chunk_prefill_pooled(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, pool, pidx,
+                                         w.use_qk_l2norm, bool(args.batch_invariant), out, stream)
+        elif ck_every:
             gdn.gdn_chunk_prefill_checkpointed(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state,
                                                fin, w.use_qk_l2norm, bool(args.batch_invariant), ck, per_seq,
                                                ck_every, out, stream)
@@ -422,7 +431,7 @@ def main():
     kern_ms = statistics.mean(launch_ms)
     value = w.T / (ms_step / 1e3)
     achieved = byts / (kern_ms / 1e3) / 1e9
-    traffic = None if ck_every else read_traffic()
+    traffic = None if (ck_every or args.pooled) else read_traffic()
     res = {
         "metric": "GDN prefill tokens/s and TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -433,7 +442,8 @@ def main():
                    "head_dim": D, "state": str(w.initial_state.dtype).replace("torch.", "")
                    if w.initial_state is not None else None, "l2norm": w.use_qk_l2norm,
                    "batch_invariant": bool(args.batch_invariant),
-                   **({"checkpoint_interval": ck_every} if ck_every else {})},
+                   **({"checkpoint_interval": ck_every} if ck_every else {}),
+                   **({"pooled": True} if args.pooled else {})},
         "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
         "mfma_frac": round(flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": round(kern_ms, 4),

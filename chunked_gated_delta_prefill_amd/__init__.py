@@ -15,6 +15,9 @@ The entry points mirror the C functions::
                                    batch_invariant, checkpoints,
                                    checkpoints_per_sequence, checkpoint_interval,
                                    out, stream=None)
+    gdn_chunk_prefill_pooled(q, k, v, g, beta, scale, cu_seqlens, state_pool,
+                             state_indices, use_qk_l2norm, batch_invariant, out,
+                             stream=None)
     gdn_decode_step(q, k, v, g, beta, scale, state_in, state_out,
                     use_qk_l2norm, out, stream=None)
 
@@ -62,6 +65,9 @@ def load():
                                                        ctypes.c_int, P, ctypes.c_int32, ctypes.c_int64, P,
                                                        ctypes.c_void_p]
         lib.gdn_chunk_prefill_checkpointed.restype = ctypes.c_int
+        lib.gdn_chunk_prefill_pooled.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int, ctypes.c_int,
+                                                 P, ctypes.c_void_p]
+        lib.gdn_chunk_prefill_pooled.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_int, P, ctypes.c_void_p]
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_last_error.argtypes = []
@@ -152,6 +158,28 @@ def gdn_chunk_prefill_checkpointed(q, k, v, g, beta, scale, cu_seqlens, initial_
                                     describe(initial_state), describe(output_state), use_qk_l2norm,
                                     batch_invariant, describe(checkpoints), checkpoints_per_sequence,
                                     checkpoint_interval, describe(out), stream)
+    if rc != 0:
+        raise GdnError(rc, msg)
+
+
+def call_pooled_raw(q, k, v, g, beta, scale, cu_seqlens, state_pool, state_indices, use_qk_l2norm, batch_invariant,
+                    out, stream):
+    """Calls gdn_chunk_prefill_pooled on descriptors; returns the status code and message."""
+    lib = load()
+    ref = lambda d: None if d is None else ctypes.byref(d)
+    rc = lib.gdn_chunk_prefill_pooled(ref(q), ref(k), ref(v), ref(g), ref(beta), ctypes.c_float(scale),
+                                      ref(cu_seqlens), ref(state_pool), ref(state_indices), int(bool(use_qk_l2norm)),
+                                      int(bool(batch_invariant)), ref(out), stream)
+    return rc, (lib.gdn_last_error() or b"").decode()
+
+
+def gdn_chunk_prefill_pooled(q, k, v, g, beta, scale, cu_seqlens, state_pool, state_indices, use_qk_l2norm,
+                             batch_invariant, out, stream=None):
+    """The scan on an indexed state pool: sequence n reads and rewrites ``state_pool[state_indices[n]]``."""
+    stream = _stream_handle(stream, q)
+    rc, msg = call_pooled_raw(describe(q), describe(k), describe(v), describe(g), describe(beta),
+                              0.0 if scale is None else float(scale), describe(cu_seqlens), describe(state_pool),
+                              describe(state_indices), use_qk_l2norm, batch_invariant, describe(out), stream)
     if rc != 0:
         raise GdnError(rc, msg)
 

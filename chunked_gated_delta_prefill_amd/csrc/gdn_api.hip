@@ -193,7 +193,8 @@ namespace {
 int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, const gdn_tensor *g,
                  const gdn_tensor *beta, float scale, const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
                  const gdn_tensor *output_state, int use_qk_l2norm, int batch_invariant, const gdn_tensor *ckpt,
-                 int32_t ck_per_seq, int64_t ck_interval, const gdn_tensor *out, void *stream) {
+                 int32_t ck_per_seq, int64_t ck_interval, const gdn_tensor *state_indices, const gdn_tensor *out,
+                 void *stream) {
     g_last_error.clear();
     std::string msg;
     int rc;
@@ -277,20 +278,27 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
         if ((rc = check_basic(st[i], st_name[i], 4, msg))) return fail(rc, msg);
         if (st[i]->dtype != GDN_F32 && st[i]->dtype != GDN_BF16)
             return fail(GDN_ERR_INVALID_ARGUMENT, std::string(st_name[i]) + " must be f32 or bf16");
-        if (st[i]->sizes[0] != N || st[i]->sizes[1] != Hv || st[i]->sizes[2] != gdn::kHeadDim ||
+        if ((!state_indices && st[i]->sizes[0] != N) || st[i]->sizes[1] != Hv || st[i]->sizes[2] != gdn::kHeadDim ||
             st[i]->sizes[3] != gdn::kHeadDim)
             return fail(GDN_ERR_INVALID_ARGUMENT, std::string(st_name[i]) + " must be [N, Hv, 128, 128]");
     }
     for (int i = 0; i < 2; ++i) {
-        if (!st[i] || N == 0) continue;
+        if (!st[i] || N == 0 || st[i]->sizes[0] == 0) continue;
         const int64_t se = (int64_t)dt_size(st[i]->dtype);
         if (!aligned16(st[i]->data, (size_t)se, st[i]->strides, 3) || st[i]->strides[2] < gdn::kHeadDim ||
             st[i]->strides[2] * se * gdn::kHeadDim >= kRowLimit)
             return fail(GDN_ERR_UNSUPPORTED, std::string(st_name[i]) +
                                                  ": rows must be 16-byte aligned, >= 128 elements apart (pointer and strides)");
     }
-    if (initial_state && output_state && initial_state->data == output_state->data && N > 0)
+    if (!state_indices && initial_state && output_state && initial_state->data == output_state->data && N > 0)
         return fail(GDN_ERR_ALIAS, "output_state must not alias initial_state");
+    if (state_indices) {
+        if ((rc = check_basic(state_indices, "state_indices", 1, msg))) return fail(rc, msg);
+        if (state_indices->dtype != GDN_I32 && state_indices->dtype != GDN_I64)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "state_indices must be i32 or i64");
+        if (state_indices->sizes[0] != N || (N > 0 && state_indices->data == nullptr))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "state_indices must hold N entries");
+    }
     if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale must be finite");
 
     // ---- state checkpoints
@@ -353,6 +361,11 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     p.o_st = (int32_t)(out->strides[0] * es); p.o_sh = out->strides[1] * es;
     p.scale = scale == 0.0f ? 1.0f / std::sqrt((float)gdn::kHeadDim) : scale;
     p.N = (int32_t)N; p.Hqk = (int32_t)Hqk; p.Hv = (int32_t)Hv; p.r = (int32_t)(Hv / Hqk);
+    if (state_indices) {
+        p.sidx = state_indices->data;
+        p.sidx_i64 = state_indices->dtype == GDN_I64;
+        p.pool_rows = initial_state ? initial_state->sizes[0] : 0;
+    }
     if (ckpt) {
         const int64_t se = (int64_t)dt_size(ckpt->dtype);
         p.ck = static_cast<char *>(ckpt->data);
@@ -403,6 +416,7 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     f.s_in = p.s_in; f.si_n = p.si_n; f.si_h = p.si_h; f.si_v = p.si_v; f.si_dt = p.si_dt;
     f.ws_n = p.ws_n; f.ws_m = p.ws_m; f.ws_sin = p.ws_sin;
     f.N = (int32_t)N; f.Hv = (int32_t)Hv;
+    f.sidx = p.sidx; f.sidx_i64 = p.sidx_i64; f.pool_rows = p.pool_rows;
     if ((e = gdn::launch_plan(p.cu, p.cu_i64, (int)N, lseg, segs, nsegs, seg_first, (int)cap, hs)) != hipSuccess ||
         (e = gdn::launch_fused_scan(p, bf, gdn::kMapN, hs)) != hipSuccess ||
         (e = gdn::launch_fused_scan(p, bf, gdn::kMapM, hs)) != hipSuccess ||
@@ -420,7 +434,7 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
                                  const gdn_tensor *output_state, int use_qk_l2norm,
                                  int batch_invariant, const gdn_tensor *out, void *stream) {
     return prefill_impl(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, use_qk_l2norm,
-                        batch_invariant, nullptr, 0, 0, out, stream);
+                        batch_invariant, nullptr, 0, 0, nullptr, out, stream);
 }
 
 extern "C" int gdn_chunk_prefill_checkpointed(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
@@ -435,7 +449,21 @@ extern "C" int gdn_chunk_prefill_checkpointed(const gdn_tensor *q, const gdn_ten
         return GDN_ERR_INVALID_ARGUMENT;
     }
     return prefill_impl(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, use_qk_l2norm,
-                        batch_invariant, checkpoints, checkpoints_per_sequence, checkpoint_interval, out, stream);
+                        batch_invariant, checkpoints, checkpoints_per_sequence, checkpoint_interval, nullptr, out,
+                        stream);
+}
+
+extern "C" int gdn_chunk_prefill_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                                        const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                                        const gdn_tensor *cu_seqlens, const gdn_tensor *state_pool,
+                                        const gdn_tensor *state_indices, int use_qk_l2norm, int batch_invariant,
+                                        const gdn_tensor *out, void *stream) {
+    if (!state_pool || !state_indices) {
+        g_last_error = "state_pool and state_indices are required";
+        return GDN_ERR_INVALID_ARGUMENT;
+    }
+    return prefill_impl(q, k, v, g, beta, scale, cu_seqlens, state_pool, state_pool, use_qk_l2norm, batch_invariant,
+                        nullptr, 0, 0, state_indices, out, stream);
 }
 
 extern "C" int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,

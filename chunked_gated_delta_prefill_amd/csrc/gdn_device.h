@@ -174,6 +174,14 @@ __device__ __forceinline__ int64_t load_cu(const void *cu, int i, int is64) {
     return is64 ? static_cast<const int64_t *>(cu)[i] : (int64_t) static_cast<const int32_t *>(cu)[i];
 }
 
+// Row of the caller's state buffers used by sequence n: n itself, or its entry
+// in the state index array (-1 when that entry is outside [0, rows)).
+__device__ __forceinline__ int64_t state_row(const void *sidx, int is64, int64_t rows, int n) {
+    if (!sidx) return n;
+    const int64_t ix = load_cu(sidx, n, is64);
+    return (ix >= 0 && ix < rows) ? ix : -1;
+}
+
 // Gate loads keep the raw bits; they are converted when first used, so the
 // load is not waited for when it is issued.
 __device__ __forceinline__ uint32_t gate_bits(__amdgpu_buffer_rsrc_t r, int off, int dt) {

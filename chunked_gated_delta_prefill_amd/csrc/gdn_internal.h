@@ -63,6 +63,11 @@ struct ScanParams {
     int64_t ck_n, ck_h;             // slot and head strides (bytes)
     int32_t ck_v, ck_dt;            // row stride (bytes), dtype
     int32_t ck_per_seq, ck_every;   // slots per sequence, chunks between checkpoints
+    // indexed state pool (sidx == nullptr: states indexed by sequence): sequence n
+    // uses row sidx[n] of s_in / s_out; rows outside [0, pool_rows) mean no state
+    const void *sidx;
+    int32_t sidx_i64;
+    int64_t pool_rows;
 };
 
 // Fix-up of the split path: per (sequence, value head), serially over its
@@ -76,6 +81,9 @@ struct FixParams {
     const float *ws_n, *ws_m;
     float *ws_sin;
     int32_t N, Hv;
+    const void *sidx;               // as ScanParams::sidx
+    int32_t sidx_i64;
+    int64_t pool_rows;
 };
 
 // One decode step (gdn_decode_step): byte strides over (sequence, head).

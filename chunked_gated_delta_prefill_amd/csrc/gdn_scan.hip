@@ -126,6 +126,7 @@ fused_scan_kernel(const ScanParams p) {
         eos = load_cu(p.cu, n + 1, p.cu_i64);
     }
     const int64_t map_off = ((int64_t)item * p.Hv + h) * kMapBytes;
+    const int64_t srow = state_row(p.sidx, p.sidx_i64, p.pool_rows, n);
 
     // ---- initial state: S[b] holds S^T rows k = 32b + acc_row(r, h32), column v0
     f32x16 S[4];
@@ -135,10 +136,13 @@ fused_scan_kernel(const ScanParams p) {
         const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
         const int h32 = lane >> 5, v0 = ws * 32 + (lane & 31);
         if (MODE == kScan) {
-            if (!first)
+            // a pooled state is read and written in place: the first segment of a
+            // split sequence takes it from the workspace (copied there by the
+            // fix-up), so no work item reads a row another one may be writing
+            if (!first || (p.sidx && !last))
                 load_state<BF>(S, reinterpret_cast<const char *>(p.ws_sin) + map_off, D * 4, GDN_F32, v0, h32);
-            else if (p.s_in)
-                load_state<BF>(S, p.s_in + n * p.si_n + h * p.si_h, p.si_v, p.si_dt, v0, h32);
+            else if (p.s_in && srow >= 0)
+                load_state<BF>(S, p.s_in + srow * p.si_n + h * p.si_h, p.si_v, p.si_dt, v0, h32);
         } else if (MODE == kMapM) {           // identity: S^T[k][v0] = (k == v0)
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
@@ -739,7 +743,7 @@ fused_scan_kernel(const ScanParams p) {
 
     // ---- final state (scan: the caller's output state, by the last segment only;
     // maps: the workspace)
-    const bool write_caller = MODE == kScan && last && p.s_out;
+    const bool write_caller = MODE == kScan && last && p.s_out && srow >= 0;
     if (write_caller || MODE != kScan) {
         if (sigma != 1.f) {
 #pragma unroll
@@ -750,7 +754,7 @@ fused_scan_kernel(const ScanParams p) {
         const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
         const int h32 = lane >> 5, v0 = ws * 32 + (lane & 31);
         if (MODE == kScan)
-            store_state<BF>(S, p.s_out + n * p.so_n + h * p.so_h, p.so_v, p.so_dt, v0, h32);
+            store_state<BF>(S, p.s_out + srow * p.so_n + h * p.so_h, p.so_v, p.so_dt, v0, h32);
         else
             store_state<BF>(S, reinterpret_cast<char *>(MODE == kMapN ? p.ws_n : p.ws_m) + map_off, D * 4, GDN_F32, v0,
                         h32);
@@ -827,7 +831,11 @@ __global__ __launch_bounds__(256) void fixup_kernel(const FixParams f) {
     f32x16 S[4];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) S[bb] = zero16();
-    if (f.s_in) load_state<false>(S, f.s_in + n * f.si_n + h * f.si_h, f.si_v, f.si_dt, v0, h32);
+    const int64_t srow = state_row(f.sidx, f.sidx_i64, f.pool_rows, n);
+    if (f.s_in && srow >= 0) load_state<false>(S, f.s_in + srow * f.si_n + h * f.si_h, f.si_v, f.si_dt, v0, h32);
+    if (f.sidx)   // the first segment of a pooled sequence starts from this copy
+        store_state<false>(S, reinterpret_cast<char *>(f.ws_sin) + ((int64_t)s0 * f.Hv + h) * kMapBytes, D * 4,
+                           GDN_F32, v0, h32);
     for (int i = 0; i + 1 < cnt; ++i) {
         const int64_t off = ((int64_t)(s0 + i) * f.Hv + h) * kMapBytes;
         const float *Mg = reinterpret_cast<const float *>(reinterpret_cast<const char *>(f.ws_m) + off);

@@ -139,6 +139,30 @@ int gdn_chunk_prefill_checkpointed(const gdn_tensor *q, const gdn_tensor *k, con
                                    const gdn_tensor *out, void *stream);
 
 /*
+ * gdn_chunk_prefill_pooled - gdn_chunk_prefill on an indexed state pool,
+ * updated in place (the indexed state pools that "flashinfer.cudnn", Linear
+ * attention, lists among the arguments the routing layer handles before cuDNN
+ * is called).
+ *
+ *   state_pool      [S, Hv, 128, 128] F32 or BF16, V-major, rows 16-byte
+ *                   aligned (required): both the initial and the final states.
+ *   state_indices   [N] I32 or I64 in device memory, contiguous (required).
+ *                   Sequence n starts from state_pool[state_indices[n]] and
+ *                   its final state is written back there.  An entry outside
+ *                   [0, S) means a zero initial state and no state written.
+ *                   Entries in [0, S) must be distinct (an unchecked
+ *                   precondition: they are never read on the host).
+ *
+ * Rows of the pool no sequence names are left as they are.  All other
+ * arguments, ownership and errors as for gdn_chunk_prefill.
+ */
+int gdn_chunk_prefill_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                             const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                             const gdn_tensor *cu_seqlens, const gdn_tensor *state_pool,
+                             const gdn_tensor *state_indices, int use_qk_l2norm, int batch_invariant,
+                             const gdn_tensor *out, void *stream);
+
+/*
  * gdn_decode_step - one recurrent step for a batch of N sequences, one new
  * token each: the decode-side update that continues from the state a prefill
  * hands over ("flashinfer.gdn_prefill": the chunked scan initialises the

@@ -25,8 +25,8 @@ def _declared_functions():
 
 def test_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["gdn_chunk_prefill", "gdn_chunk_prefill_checkpointed", "gdn_decode_step", "gdn_last_error",
-                     "gdn_release_workspace"]
+    assert names == ["gdn_chunk_prefill", "gdn_chunk_prefill_checkpointed", "gdn_chunk_prefill_pooled",
+                     "gdn_decode_step", "gdn_last_error", "gdn_release_workspace"]
     L = lib.load()
     for n in names:
         assert hasattr(L, n), n
@@ -228,4 +228,38 @@ def test_checkpointed_valid_call_without_gpu():
     if _has_gpu():
         pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
     rc, msg = _ccall()
+    assert rc == NO_DEVICE, (rc, msg)
+
+
+# ---- gdn_chunk_prefill_pooled (N = 2 sequences, a pool of 5 rows)
+
+def _pcall(pool="default", idx="default", **over):
+    a = _args(**over)
+    pool = _t([5, 4, 128, 128], GDN_F32, FAKE + (1 << 30)) if pool == "default" else pool
+    idx = _t([2], GDN_I32, FAKE + (1 << 34)) if idx == "default" else idx
+    return lib.call_pooled_raw(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["cu"], pool, idx,
+                               a["l2"], a["bi"], a["out"], None)
+
+
+POOL_CASES = {
+    "pool_missing": (dict(pool=None), INVALID),
+    "indices_missing": (dict(idx=None), INVALID),
+    "indices_dtype": (dict(idx=_t([2], GDN_F32, FAKE + (1 << 34))), INVALID),
+    "indices_count": (dict(idx=_t([3], GDN_I64, FAKE + (1 << 34))), INVALID),
+    "pool_heads": (dict(pool=_t([5, 2, 128, 128], GDN_F32, FAKE + (1 << 30))), INVALID),
+    "pool_dtype": (dict(pool=_t([5, 4, 128, 128], GDN_F16, FAKE + (1 << 30))), INVALID),
+}
+
+
+@pytest.mark.parametrize("name", sorted(POOL_CASES))
+def test_pooled_rejected_before_any_device_access(name):
+    rc, msg = _pcall(**POOL_CASES[name][0])
+    assert rc == POOL_CASES[name][1], (rc, msg)
+    assert msg
+
+
+def test_pooled_valid_call_without_gpu():
+    if _has_gpu():
+        pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
+    rc, msg = _pcall()
     assert rc == NO_DEVICE, (rc, msg)
