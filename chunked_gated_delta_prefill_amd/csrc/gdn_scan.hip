@@ -75,7 +75,7 @@ template <typename IO> struct Smem {
 
 // bf16: two workgroups per CU (LDS < 80 KB) need <= 256 registers per lane;
 // fp32 (LDS-bound to one workgroup per CU) keeps the full register file.
-template <typename IO, int MODE>
+template <typename IO, int MODE, bool CK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(is_bf<IO>::value ? 2 : 1,
                                                                     is_bf<IO>::value ? 2 : 1))) void
 fused_scan_kernel(const ScanParams p) {
@@ -153,7 +153,7 @@ fused_scan_kernel(const ScanParams p) {
 
     const int nchunks = (int)((eos - bos + C - 1) / C);
     // chunks of the sequence before this work item (segments start on chunk bounds)
-    const int seq_chunk0 = (MODE == kScan && p.ck && p.segs) ? (int)((bos - load_cu(p.cu, n, p.cu_i64)) / C) : 0;
+    const int seq_chunk0 = (CK && p.segs) ? (int)((bos - load_cu(p.cu, n, p.cu_i64)) / C) : 0;
     float sigma = 1.f;          // true state = sigma * S (uniform across the workgroup)
     Prefetch<IO> pf;
     if (nchunks > 0) issue_loads<IO>(pf, p, chunk_at(bos, eos, 0), hq, h, threadIdx.x, threadIdx.x & 63, threadIdx.x >> 6);
@@ -724,9 +724,9 @@ fused_scan_kernel(const ScanParams p) {
         }
         // ---- state checkpoint at a full chunk that ends on a checkpoint boundary:
         // the lazy scale is folded into the state first (a renorm), then stored
-        if constexpr (MODE == kScan) {
+        if constexpr (CK) {
             const int done = seq_chunk0 + c + 1;
-            if (p.ck && Lc == C && done % p.ck_every == 0 && done / p.ck_every <= p.ck_per_seq) {
+            if (Lc == C && done % p.ck_every == 0 && done / p.ck_every <= p.ck_per_seq) {
                 if (sigma != 1.f) {
 #pragma unroll
                     for (int bb = 0; bb < 4; ++bb)
@@ -868,7 +868,10 @@ hipError_t launch(const ScanParams &p, hipStream_t stream) {
     const int64_t pairs = items * p.Hqk;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * p.r;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((fused_scan_kernel<IO, MODE>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    if (MODE == kScan && p.ck)   // the scan that also writes state checkpoints
+        hipLaunchKernelGGL((fused_scan_kernel<IO, kScan, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fused_scan_kernel<IO, MODE, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
