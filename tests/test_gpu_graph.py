@@ -35,7 +35,7 @@ def _replays_match(call, outs, label, replays=3):
 @pytest.mark.parametrize("split", [False, True])
 def test_prefill_graph_replay(gdn, split):
     if split:   # one long sequence on few heads: plan, maps, fix-up and scan kernels
-        w = W.build([4096, 100], 1, 4, torch.bfloat16, seed=51, gate="long").to(DEV)
+        w = W.build([8200, 100], 1, 4, torch.bfloat16, seed=51, gate="long").to(DEV)
     else:
         w = W.build([300, 64, 1, 129], 2, 4, torch.bfloat16, seed=52).to(DEV)
     out = torch.empty(w.T, w.Hv, 128, dtype=w.q.dtype, device=DEV)
@@ -56,7 +56,7 @@ def test_decode_graph_replay(gdn):
 def test_two_streams_concurrently(gdn):
     """Split-path calls on two streams at once use separate workspaces."""
     w1 = W.build([4096], 1, 4, torch.bfloat16, seed=53, gate="long").to(DEV)
-    w2 = W.build([3000], 1, 4, torch.bfloat16, seed=54, gate="long").to(DEV)
+    w2 = W.build([4100], 1, 4, torch.bfloat16, seed=54, gate="long").to(DEV)
     res = []
     for w in (w1, w2):
         out = torch.empty(w.T, w.Hv, 128, dtype=w.q.dtype, device=DEV)

@@ -165,7 +165,7 @@ def test_no_output_state_writes_nothing_else(gdn):
 def test_split_path_matches_oracle(gdn, gate):
     """Few long sequences (N * Hv far below two work items per CU) take the split
     path; empty and single-chunk sequences ride along."""
-    w = W.build([5000, 3000, 0, 1500, 64], 2, 4, torch.bfloat16, seed=31, gate=gate)
+    w = W.build([14000, 5000, 0, 1500, 64], 2, 4, torch.bfloat16, seed=31, gate=gate)
     say(f"[gpu] split path bf16 gate={gate}")
     out, fin = run_gpu(gdn, w, False)
     ro, rf = run_oracle(w)
@@ -174,12 +174,13 @@ def test_split_path_matches_oracle(gdn, gate):
     assert e1 <= BF16_TOL and e2 <= BF16_TOL
     assert torch.equal(fin[2].cpu(), w.initial_state[2])
     o_u, f_u = run_gpu(gdn, w, True)
+    assert not torch.equal(out, o_u), "the split path was not taken (results bitwise equal to the unsplit scan)"
     assert nerr(out.float(), o_u.float().cpu().numpy()) <= BF16_TOL
     assert nerr(fin, f_u.cpu().numpy()) <= BF16_TOL
 
 
 def test_split_path_fp32(gdn):
-    w = W.build([3000, 1025, 2048], 2, 2, torch.float32, seed=32, gate="long")
+    w = W.build([8000, 1025, 3300], 2, 2, torch.float32, seed=32, gate="long")
     say("[gpu] split path fp32")
     out, fin = run_gpu(gdn, w, False)
     ro, rf = run_oracle(w)
@@ -189,7 +190,7 @@ def test_split_path_fp32(gdn):
 
 
 def test_split_path_no_states(gdn):
-    w = W.build([4000, 2500], 2, 4, torch.bfloat16, seed=33, state_in=None, state_out=None)
+    w = W.build([6000, 2500], 2, 4, torch.bfloat16, seed=33, state_in=None, state_out=None)
     say("[gpu] split path without states")
     out, _ = run_gpu(gdn, w, False)
     ro, _ = run_oracle(w)
@@ -197,7 +198,7 @@ def test_split_path_no_states(gdn):
 
 
 def test_split_path_bf16_states(gdn):
-    w = W.build([3500, 0, 1100], 2, 4, torch.bfloat16, seed=34, state_in=torch.bfloat16,
+    w = W.build([10000, 0, 2400], 2, 4, torch.bfloat16, seed=34, state_in=torch.bfloat16,
                 state_out=torch.bfloat16, gate="long")
     say("[gpu] split path bf16 states")
     out, fin = run_gpu(gdn, w, False)

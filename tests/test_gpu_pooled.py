@@ -69,5 +69,5 @@ def test_pooled_fp32(gdn):
 def test_pooled_split_path(gdn):
     # one long sequence on few heads takes the split path: the pooled row is read
     # by the fix-up and rewritten by the last segment only
-    w = W.build([4096, 50], 1, 4, torch.bfloat16, seed=44, gate="long", state_in=None, name="pool_split")
+    w = W.build([8200, 50], 1, 4, torch.bfloat16, seed=44, gate="long", state_in=None, name="pool_split")
     _check(gdn, w, 6, [4, 1], False, BF16_TOL)
