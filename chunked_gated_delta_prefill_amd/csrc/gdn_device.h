@@ -220,15 +220,6 @@ __device__ __forceinline__ float quad_bcast(float v, int e) {
     }
 }
 
-// Sum over the 16 lanes of a DPP row (every lane gets the total).
-__device__ __forceinline__ __attribute__((unused)) float row_sum16(float x) {
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
-    return x;
-}
-
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 // Sum of squares of 8 bf16 values (products exact in fp32, fp32 accumulation).
@@ -388,10 +379,6 @@ __device__ __forceinline__ void issue_v_wide_part(VWide &vw, const ScanParams &p
     const auto rv = rsrc(p.v + ch.t0 * p.v_st + h * p.v_sh, L > 0 ? (L - 1) * p.v_st + D * 2 : 0);
     const int vo = (lane >> 2) * p.v_st + (32 * ws + 8 * (lane & 3)) * 2;
     vw.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * j * p.v_st, 0, 0);
-}
-__device__ __forceinline__ void issue_v_wide(VWide &vw, const ScanParams &p, ChunkRef ch, int h, int ws, int lane) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) issue_v_wide_part(vw, p, ch, h, ws, lane, j);
 }
 
 __device__ __forceinline__ ChunkRef chunk_at(int64_t bos, int64_t eos, int c) {

@@ -130,3 +130,8 @@ def test_prefill_then_decode_steps(gdn):
     e_fin = nerr(state, ref_fin)
     say(f"      final state error {e_fin:.3e}")
     assert e_fin <= BF16_TOL
+
+
+def test_decode_full_batch_in_place(gdn):
+    """The benchmarked decode configuration (256 sequences, Hqk 16, Hv 32, fp32 state updated in place)."""
+    _check(gdn, W.decode_batch(), BF16_TOL, in_place=True)
