@@ -20,6 +20,8 @@ The entry points mirror the C functions::
                              stream=None)
     gdn_decode_step(q, k, v, g, beta, scale, state_in, state_out,
                     use_qk_l2norm, out, stream=None)
+    gdn_decode_step_pooled(q, k, v, g, beta, scale, state_pool, state_indices,
+                           use_qk_l2norm, out, stream=None)
 
 All tensors are torch CUDA (HIP) tensors; ``out`` and ``output_state`` are
 written in place.  See include/gdn.h for shapes, dtypes and error codes.
@@ -70,6 +72,9 @@ def load():
         lib.gdn_chunk_prefill_pooled.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_int, P, ctypes.c_void_p]
         lib.gdn_decode_step.restype = ctypes.c_int
+        lib.gdn_decode_step_pooled.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_int, P,
+                                               ctypes.c_void_p]
+        lib.gdn_decode_step_pooled.restype = ctypes.c_int
         lib.gdn_last_error.argtypes = []
         lib.gdn_last_error.restype = ctypes.c_char_p
         lib.gdn_release_workspace.argtypes = []
@@ -199,6 +204,25 @@ def gdn_decode_step(q, k, v, g, beta, scale, state_in, state_out, use_qk_l2norm,
     rc, msg = call_decode_raw(describe(q), describe(k), describe(v), describe(g), describe(beta),
                               0.0 if scale is None else float(scale), describe(state_in), describe(state_out),
                               use_qk_l2norm, describe(out), stream)
+    if rc != 0:
+        raise GdnError(rc, msg)
+
+
+def call_decode_pooled_raw(q, k, v, g, beta, scale, state_pool, state_indices, use_qk_l2norm, out, stream):
+    """Calls gdn_decode_step_pooled on descriptors; returns the status code and message."""
+    lib = load()
+    ref = lambda d: None if d is None else ctypes.byref(d)
+    rc = lib.gdn_decode_step_pooled(ref(q), ref(k), ref(v), ref(g), ref(beta), ctypes.c_float(scale),
+                                    ref(state_pool), ref(state_indices), int(bool(use_qk_l2norm)), ref(out), stream)
+    return rc, (lib.gdn_last_error() or b"").decode()
+
+
+def gdn_decode_step_pooled(q, k, v, g, beta, scale, state_pool, state_indices, use_qk_l2norm, out, stream=None):
+    """One decode step on an indexed pool: sequence n reads and rewrites ``state_pool[state_indices[n]]``."""
+    stream = _stream_handle(stream, q)
+    rc, msg = call_decode_pooled_raw(describe(q), describe(k), describe(v), describe(g), describe(beta),
+                                     0.0 if scale is None else float(scale), describe(state_pool),
+                                     describe(state_indices), use_qk_l2norm, describe(out), stream)
     if rc != 0:
         raise GdnError(rc, msg)
 

@@ -471,10 +471,11 @@ extern "C" int gdn_chunk_prefill_pooled(const gdn_tensor *q, const gdn_tensor *k
                         nullptr, 0, 0, state_indices, out, stream);
 }
 
-extern "C" int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
-                               const gdn_tensor *g, const gdn_tensor *beta, float scale,
-                               const gdn_tensor *state_in, const gdn_tensor *state_out, int use_qk_l2norm,
-                               const gdn_tensor *out, void *stream) {
+namespace {
+
+int decode_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, const gdn_tensor *g,
+                const gdn_tensor *beta, float scale, const gdn_tensor *state_in, const gdn_tensor *state_out,
+                const gdn_tensor *state_indices, int use_qk_l2norm, const gdn_tensor *out, void *stream) {
     g_last_error.clear();
     std::string msg;
     int rc;
@@ -522,10 +523,10 @@ extern "C" int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const g
         if ((rc = check_basic(st[i], st_name[i], 4, msg))) return fail(rc, msg);
         if (st[i]->dtype != GDN_F32 && st[i]->dtype != GDN_BF16)
             return fail(GDN_ERR_INVALID_ARGUMENT, std::string(st_name[i]) + " must be f32 or bf16");
-        if (st[i]->sizes[0] != N || st[i]->sizes[1] != Hv || st[i]->sizes[2] != gdn::kHeadDim ||
+        if ((!state_indices && st[i]->sizes[0] != N) || st[i]->sizes[1] != Hv || st[i]->sizes[2] != gdn::kHeadDim ||
             st[i]->sizes[3] != gdn::kHeadDim)
             return fail(GDN_ERR_INVALID_ARGUMENT, std::string(st_name[i]) + " must be [N, Hv, 128, 128]");
-        if (N > 0 && !aligned16(st[i]->data, dt_size(st[i]->dtype), st[i]->strides, 3))
+        if (N > 0 && st[i]->sizes[0] > 0 && !aligned16(st[i]->data, dt_size(st[i]->dtype), st[i]->strides, 3))
             return fail(GDN_ERR_UNSUPPORTED, std::string(st_name[i]) + ": rows must be 16-byte aligned (pointer and strides)");
     }
     if (state_in && state_out && state_in->data == state_out->data && N > 0) {
@@ -534,12 +535,24 @@ extern "C" int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const g
         if (!same)
             return fail(GDN_ERR_ALIAS, "state_out may share state_in's buffer only as the identical view (in-place update)");
     }
+    if (state_indices) {
+        if ((rc = check_basic(state_indices, "state_indices", 1, msg))) return fail(rc, msg);
+        if (state_indices->dtype != GDN_I32 && state_indices->dtype != GDN_I64)
+            return fail(GDN_ERR_INVALID_ARGUMENT, "state_indices must be i32 or i64");
+        if (state_indices->sizes[0] != N || (N > 0 && state_indices->data == nullptr))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "state_indices must hold N entries");
+    }
     if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale must be finite");
     int dev = 0, cus = 256;
     if ((rc = check_device(msg, &dev, &cus))) return fail(rc, msg);
     if (N == 0) return GDN_OK;
 
     gdn::DecodeParams p{};
+    if (state_indices) {
+        p.sidx = state_indices->data;
+        p.sidx_i64 = state_indices->dtype == GDN_I64;
+        p.pool_rows = state_in->sizes[0];
+    }
     const int64_t es = (int64_t)esz;
     p.q = static_cast<const char *>(q->data); p.q_sn = q->strides[0] * es; p.q_sh = q->strides[1] * es;
     p.k = static_cast<const char *>(k->data); p.k_sn = k->strides[0] * es; p.k_sh = k->strides[1] * es;
@@ -574,4 +587,24 @@ extern "C" int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const g
     const hipError_t e = gdn::launch_decode(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                               const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                               const gdn_tensor *state_in, const gdn_tensor *state_out, int use_qk_l2norm,
+                               const gdn_tensor *out, void *stream) {
+    return decode_impl(q, k, v, g, beta, scale, state_in, state_out, nullptr, use_qk_l2norm, out, stream);
+}
+
+extern "C" int gdn_decode_step_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                                      const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                                      const gdn_tensor *state_pool, const gdn_tensor *state_indices,
+                                      int use_qk_l2norm, const gdn_tensor *out, void *stream) {
+    if (!state_pool || !state_indices) {
+        g_last_error = "state_pool and state_indices are required";
+        return GDN_ERR_INVALID_ARGUMENT;
+    }
+    return decode_impl(q, k, v, g, beta, scale, state_pool, state_pool, state_indices, use_qk_l2norm, out, stream);
 }

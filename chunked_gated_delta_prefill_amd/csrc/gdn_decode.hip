@@ -94,11 +94,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
     const float a = p.g ? load1(p.g + n * p.g_sn + h * p.g_sh, p.g_dt) : 1.f;
     const float b = p.beta ? load1(p.beta + n * p.b_sn + h * p.b_sh, p.b_dt) : 1.f;
 
+    // the sequence's state row: n itself, or its entry in the pool index
+    int64_t srow = n;
+    if (p.sidx) {
+        const int64_t ix = p.sidx_i64 ? reinterpret_cast<const int64_t *>(p.sidx)[n]
+                                      : (int64_t)reinterpret_cast<const int32_t *>(p.sidx)[n];
+        srow = (ix >= 0 && ix < p.pool_rows) ? ix : -1;
+    }
     // this wave's rows: v = 64 rb + 16 ws + 2 j + sub
     const int v0 = kRowsPerBlock * rb + kRowsPerWave * ws + sub;
     const int es_si = p.si_dt == GDN_F32 ? 4 : 2, es_so = p.so_dt == GDN_F32 ? 4 : 2;
-    const char *si = p.s_in ? p.s_in + n * p.si_n + h * p.si_h + c4 * es_si : nullptr;
-    char *so = p.s_out ? p.s_out + n * p.so_n + h * p.so_h + c4 * es_so : nullptr;
+    const char *si = (p.s_in && srow >= 0) ? p.s_in + srow * p.si_n + h * p.si_h + c4 * es_si : nullptr;
+    char *so = (p.s_out && srow >= 0) ? p.s_out + srow * p.so_n + h * p.so_h + c4 * es_so : nullptr;
     const char *vrow = p.v + n * p.v_sn + h * p.v_sh;
     f32x4 s[8];
     float vv[8];

@@ -102,6 +102,11 @@ struct DecodeParams {
     int64_t o_sn, o_sh;
     float scale;
     int32_t l2norm, N, Hv, r;
+    // indexed state pool (sidx == nullptr: state row n for sequence n): sequence n
+    // uses row sidx[n] of s_in / s_out; rows outside [0, pool_rows) mean no state
+    const void *sidx;
+    int32_t sidx_i64;
+    int64_t pool_rows;
 };
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 

@@ -198,6 +198,19 @@ int gdn_decode_step(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *
                     const gdn_tensor *state_in, const gdn_tensor *state_out,
                     int use_qk_l2norm, const gdn_tensor *out, void *stream);
 
+/*
+ * gdn_decode_step_pooled - gdn_decode_step on an indexed state pool, updated
+ * in place: sequence n reads and rewrites state_pool[state_indices[n]]
+ * (state_pool [S, Hv, 128, 128] F32 or BF16, state_indices [N] I32 or I64 in
+ * device memory; entries outside [0, S) mean a zero state and no write;
+ * entries in [0, S) must be distinct, an unchecked precondition).  Other
+ * arguments, ownership and errors as for gdn_decode_step.
+ */
+int gdn_decode_step_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                           const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                           const gdn_tensor *state_pool, const gdn_tensor *state_indices,
+                           int use_qk_l2norm, const gdn_tensor *out, void *stream);
+
 /* Message for the last non-zero return of a gdn_* call on this thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */
 const char *gdn_last_error(void);

@@ -26,7 +26,7 @@ def _declared_functions():
 def test_exports_every_declared_function():
     names = _declared_functions()
     assert names == ["gdn_chunk_prefill", "gdn_chunk_prefill_checkpointed", "gdn_chunk_prefill_pooled",
-                     "gdn_decode_step", "gdn_last_error", "gdn_release_workspace"]
+                     "gdn_decode_step", "gdn_decode_step_pooled", "gdn_last_error", "gdn_release_workspace"]
     L = lib.load()
     for n in names:
         assert hasattr(L, n), n
@@ -263,3 +263,20 @@ def test_pooled_valid_call_without_gpu():
         pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
     rc, msg = _pcall()
     assert rc == NO_DEVICE, (rc, msg)
+
+
+def test_decode_pooled_argument_checks():
+    a = _dargs()
+    pool = _t([7, 4, 128, 128], GDN_F32, FAKE + (1 << 30))
+    bad = [(None, _t([3], GDN_I32, FAKE + (1 << 34)), INVALID),
+           (pool, None, INVALID),
+           (pool, _t([2], GDN_I32, FAKE + (1 << 34)), INVALID),
+           (pool, _t([3], GDN_F32, FAKE + (1 << 34)), INVALID),
+           (_t([7, 2, 128, 128], GDN_F32, FAKE + (1 << 30)), _t([3], GDN_I64, FAKE + (1 << 34)), INVALID)]
+    for pl, ix, code in bad:
+        rc, msg = lib.call_decode_pooled_raw(a["q"], a["k"], a["v"], a["g"], a["beta"], 0.0, pl, ix, 1, a["out"], None)
+        assert rc == code and msg, (rc, msg)
+    if not _has_gpu():
+        rc, msg = lib.call_decode_pooled_raw(a["q"], a["k"], a["v"], a["g"], a["beta"], 0.0, pool,
+                                             _t([3], GDN_I32, FAKE + (1 << 34)), 1, a["out"], None)
+        assert rc == NO_DEVICE, (rc, msg)

@@ -71,3 +71,30 @@ def test_pooled_split_path(gdn):
     # by the fix-up and rewritten by the last segment only
     w = W.build([8200, 50], 1, 4, torch.bfloat16, seed=44, gate="long", state_in=None, name="pool_split")
     _check(gdn, w, 6, [4, 1], False, BF16_TOL)
+
+
+def test_decode_pooled(gdn):
+    """One decode step on a pool: rows named by the index are stepped in place,
+    the others stay bitwise unchanged, out-of-range entries start from zero."""
+    w = W.build([1] * 5, 2, 4, torch.bfloat16, seed=45, state_in=None, name="pool_decode")
+    rows, indices = 8, [6, 0, -1, 3, 9]
+    gen = torch.Generator().manual_seed(46)
+    pool = torch.randn(rows, w.Hv, 128, 128, generator=gen) * 0.01
+    s0 = torch.zeros(w.N, w.Hv, 128, 128)
+    valid = [(n, i) for n, i in enumerate(indices) if 0 <= i < rows]
+    for n, i in valid:
+        s0[n] = pool[i]
+    ref_out, ref_fin = oracle.run(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, s0, w.use_qk_l2norm)
+    wd = w.to(DEV)
+    dpool = pool.to(DEV)
+    out = torch.empty(w.N, w.Hv, 128, dtype=w.q.dtype, device=DEV)
+    gdn.gdn_decode_step_pooled(wd.q, wd.k, wd.v, wd.g, wd.beta, 0.0, dpool,
+                               torch.tensor(indices, dtype=torch.int32, device=DEV), True, out)
+    torch.cuda.synchronize()
+    say(f"[gpu] pooled decode: out {nerr(out, ref_out):.3e}")
+    assert nerr(out, ref_out) <= BF16_TOL
+    got = dpool.cpu()
+    for r in set(range(rows)) - {i for _, i in valid}:
+        assert torch.equal(got[r], pool[r])
+    for n, i in valid:
+        assert nerr(got[i], ref_fin[n]) <= BF16_TOL
