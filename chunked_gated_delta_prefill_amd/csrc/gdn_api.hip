@@ -269,6 +269,9 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
         return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens must be contiguous");
     const int64_t N = cu_seqlens->sizes[0] - 1;
     if (N > ((int64_t)1 << 24)) return fail(GDN_ERR_UNSUPPORTED, "too many sequences");
+    // one workgroup per (sequence, value head), rounded up to groups of 8 q/k heads
+    if ((N + 8) * Hv > ((int64_t)1 << 30))
+        return fail(GDN_ERR_UNSUPPORTED, "too many (sequence, value head) pairs for one launch");
 
     // ---- states
     const gdn_tensor *st[2] = {initial_state, output_state};
@@ -501,6 +504,8 @@ int decode_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, c
     if (Hv % Hqk != 0)
         return fail(GDN_ERR_UNSUPPORTED, "Hv must be a multiple of Hqk (each q/k head serves Hv/Hqk value heads)");
     if (N > ((int64_t)1 << 24) || Hv > 65536) return fail(GDN_ERR_UNSUPPORTED, "problem too large");
+    if (N * Hv > ((int64_t)1 << 29))   // two workgroups per (sequence, value head)
+        return fail(GDN_ERR_UNSUPPORTED, "too many (sequence, value head) pairs for one launch");
     const size_t esz = dt_size(io);
     if (N > 0 && (!aligned16(q->data, esz, q->strides, 2) || !aligned16(k->data, esz, k->strides, 2)))
         return fail(GDN_ERR_UNSUPPORTED, "q and k rows must be 16-byte aligned (pointer and sequence/head strides)");

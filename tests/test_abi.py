@@ -280,3 +280,16 @@ def test_decode_pooled_argument_checks():
         rc, msg = lib.call_decode_pooled_raw(a["q"], a["k"], a["v"], a["g"], a["beta"], 0.0, pool,
                                              _t([3], GDN_I32, FAKE + (1 << 34)), 1, a["out"], None)
         assert rc == NO_DEVICE, (rc, msg)
+
+
+def test_launch_size_limits():
+    """(sequence, value head) counts whose grid would not fit one launch are refused."""
+    N, Hv = 1 << 24, 128
+    a = _args(T=N, N=N, Hqk=1, Hv=Hv, g=None, beta=None, s0=None, s1=None,
+              q=_t([N, 1, 128]), k=_t([N, 1, 128]), v=_t([N, Hv, 128]), out=_t([N, Hv, 128], ptr=FAKE + (1 << 40)))
+    rc, msg = _call(a)
+    assert rc == UNSUPPORTED and "launch" in msg, (rc, msg)
+    d = _dargs(N=N, Hqk=1, Hv=Hv, g=None, beta=None, s0=None, s1=None, q=_t([N, 1, 128]), k=_t([N, 1, 128]),
+               v=_t([N, Hv, 128]), out=_t([N, Hv, 128], ptr=FAKE + (1 << 40)))
+    rc, msg = _dcall(d)
+    assert rc == UNSUPPORTED and "launch" in msg, (rc, msg)
