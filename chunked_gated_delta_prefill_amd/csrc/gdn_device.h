@@ -198,9 +198,9 @@ __device__ __forceinline__ float gate_value(uint32_t bits, int dt) {
 // Per-row factor arrays (64 floats each), written once per chunk.  The state
 // is held as S = sigma * S~ (sigma a per-sequence scalar, see the kernel); c
 // is the query scale:
-//   RG  in-chunk log-gate cumsum G_i   GM gamma_i = exp(G_i)   IG 1 / gamma_i
+//   RG  in-chunk log-gate cumsum G_i   GM gamma_i = exp(G_i)   IG 1 / gamma_i, then rk_i / gamma_i
 //   DC  exp(G_L - G_i)                 FB b_i                  (b also scales T' columns)
-//   RK  rk_i, RQ rq_i  (1 without L2 norm; computed with the Gram tiles)
+//   RK  rk_i, RQ rq_i  (1 without L2 norm; computed with the Gram tiles, which also fold rk_i into IG)
 //   FZ  sigma gamma_i rk_i   (rows of K S~^T)     FY  c sigma gamma_i rq_i  (output rows)
 //   FU  rk_i exp(G_L - G_i) / sigma'   (state update; without / sigma' on renorm)
 // followed by gamma_L.
@@ -222,13 +222,15 @@ __device__ __forceinline__ float quad_bcast(float v, int e) {
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
-// Sum of squares of 8 bf16 values (products exact in fp32, fp32 accumulation).
-__device__ __forceinline__ float sumsq8(bf16x8 x) {
+// acc + the sum of squares of 8 bf16 values (products exact in fp32, fp32
+// accumulation), as one chain of four dot2 steps into the running sum.
+__device__ __forceinline__ float sumsq8_acc(bf16x8 x, float acc) {
     const bf16x2 x0 = __builtin_shufflevector(x, x, 0, 1), x1 = __builtin_shufflevector(x, x, 2, 3);
     const bf16x2 x2 = __builtin_shufflevector(x, x, 4, 5), x3 = __builtin_shufflevector(x, x, 6, 7);
-    const float a = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, __builtin_amdgcn_fdot2_f32_bf16(x0, x0, 0.f, false), false);
-    const float b = __builtin_amdgcn_fdot2_f32_bf16(x3, x3, __builtin_amdgcn_fdot2_f32_bf16(x1, x1, 0.f, false), false);
-    return a + b;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(x0, x0, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(x1, x1, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(x3, x3, acc, false);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts of 1, 2, 4, 8 inside

@@ -247,12 +247,19 @@ fused_scan_kernel(const ScanParams p) {
                 else return ld_acc<IO>(M, L::KLD, 32 * blk + l32, 32 * (k / S32), k % S32, h32);
             };
             auto sq = [&](const frag &f) {
-                if constexpr (BF) return sumsq8(f);
+                if constexpr (BF) return sumsq8_acc(f, 0.f);
                 else return f * f;
             };
+            // 1 / |row| (or 1 without the norm); a K row's factor also goes into
+            // its 1 / gamma entry, which only the A tiles read
             auto put_norm = [&](float ss, int which, int blk) {
                 ss += __shfl_xor(ss, 32);
-                if (h32 == 0) rf(which)[32 * blk + l32] = p.l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;
+                if (h32 == 0) {
+                    const int row = 32 * blk + l32;
+                    const float r = p.l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;
+                    rf(which)[row] = r;
+                    if (which == RK_) rf(IG_)[row] *= r;
+                }
             };
             auto pass = [&](auto role) {
                 constexpr int R = decltype(role)::value;
@@ -335,25 +342,24 @@ fused_scan_kernel(const ScanParams p) {
             // Wave w holds tile w (A tiles (0,0) (1,0) (1,1) for w < 3, P tile (0,0) for
             // w = 3) and, when w < 2, P tile (1, w); the map modes need no P.
             const float cP = renorm ? 1.f / sig_next : 1.f;
-            auto mask_row = [&](f32x4 &v, int i, int j0, int keep_diag) {
+            // diagonal tiles only (bi == bj): row - column = l32 - 4 h32 - 8 jj - t
+            const int dlane = l32 - 4 * h32;
+            auto mask_row = [&](f32x4 &v, int jj, int keep_diag) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = i - (j0 + t) + keep_diag > 0 ? v[t] : 0.f;
+                for (int t = 0; t < 4; ++t) v[t] = dlane > 8 * jj + t - keep_diag ? v[t] : 0.f;
             };
             auto a_tile = [&](const f32x16 &acc, int bi, int bj) {
                 const int i = 32 * bi + l32, jb = 32 * bj + 4 * h32;
                 f32x4 v[4];
-                if (fast) {   // (b_i rk_i gamma_i) (rk_j / gamma_j) (k_i . k_j)
+                if (fast) {   // (b_i rk_i gamma_i) (rk_j / gamma_j) (k_i . k_j); IG_ holds rk_j / gamma_j
                     const float ea = rf(FB_)[i] * rf(RK_)[i] * rf(GM_)[i];
-                    f32x4 rk[4], ig[4];
+                    f32x4 ig[4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        rk[jj] = ld4(rf(RK_) + jb + 8 * jj);
-                        ig[jj] = ld4(rf(IG_) + jb + 8 * jj);
-                    }
+                    for (int jj = 0; jj < 4; ++jj) ig[jj] = ld4(rf(IG_) + jb + 8 * jj);
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[jj][t] = ea * (rk[jj][t] * ig[jj][t]) * acc[4 * jj + t];
+                        for (int t = 0; t < 4; ++t) v[jj][t] = ea * ig[jj][t] * acc[4 * jj + t];
                 } else {
                     const float fi = rf(FB_)[i] * rf(RK_)[i], Gi = rf(RG_)[i];
                     f32x4 rk[4], G4[4];
@@ -370,7 +376,7 @@ fused_scan_kernel(const ScanParams p) {
                 }
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    mask_row(v[jj], i, jb + 8 * jj, 0);
+                    if (bi == bj) mask_row(v[jj], jj, 0);
                     *reinterpret_cast<f32x4 *>(Af + i * L::FLD + jb + 8 * jj) = v[jj];
                 }
                 if (bi == bj) {   // this lane's row lies in diagonal block 2 bi + (l32 >= 16)
@@ -408,7 +414,7 @@ fused_scan_kernel(const ScanParams p) {
                 }
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    mask_row(v[jj], i, jb + 8 * jj, 1);
+                    if (bi == bj) mask_row(v[jj], jj, 1);
                     if constexpr (BF) {
                         const bf16x4 b4 = {(bf16)v[jj][0], (bf16)v[jj][1], (bf16)v[jj][2], (bf16)v[jj][3]};
                         *reinterpret_cast<bf16x4 *>(Ps + i * L::OLD + jb + 8 * jj) = b4;
