@@ -248,6 +248,22 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return x;
 }
 
+// bf16 K and Q tiles in LDS: rows of 128 values padded to kKqLd, row r stored at
+// row kq_row(r), which permutes each aligned group of 8 rows as 0 2 4 6 1 3 5 7.
+// With the 4-dword pad, 8 consecutive rows at one column (16-byte operand reads)
+// start in 8 different bank quads, and 4 consecutive rows at 32-byte spans
+// (transposing 8-byte reads) fall two quads apart, so both patterns, like the
+// 16-byte staging writes along a row, touch 32 distinct banks per group of lanes
+// the LDS serves together.  The permutation is a per-lane constant for every
+// access, so it costs no address arithmetic beyond the base.
+constexpr int kKqLd = 136;
+__device__ __forceinline__ int kq_row(int r) { return (r & ~7) | (2 * (r & 3) + ((r >> 2) & 1)); }
+__device__ __forceinline__ int kq_off(int row, int col) { return kq_row(row) * kKqLd + col; }
+// 32x32 operand, natural order (see ld_nat) from a K or Q tile
+__device__ __forceinline__ bf16x8 ld_kq(const bf16 *M, int row, int s, int h) {
+    return *reinterpret_cast<const bf16x8 *>(M + kq_off(row, 16 * s + 8 * h));
+}
+
 // 32x32 bf16 A operand of a product contracting over tokens, rows = K columns
 // [m0, m0 + 32), read straight from row-major K with the transposing LDS load
 // (within 16 lanes, output lane i element e comes from source lane i/4 + 4e,
@@ -258,14 +274,16 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // accumulator register r of half h is column m0 + 16 (r/8) + 8h + r%8: the
 // state's natural operand order.  With PERM = false operand row m is column
 // m0 + m (a plain operand of a column-major read).
+//
+// Ks is a K tile in the row order of kq_row.
 template <bool PERM = true>
-__device__ __forceinline__ bf16x8 ld_acc_tr(const bf16 *Ks, int ld, int m0, int cb, int s, int lane) {
+__device__ __forceinline__ bf16x8 ld_acc_tr(const bf16 *Ks, int m0, int cb, int s, int lane) {
     const int i = lane & 15, h = lane >> 5, g16 = (lane >> 4) & 1;
     const int q = i & 3, qs = PERM ? ((q & 1) << 1) | (q >> 1) : q;
-    const bf16 *p = Ks + (cb + 16 * s + 4 * h + (i >> 2)) * ld + m0 + 16 * g16 + 4 * qs;
+    const bf16 *p = Ks + kq_off(cb + 16 * s + 4 * h + (i >> 2), m0 + 16 * g16 + 4 * qs);
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * ld));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * kKqLd));   // kq_row(r + 8) = kq_row(r) + 8
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 

@@ -52,7 +52,7 @@ using namespace dev;
 
 template <typename IO> struct Smem {
     static constexpr bool BF = is_bf<IO>::value;
-    static constexpr int KLD = BF ? 136 : 132;   // K, Q rows (elements of IO)
+    static constexpr int KLD = BF ? kKqLd : 132;   // K, Q rows (elements of IO; bf16 rows permuted, see kq_row)
     static constexpr int OLD = 68;               // T', P rows (elements of IO)
     static constexpr int FLD = 68;               // fp32 64x64 work matrix (A, inverse blocks)
     static constexpr int KB = C * KLD * (int)sizeof(IO);
@@ -184,7 +184,7 @@ fused_scan_kernel(const ScanParams p) {
             for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    *reinterpret_cast<i32x4 *>((mat ? Qs : Ks) + (4 * rq4 + t) * L::KLD + 8 * cg) = pf.kq[mat][t];
+                    *reinterpret_cast<i32x4 *>((mat ? Qs : Ks) + kq_off(4 * rq4 + t, 8 * cg)) = pf.kq[mat][t];
         } else {
             const int r0 = tid >> 5, cg = tid & 31;
 #pragma unroll
@@ -243,7 +243,7 @@ fused_scan_kernel(const ScanParams p) {
         {
             constexpr int NK = 4 * S32;
             auto frag_at = [&](const IO *M, int blk, int k) -> frag {
-                if constexpr (BF) return ld_nat<IO>(M, L::KLD, 32 * blk + l32, k, h32);
+                if constexpr (BF) return ld_kq(M, 32 * blk + l32, k, h32);
                 else return ld_acc<IO>(M, L::KLD, 32 * blk + l32, 32 * (k / S32), k % S32, h32);
             };
             auto sq = [&](const frag &f) {
@@ -708,7 +708,7 @@ fused_scan_kernel(const ScanParams p) {
                 const int ib = k / S32, st = k % S32;
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
-                    if constexpr (BF) f[bb] = ld_acc_tr(Ks, L::KLD, 32 * bb, 32 * ib, st, lane);
+                    if constexpr (BF) f[bb] = ld_acc_tr(Ks, 32 * bb, 32 * ib, st, lane);
                     else f[bb] = ld_acc_t<float>(Ks, L::KLD, 32 * bb + l32, 32 * ib, st, h32);
                 }
             };
