@@ -203,8 +203,13 @@ __device__ __forceinline__ float gate_value(uint32_t bits, int dt) {
 //   RK  rk_i, RQ rq_i  (1 without L2 norm; computed with the Gram tiles, which also fold rk_i into IG)
 //   FZ  sigma gamma_i rk_i   (rows of K S~^T)     FY  c sigma gamma_i rq_i  (output rows)
 //   FU  rk_i exp(G_L - G_i) / sigma'   (state update; without / sigma' on renorm)
-// followed by gamma_L.
+// The gate rows RG .. FB come in two sets, for chunks of even and odd index:
+// one wave writes the next chunk's set while the current one is in use.  Row
+// `which` of set 1 sits at NROWF + which; after all rows, gamma_L of each set.
 enum { RG_ = 0, GM_ = 1, IG_ = 2, DC_ = 3, FB_ = 4, RK_ = 5, RQ_ = 6, FZ_ = 7, FY_ = 8, FU_ = 9, NROWF = 10 };
+constexpr int kGateRows = 5;                  // RG_ .. FB_
+constexpr int kRowsTotal = NROWF + kGateRows;
+constexpr int kGateWave = 2;                  // the wave that loads and converts the gates
 constexpr float kFastDecay = -60.f;   // G_L above this: exp(G_i - G_j) = gamma_i / gamma_j is safe
 constexpr float kRenorm = 0x1p-40f;   // sigma below this is folded back into the state
 
@@ -360,7 +365,6 @@ __device__ __forceinline__ void issue_loads(Prefetch<IO> &pf, const ScanParams &
             pf.kq[1][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vq + 8 * j * p.q_st, 0, 0));
         }
     }
-    if (ws == 0) issue_gates(pf, p, ch, h, lane);
 }
 
 template <typename IO>

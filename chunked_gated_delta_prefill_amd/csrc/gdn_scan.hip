@@ -50,6 +50,8 @@ namespace {
 
 using namespace dev;
 
+static_assert(kGateWave == 2, "the gate rows ride on the third wave's Gram pass");
+
 template <typename IO> struct Smem {
     static constexpr bool BF = is_bf<IO>::value;
     static constexpr int KLD = BF ? kKqLd : 132;   // K, Q rows (elements of IO; bf16 rows permuted, see kq_row)
@@ -66,7 +68,7 @@ template <typename IO> struct Smem {
     static constexpr int NTS = 16 * 16 + 4;
     static constexpr int NT_OFF = AF_OFF + C * FLD * 4;
     static constexpr int ROW_OFF = NT_OFF + 4 * NTS * 4;
-    static constexpr int BYTES = ROW_OFF + (NROWF * C + 4) * 4;
+    static constexpr int BYTES = ROW_OFF + (kRowsTotal * C + 4) * 4;
     static_assert(!BF || BYTES <= 80 * 1024, "two workgroups per CU");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(Q_OFF % 16 == 0 && AF_OFF % 16 == 0 && T_OFF % 16 == 0 &&
@@ -97,7 +99,9 @@ fused_scan_kernel(const ScanParams p) {
     float *Af = reinterpret_cast<float *>(smem + L::AF_OFF);
     float *RF = reinterpret_cast<float *>(smem + L::ROW_OFF);     // per-row factors
     float *NT = reinterpret_cast<float *>(smem + L::NT_OFF);      // transposed diagonal blocks of A
-    auto rf = [&](int which) { return RF + which * C; };
+    // factor row `which`, gate rows of set `set`; gamma_L of a set
+    auto rf_set = [&](int which, int set) { return RF + (which < kGateRows ? which + set * NROWF : which) * C; };
+    auto gamma_l = [&](int set) -> float & { return RF[kRowsTotal * C + set]; };
 
     // ---- work item: XCD-aware so the r value heads of one q/k head meet in one L2
     const int r = p.r;
@@ -155,14 +159,42 @@ fused_scan_kernel(const ScanParams p) {
     // chunks of the sequence before this work item (segments start on chunk bounds)
     const int seq_chunk0 = (CK && p.segs) ? (int)((bos - load_cu(p.cu, n, p.cu_i64)) / C) : 0;
     float sigma = 1.f;          // true state = sigma * S (uniform across the workgroup)
-    Prefetch<IO> pf;
-    if (nchunks > 0) issue_loads<IO>(pf, p, chunk_at(bos, eos, 0), hq, h, threadIdx.x, threadIdx.x & 63, threadIdx.x >> 6);
-    // Wait for the first chunk's loads here, once.  In the loop the prefetch of
-    // chunk c + 1 is retired by the wait for chunk c's V, so the chunk head
-    // needs no vector-memory wait; without this the loop entry would make the
-    // head wait for everything outstanding, the previous chunk's output stores
-    // included.
+    // Gate rows of one chunk into set `set`, on the gate wave (lane i = token i of
+    // the chunk): the in-chunk log-gate cumsum G, gamma = exp(G), 1 / gamma,
+    // exp(G_L - G), b (zero past the chunk end) and gamma_L.
+    auto gate_rows = [&](const Prefetch<IO> &g, int Lch, int set, int lane) {
+        const bool valid = lane < Lch;
+        const float ga = p.g ? gate_value(g.g, p.g_dt) : 1.f;
+        const float gb = p.beta ? gate_value(g.b, p.b_dt) : 1.f;
+        const float G = wave_prefix_sum(valid ? fmaxf(__logf(ga), -80.f) : 0.f);
+        const float GL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
+        const float gam = __expf(G);
+        rf_set(RG_, set)[lane] = G;
+        rf_set(GM_, set)[lane] = gam;
+        rf_set(IG_, set)[lane] = __expf(-G);
+        rf_set(DC_, set)[lane] = __expf(GL - G);
+        rf_set(FB_, set)[lane] = valid ? gb : 0.f;
+        gamma_l(set) = __expf(GL);   // the same value from every lane
+    };
+    // The gates run two chunks ahead of K and Q: chunk c + 1's gate rows are
+    // written during chunk c (phase [A], gate wave), from values loaded during
+    // chunk c - 1.
+    Prefetch<IO> pf, pf_g0;   // pf_g0: chunk 0's gates (gate wave)
+    const int ws0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (nchunks > 0) {
+        issue_loads<IO>(pf, p, chunk_at(bos, eos, 0), hq, h, threadIdx.x, threadIdx.x & 63, ws0);
+        if (ws0 == kGateWave) {
+            issue_gates(pf_g0, p, chunk_at(bos, eos, 0), h, threadIdx.x & 63);
+            issue_gates(pf, p, chunk_at(bos, eos, 1), h, threadIdx.x & 63);
+        }
+    }
+    // Wait for the first chunk's loads (and chunk 1's gates) here, once.  In the
+    // loop the prefetches are retired by the wait for chunk c's V, so the chunk
+    // head needs no vector-memory wait; without this the loop entry would make
+    // the head wait for everything outstanding, the previous chunk's output
+    // stores included.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (nchunks > 0 && ws0 == kGateWave) gate_rows(pf_g0, chunk_at(bos, eos, 0).L, 0, threadIdx.x & 63);
 
     for (int c = 0; c < nchunks; ++c) {
         const ChunkRef ch = chunk_at(bos, eos, c);
@@ -176,8 +208,10 @@ fused_scan_kernel(const ScanParams p) {
         const int ws = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int h32 = lane >> 5, l32 = lane & 31;
         const int v0 = ws * 32 + l32;
+        const int gset = c & 1;
+        auto rf = [&](int which) { return rf_set(which, gset); };
 
-        // ---- [L] stage K and Q; gates and the in-chunk log-gate cumsum
+        // ---- [L] stage K and Q (this chunk's gate rows are already in set gset)
         if constexpr (BF) {
             const int rq4 = tid >> 4, cg = tid & 15;
 #pragma unroll
@@ -193,21 +227,6 @@ fused_scan_kernel(const ScanParams p) {
                 for (int j = 0; j < 8; ++j)
                     *reinterpret_cast<f32x4 *>((mat ? Qs : Ks) + (r0 + 8 * j) * L::KLD + 4 * cg) = pf.kq[mat][j];
         }
-        // wave 0, lane i = token i of the chunk
-        if (ws == 0) {
-            const bool valid = lane < Lc;
-            const float ga = p.g ? gate_value(pf.g, p.g_dt) : 1.f;
-            const float gb = p.beta ? gate_value(pf.b, p.b_dt) : 1.f;
-            const float G = wave_prefix_sum(valid ? fmaxf(__logf(ga), -80.f) : 0.f);
-            const float GL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
-            const float gam = __expf(G);
-            rf(RG_)[lane] = G;
-            rf(GM_)[lane] = gam;
-            rf(IG_)[lane] = __expf(-G);
-            rf(DC_)[lane] = __expf(GL - G);
-            rf(FB_)[lane] = valid ? gb : 0.f;
-            if (lane == 63) RF[NROWF * C] = gam;    // gamma_L
-        }
         __syncthreads();
 
         // ---- [A] Gram tiles; row norms from their operands
@@ -216,7 +235,7 @@ fused_scan_kernel(const ScanParams p) {
         // so the decay costs no per-element work; when sigma' gets small it is
         // folded back into S~ (renorm) to keep U / sigma' in range.
         const float gLc =
-            __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, RF[NROWF * C])));
+            __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gamma_l(gset))));
         const float sig_next = sigma * gLc;
         const bool renorm = !(sig_next >= kRenorm);
         const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
@@ -231,7 +250,8 @@ fused_scan_kernel(const ScanParams p) {
         //   this wave's Gram tiles (first operand = K rows of the column block):
         //     wave 0: A(0,0) = K_0 K_0, P(1,0) = K_0 Q_1      norms of K_0, Q_1
         //     wave 1: A(1,0) = K_0 K_1, P(1,1) = K_1 Q_1      norms of K_1
-        //     wave 2: A(1,1) = K_1 K_1 (two accumulators: even / odd steps)
+        //     wave 2: A(1,1) = K_1 K_1 (two accumulators: even / odd steps); then the
+        //             next chunk's gate rows (kGateWave)
         //     wave 3: P(0,0) = K_0 Q_0 (two accumulators)      norms of Q_0
         //   the squared row norms (dot2 on the fragments).
         // The contraction runs in the state's register order (natural for bf16,
@@ -316,12 +336,15 @@ fused_scan_kernel(const ScanParams p) {
             };
             if (ws == 0) pass(std::integral_constant<int, 0>{});
             else if (ws == 1) pass(std::integral_constant<int, 1>{});
-            else if (ws == 2) pass(std::integral_constant<int, 2>{});
+            else if (ws == kGateWave) {   // also the next chunk's gate rows (the other set)
+                pass(std::integral_constant<int, 2>{});
+                gate_rows(pf, next.L, gset ^ 1, lane);
+            }
             else pass(std::integral_constant<int, 3>{});
         }
         __syncthreads();
 
-        // ---- [B] next chunk's K, Q, gates in flight; A (fp32) and P into LDS.  bf16:
+        // ---- [B] next chunk's K, Q and the gates of chunk c + 2 in flight; A (fp32) and P into LDS.  bf16:
         // half of the K, Q loads go out here, the rest after the tiles are formed, so
         // that a wave does not stall on a long run of load issues
         if constexpr (BF) {
@@ -329,6 +352,7 @@ fused_scan_kernel(const ScanParams p) {
             issue_kq_part(pf, p, next, hq, tid, 1);
         } else {
             issue_loads<IO>(pf, p, next, hq, h, tid, lane, ws);
+            if (ws == kGateWave) issue_gates(pf, p, chunk_at(bos, eos, c + 2), h, lane);
         }
         {
             // Lane row i = 32 bi + l32; register 4 jj + t is column j = 32 bj + 8 jj + 4 h32 + t.
@@ -431,7 +455,7 @@ fused_scan_kernel(const ScanParams p) {
             if constexpr (BF) {
                 issue_kq_part(pf, p, next, hq, tid, 2);
                 issue_kq_part(pf, p, next, hq, tid, 3);
-                if (ws == 0) issue_gates(pf, p, next, h, lane);
+                if (ws == kGateWave) issue_gates(pf, p, chunk_at(bos, eos, c + 2), h, lane);
             }
             if (ws == 2) {   // row factors of [D], lane = token
                 const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
