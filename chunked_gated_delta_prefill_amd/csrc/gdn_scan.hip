@@ -248,11 +248,11 @@ fused_scan_kernel(const ScanParams p) {
         //   X = K S~^T and (S~ Q^T) for this wave's 32 state rows (S~ as the A operand
         //   gives the transpose), four accumulator chains;
         //   this wave's Gram tiles (first operand = K rows of the column block):
-        //     wave 0: A(0,0) = K_0 K_0, P(1,0) = K_0 Q_1      norms of K_0, Q_1
+        //     wave 0: A(0,0) = K_0 K_0 (two accumulators: even / odd steps)   norms of K_0, Q_1
         //     wave 1: A(1,0) = K_0 K_1, P(1,1) = K_1 Q_1      norms of K_1
-        //     wave 2: A(1,1) = K_1 K_1 (two accumulators: even / odd steps); then the
-        //             next chunk's gate rows (kGateWave)
-        //     wave 3: P(0,0) = K_0 Q_0 (two accumulators)      norms of Q_0
+        //     wave 2: A(1,1) = K_1 K_1 (two accumulators); then the next chunk's
+        //             gate rows (kGateWave)
+        //     wave 3: P(0,0) = K_0 Q_0, P(1,0) = K_0 Q_1      norms of Q_0
         //   the squared row norms (dot2 on the fragments).
         // The contraction runs in the state's register order (natural for bf16,
         // accumulator order for fp32); the next step's fragments are read while
@@ -307,12 +307,9 @@ fused_scan_kernel(const ScanParams p) {
                         Y[1] = M::run(sf, fq[cur][1], Y[1]);
                     }
                     if constexpr (R == 0) {
-                        gt[0] = M::run(k0, k0, gt[0]);
+                        gt[cur] = M::run(k0, k0, gt[cur]);
                         ssa += sq(k0);
-                        if constexpr (OUT) {
-                            gt[1] = M::run(k0, fq[cur][1], gt[1]);
-                            ssb += sq(fq[cur][1]);
-                        }
+                        if constexpr (OUT) ssb += sq(fq[cur][1]);
                     } else if constexpr (R == 1) {
                         gt[0] = M::run(k0, k1, gt[0]);
                         ssa += sq(k1);
@@ -320,18 +317,21 @@ fused_scan_kernel(const ScanParams p) {
                     } else if constexpr (R == 2) {
                         gt[cur] = M::run(k1, k1, gt[cur]);
                     } else if constexpr (OUT) {
-                        gt[cur] = M::run(k0, fq[cur][0], gt[cur]);
+                        gt[0] = M::run(k0, fq[cur][0], gt[0]);
+                        gt[1] = M::run(k0, fq[cur][1], gt[1]);
                         ssb += sq(fq[cur][0]);
                     }
                 }
                 if constexpr (R == 0) {
+                    gt[0] += gt[1];
                     put_norm(ssa, RK_, 0);
                     if constexpr (OUT) put_norm(ssb, RQ_, 1);
                 } else if constexpr (R == 1) {
                     put_norm(ssa, RK_, 1);
-                } else {
+                } else if constexpr (R == 2) {
                     gt[0] += gt[1];
-                    if constexpr (R == 3 && OUT) put_norm(ssb, RQ_, 0);
+                } else if constexpr (OUT) {
+                    put_norm(ssb, RQ_, 0);
                 }
             };
             if (ws == 0) pass(std::integral_constant<int, 0>{});
@@ -363,8 +363,8 @@ fused_scan_kernel(const ScanParams p) {
             //       operand, see [D])
             // Four consecutive columns are stored at once; every factor read is
             // issued before the first store.
-            // Wave w holds tile w (A tiles (0,0) (1,0) (1,1) for w < 3, P tile (0,0) for
-            // w = 3) and, when w < 2, P tile (1, w); the map modes need no P.
+            // Wave w < 3 holds A tile (0,0), (1,0), (1,1); wave 1 also P tile (1,1) and
+            // wave 3 P tiles (0,0) and (1,0); the map modes need no P.
             const float cP = renorm ? 1.f / sig_next : 1.f;
             // diagonal tiles only (bi == bj): row - column = l32 - 4 h32 - 8 jj - t
             const int dlane = l32 - 4 * h32;
@@ -449,15 +449,18 @@ fused_scan_kernel(const ScanParams p) {
             };
             if (ws < 3) a_tile(gt[0], ws > 0, ws == 2);
             if constexpr (OUT) {
-                if (ws == 3) p_tile(gt[0], 0, 0);
-                if (ws < 2) p_tile(gt[1], 1, ws);
+                if (ws == 3) {
+                    p_tile(gt[0], 0, 0);
+                    p_tile(gt[1], 1, 0);
+                }
+                if (ws == 1) p_tile(gt[1], 1, 1);
             }
             if constexpr (BF) {
                 issue_kq_part(pf, p, next, hq, tid, 2);
                 issue_kq_part(pf, p, next, hq, tid, 3);
                 if (ws == kGateWave) issue_gates(pf, p, chunk_at(bos, eos, c + 2), h, lane);
             }
-            if (ws == 2) {   // row factors of [D], lane = token
+            if (ws == 0) {   // row factors of [D], lane = token
                 const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
                 rf(FZ_)[lane] = sigma * gam * rk;
                 rf(FU_)[lane] = renorm ? rk * dec : rk * dec / sig_next;
