@@ -135,6 +135,26 @@ def test_strong_decay_slow_path(gdn):
     assert nerr(out, ro) <= BF16_TOL and nerr(fin, rf) <= BF16_TOL
 
 
+@pytest.mark.parametrize("lengths,bi", [((7 * 64 + 13, 130, 64), True), ((8200, 300), False)])
+def test_decay_regime_alternating_by_chunk(gdn, lengths, bi):
+    """Chunks alternate between mild gates and gates strong enough for the
+    entry-wise exp path (total log-decay below -60), so consecutive chunks of one
+    sequence take different paths and renormalise the lazy decay at different
+    points; the second case is long enough to take the split path."""
+    w = _w(lengths=lengths, seed=33)
+    t = torch.arange(w.T)
+    starts = w.cu_seqlens.to(torch.int64)
+    seq = torch.searchsorted(starts[1:], t, right=True)
+    chunk = (t - starts[seq]) // 64
+    strong = (chunk % 2 == 1).unsqueeze(1)
+    g = torch.where(strong, torch.full_like(w.g, 0.2), w.g)
+    w = W.Workload(**{**w.__dict__, "g": g})
+    say(f"[gpu] alternating decay regimes {lengths} batch_invariant={bi}")
+    out, fin = run_gpu(gdn, w, bi)
+    ro, rf = run_oracle(w)
+    assert nerr(out, ro) <= BF16_TOL and nerr(fin, rf) <= BF16_TOL
+
+
 def test_bf16_gates_and_fp16_gate(gdn):
     w = _w(seed=29)
     say("[gpu] gate dtypes")
