@@ -431,7 +431,9 @@ def main():
     kern_ms = statistics.mean(launch_ms)
     value = w.T / (ms_step / 1e3)
     achieved = byts / (kern_ms / 1e3) / 1e9
-    traffic = None if (ck_every or args.pooled) else read_traffic()
+    # the counters were taken on the unsplit 32 x 8192 batch: no other workload carries them
+    profiled = args.workload == "large_batch" and args.variant is None and not (ck_every or args.pooled)
+    traffic = read_traffic() if profiled else None
     res = {
         "metric": "GDN prefill tokens/s and TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

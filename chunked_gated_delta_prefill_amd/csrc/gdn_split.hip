@@ -73,60 +73,121 @@ __global__ __launch_bounds__(256) void plan_kernel(const void *cu, int cu_i64, i
 //   (S M)^T[k][v] = sum_v' M[v'][k] S^T[v'][v]
 // the accumulator is the B operand (contraction v' in accumulator order) and
 // M, staged V-major in LDS, is read column-wise as the A operand.
+//
+// Rows of the state evolve independently (row v of S M needs row v of S only),
+// so one workgroup takes one block of 32 state rows of a (sequence, head) and
+// its wave w forms columns 32w .. 32w+31 of those rows: 64 MFMAs per step
+// instead of 256.  After each step the four column blocks meet in LDS (Sx, in
+// register order) to form the next step's B operand.  The next M and N are
+// loaded into registers while the current products run.  The four row blocks
+// of a head get workgroup ids 8 apart (one XCD), so M is fetched into one L2.
+constexpr int kFixRowBlocks = D / 32;
+
+__device__ __forceinline__ void load_block(f32x16 &S, const float *base, int bb, int v0, int h32) {
+    const auto r = rsrc(base, (int64_t)D * D * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {   // registers 4j .. 4j+3 hold 4 consecutive k
+        const f32x4 x = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (v0 * D + state_k<false>(bb, 4 * j, h32)) * 4, 0, 0));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[4 * j + t] = x[t];
+    }
+}
+__device__ __forceinline__ void store_block(const f32x16 &S, float *base, int bb, int v0, int h32) {
+    const auto r = rsrc(base, (int64_t)D * D * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 x = {S[4 * j], S[4 * j + 1], S[4 * j + 2], S[4 * j + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r,
+                                               (v0 * D + state_k<false>(bb, 4 * j, h32)) * 4, 0, 0);
+    }
+}
+
+struct MPieces {
+    f32x4 x[16];
+};
+__device__ __forceinline__ void load_m(MPieces &m, const float *Mg, int tid) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int u = tid + 256 * e;
+        m.x[e] = *reinterpret_cast<const f32x4 *>(Mg + (u >> 5) * D + 4 * (u & 31));
+    }
+}
+__device__ __forceinline__ void put_m(float *Ms, int ld, const MPieces &m, int tid) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int u = tid + 256 * e;
+        *reinterpret_cast<f32x4 *>(Ms + (u >> 5) * ld + 4 * (u & 31)) = m.x[e];
+    }
+}
+
 __global__ __launch_bounds__(256) void fixup_kernel(const FixParams f) {
     constexpr int MLD = 132;
     __shared__ __attribute__((aligned(16))) float Ms[D * MLD];
-    const int n = blockIdx.x / f.Hv, h = blockIdx.x % f.Hv;
+    __shared__ __attribute__((aligned(16))) f32x4 Sx[4][4][64];   // [column block][register quad][lane]
+    const int b = blockIdx.x;
+    const int rb = (b >> 3) % kFixRowBlocks, pair = 8 * (b / (8 * kFixRowBlocks)) + (b & 7);
+    if (pair >= f.N * f.Hv) return;
+    const int n = pair / f.Hv, h = pair % f.Hv;
     const int s0 = f.seg_first[n], cnt = f.seg_first[n + 1] - s0;
     if (cnt <= 1) return;
-    const int tid = threadIdx.x, lane = tid & 63, ws = tid >> 6;
-    const int h32 = lane >> 5, l32 = lane & 31, v0 = ws * 32 + l32;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ws = __builtin_amdgcn_readfirstlane(tid >> 6);   // the column block this wave forms
+    const int h32 = lane >> 5, l32 = lane & 31, v0 = 32 * rb + l32;
     f32x16 S[4];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) S[bb] = zero16();
     const int64_t srow = state_row(f.sidx, f.sidx_i64, f.pool_rows, n);
     if (f.s_in && srow >= 0) load_state<false>(S, f.s_in + srow * f.si_n + h * f.si_h, f.si_v, f.si_dt, v0, h32);
-    if (f.sidx)   // the first segment of a pooled sequence starts from this copy
-        store_state<false>(S, reinterpret_cast<char *>(f.ws_sin) + ((int64_t)s0 * f.Hv + h) * kMapBytes, D * 4,
-                           GDN_F32, v0, h32);
+    auto map_at = [&](const float *base, int i) {
+        return reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) +
+                                               ((int64_t)(s0 + i) * f.Hv + h) * kMapBytes);
+    };
+    auto sin_at = [&](int i) {
+        return reinterpret_cast<float *>(reinterpret_cast<char *>(f.ws_sin) + ((int64_t)(s0 + i) * f.Hv + h) * kMapBytes);
+    };
+    // a pooled sequence's first segment starts from this copy (each wave its column block)
+    if (f.sidx) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)   // constant indices keep S in registers
+            if (bb == ws) store_block(S[bb], sin_at(0), bb, v0, h32);
+    }
+    // M_i in 16 16-byte pieces per thread: row u / 32, columns 4 (u % 32) .. +3
+    // (u = tid + 256 e), held in registers from its load to its LDS store
+    MPieces mreg;
+    f32x16 Nn;
+    load_m(mreg, map_at(f.ws_m, 0), tid);
+    load_block(Nn, map_at(f.ws_n, 0), ws, v0, h32);
+    put_m(Ms, MLD, mreg, tid);
+    __syncthreads();
     for (int i = 0; i + 1 < cnt; ++i) {
-        const int64_t off = ((int64_t)(s0 + i) * f.Hv + h) * kMapBytes;
-        const float *Mg = reinterpret_cast<const float *>(reinterpret_cast<const char *>(f.ws_m) + off);
-        // N_i (the product's accumulator) and M_i are fetched together, M in two
-        // batches of eight 16-byte loads per thread, so a step waits for memory
-        // about twice instead of once per load (232 -> 172 us for 15 steps of
-        // 32 heads); the products themselves, 256 fp32 32x32x2 MFMAs per wave,
-        // take about 7 us per step
-        f32x16 Sn[4];
-        load_state<false>(Sn, reinterpret_cast<const char *>(f.ws_n) + off, D * 4, GDN_F32, v0, h32);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            f32x4 t[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int u = tid + 256 * (8 * half + e), row = u >> 5, c4 = u & 31;
-                t[e] = *reinterpret_cast<const f32x4 *>(Mg + row * D + 4 * c4);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int u = tid + 256 * (8 * half + e), row = u >> 5, c4 = u & 31;
-                *reinterpret_cast<f32x4 *>(Ms + row * MLD + 4 * c4) = t[e];
-            }
+        f32x16 Sn = Nn;
+        const bool more = i + 2 < cnt;
+        if (more) {   // the next step's M and N in flight during this step's products
+            load_m(mreg, map_at(f.ws_m, i + 1), tid);
+            load_block(Nn, map_at(f.ws_n, i + 1), ws, v0, h32);
         }
-        __syncthreads();
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
+            for (int st = 0; st < 16; ++st)
+                Sn = __builtin_amdgcn_mfma_f32_32x32x2f32(Ms[(32 * cb + acc_row(st, h32)) * MLD + 32 * ws + l32],
+                                                          S[cb][st], Sn, 0, 0, 0);
+        store_block(Sn, sin_at(i + 1), ws, v0, h32);
+        if (!more) break;   // the last segment's entry state was the last one needed
 #pragma unroll
-                for (int st = 0; st < 16; ++st)
-                    Sn[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ms[(32 * cb + acc_row(st, h32)) * MLD + 32 * mb + l32],
-                                                                  S[cb][st], Sn[mb], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) Sx[ws][j][lane] = f32x4{Sn[4 * j], Sn[4 * j + 1], Sn[4 * j + 2], Sn[4 * j + 3]};
+        __syncthreads();   // every wave's products are done: Ms may be rewritten, Sx read
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) S[bb] = Sn[bb];
-        store_state<false>(S, reinterpret_cast<char *>(f.ws_sin) + ((int64_t)(s0 + i + 1) * f.Hv + h) * kMapBytes, D * 4,
-                    GDN_F32, v0, h32);
-        __syncthreads();
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 x = Sx[bb][j][lane];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[bb][4 * j + t] = x[t];
+            }
+        put_m(Ms, MLD, mreg, tid);
+        __syncthreads();   // M_{i+1} staged, and Sx read by every wave before it is rewritten
     }
 }
 
@@ -139,7 +200,8 @@ hipError_t launch_plan(const void *cu, int cu_i64, int N, int64_t lseg, SegEntry
 }
 
 hipError_t launch_fixup(const FixParams &f, hipStream_t stream) {
-    const int64_t blocks = (int64_t)f.N * f.Hv;
+    const int64_t pairs = (int64_t)f.N * f.Hv;
+    const int64_t blocks = ((pairs + 7) / 8) * 8 * kFixRowBlocks;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(fixup_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, f);
     return hipGetLastError();
