@@ -104,17 +104,6 @@ __device__ __forceinline__ typename Mma<OT>::frag ld_acc_t(const ST *M, int ld, 
     }
 }
 
-// 32x32 operand, natural order: step s covers [2E*s, 2E*s + 2E), half h holds
-// E consecutive indices.  Row-major LDS in the operand type.
-template <typename OT>
-__device__ __forceinline__ typename Mma<OT>::frag ld_nat(const OT *M, int ld, int row, int s, int h) {
-    if constexpr (is_bf<OT>::value) {
-        return *reinterpret_cast<const bf16x8 *>(M + row * ld + 16 * s + 8 * h);
-    } else {
-        return M[row * ld + 2 * s + h];
-    }
-}
-
 // Accumulator registers of step s as a 32x32 operand (accumulator order).
 template <typename OT>
 __device__ __forceinline__ typename Mma<OT>::frag acc_frag(const f32x16 &a, int s) {
@@ -264,7 +253,8 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 constexpr int kKqLd = 136;
 __device__ __forceinline__ int kq_row(int r) { return (r & ~7) | (2 * (r & 3) + ((r >> 2) & 1)); }
 __device__ __forceinline__ int kq_off(int row, int col) { return kq_row(row) * kKqLd + col; }
-// 32x32 operand, natural order (see ld_nat) from a K or Q tile
+// 32x32 operand in natural order from a K or Q tile: step s covers columns
+// [16 s, 16 s + 16), half h holds the 8 consecutive columns 16 s + 8 h ..
 __device__ __forceinline__ bf16x8 ld_kq(const bf16 *M, int row, int s, int h) {
     return *reinterpret_cast<const bf16x8 *>(M + kq_off(row, 16 * s + 8 * h));
 }
