@@ -278,7 +278,8 @@ __device__ __forceinline__ bf16x8 ld_acc_tr(const bf16 *Ks, int m0, int cb, int 
     const bf16 *p = Ks + kq_off(cb + 16 * s + 4 * h + (i >> 2), m0 + 16 * g16 + 4 * qs);
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * kKqLd));   // kq_row(r + 8) = kq_row(r) + 8
+    // 8 rows further down: kq_row(r + 8) = kq_row(r) + 8
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * kKqLd));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 

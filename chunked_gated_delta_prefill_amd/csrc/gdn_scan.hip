@@ -25,9 +25,10 @@
 //   * Accumulators are reused directly as B operands (S0^T, Z, Vnew): the
 //     contraction index of those products is permuted to the accumulator's
 //     row order and the LDS-side operand is read with the same permutation.
-//   * Per chunk: [L] stage K and Q in LDS, gate prefix sums and decay rows;
-//     [A] one pass over the 128-wide contraction gives K S~^T and S~ Q^T for
-//     the wave's own state rows plus its Gram tiles and row norms; [B] A (fp32)
+//   * Per chunk: [L] stage K and Q in LDS; [A] one pass over the 128-wide
+//     contraction gives K S~^T and S~ Q^T for the wave's own state rows plus
+//     its Gram tiles and row norms, and one wave forms the next chunk's gate
+//     prefix sums and decay rows (two row sets alternate); [B] A (fp32)
 //     and P into LDS while the next chunk's K, Q loads are in flight; [C] the
 //     four 16x16 diagonal inverses by forward substitution (one per wave), the
 //     16->32 merges and the 32->64 merge on MFMA; [D] Vnew, O and the state
@@ -344,9 +345,10 @@ fused_scan_kernel(const ScanParams p) {
         }
         __syncthreads();
 
-        // ---- [B] next chunk's K, Q and the gates of chunk c + 2 in flight; A (fp32) and P into LDS.  bf16:
-        // half of the K, Q loads go out here, the rest after the tiles are formed, so
-        // that a wave does not stall on a long run of load issues
+        // ---- [B] next chunk's K, Q and the gates of chunk c + 2 in flight; A (fp32)
+        // and P into LDS.  bf16: half of the K, Q loads go out here, the rest after
+        // the tiles are formed, so that a wave does not stall on a long run of load
+        // issues
         if constexpr (BF) {
             issue_kq_part(pf, p, next, hq, tid, 0);
             issue_kq_part(pf, p, next, hq, tid, 1);
