@@ -44,6 +44,9 @@ KERNEL = "fused_scan_kernel"
 KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_prefill_amd", "csrc", f)
                for f in ("gdn_scan.hip", "gdn_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_scan_large_batch.txt")
+DECODE_KERNEL = "decode_kernel"
+DECODE_SRCS = [os.path.join(ROOT, "chunked_gated_delta_prefill_amd", "csrc", "gdn_decode.hip")]
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_kernel_decode_batch.txt")
 
 
 def algorithmic(w):
@@ -59,24 +62,24 @@ def algorithmic(w):
     return flops, byts
 
 
-def kernel_source_sha():
+def kernel_source_sha(srcs=None):
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
+    for f in srcs or KERNEL_SRCS:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(path=TRAFFIC_FILE, srcs=None):
     """HBM bytes per launch measured by rocprofv3 PMC runs, if they were taken
     on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("kernel_source_sha") != kernel_source_sha():
+    if kv.get("kernel_source_sha") != kernel_source_sha(srcs):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -214,11 +217,17 @@ def summarize_counters(dirs, out_path, commands):
     print("\n".join(lines))
 
 
-def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes):
+SCAN_TRAFFIC_TITLE = "# HBM traffic of fused_scan_kernel, large_batch workload (32 x 8192 tokens, Hqk 16, Hv 32, bf16)"
+DECODE_TRAFFIC_TITLE = ("# HBM traffic of decode_kernel, decode_batch workload (256 one-token sequences, Hqk 16, Hv 32, "
+                        "fp32 state updated in place)")
+
+
+def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes, kernel=KERNEL, out_path=TRAFFIC_FILE,
+                  srcs=None, title=SCAN_TRAFFIC_TITLE):
     """Reads four rocprofv3 --pmc output dirs (kernel FETCH_SIZE, WRITE_SIZE;
     copy FETCH_SIZE, WRITE_SIZE) and writes the traffic summary file."""
-    kf = _pmc_values(os.path.join(base, "pmc_fetch"), KERNEL, "FETCH_SIZE")
-    kw = _pmc_values(os.path.join(base, "pmc_write"), KERNEL, "WRITE_SIZE")
+    kf = _pmc_values(os.path.join(base, "pmc_fetch"), kernel, "FETCH_SIZE")
+    kw = _pmc_values(os.path.join(base, "pmc_write"), kernel, "WRITE_SIZE")
     cf = _pmc_values(os.path.join(base, "pmc_copy_fetch"), "copyBuffer", "FETCH_SIZE")
     cw = _pmc_values(os.path.join(base, "pmc_copy_write"), "copyBuffer", "WRITE_SIZE")
     copy_bytes = float(1 << 30)
@@ -228,14 +237,14 @@ def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes):
     fetch = statistics.median(kf) * 1024.0 * f_fac
     write = statistics.median(kw) * 1024.0 * w_fac
     lines = [
-        "# HBM traffic of fused_scan_kernel, large_batch workload (32 x 8192 tokens, Hqk 16, Hv 32, bf16)",
+        title,
         "# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the same counter",
         "# read for a plain 1 GiB device-to-device copy (bench.py --copy-calibration).",
         f"# kernel FETCH_SIZE command: {cmd_fetch}",
         f"# kernel WRITE_SIZE command: {cmd_write}",
         f"# copy FETCH_SIZE command:   {cmd_cf}",
         f"# copy WRITE_SIZE command:   {cmd_cw}",
-        f"kernel_source_sha = {kernel_source_sha()}",
+        f"kernel_source_sha = {kernel_source_sha(srcs)}",
         f"dispatches_fetch = {len(kf)}",
         f"dispatches_write = {len(kw)}",
         f"raw_fetch_kib_median = {statistics.median(kf):.1f}",
@@ -250,9 +259,16 @@ def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes):
         f"algorithmic_bytes_per_launch = {launch_alg_bytes:.0f}",
         f"traffic_over_algorithmic = {(fetch + write) / launch_alg_bytes:.3f}",
     ]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    open(TRAFFIC_FILE, "w").write("\n".join(lines) + "\n")
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decode step on w: q, k, v, out, gates, and
+    the fp32 state read and written once."""
+    io = w.q.element_size()
+    return w.N * (2 * w.Hqk * D * io + 2 * w.Hv * D * io + w.Hv * 8) + 2 * w.N * w.Hv * D * D * 4
 
 
 def bench_decode(args, gdn, W):
@@ -263,8 +279,7 @@ def bench_decode(args, gdn, W):
     state = w.initial_state.clone()
     out = torch.empty(w.T, w.Hv, D, dtype=w.q.dtype, device="cuda")
     stream = torch.cuda.current_stream()
-    io = w.q.element_size()
-    byts = w.N * (2 * w.Hqk * D * io + 2 * w.Hv * D * io + w.Hv * 8) + 2 * w.N * w.Hv * D * D * 4
+    byts = decode_bytes(w)
 
     def step():
         gdn.gdn_decode_step(w.q, w.k, w.v, w.g, w.beta, w.scale, state, state, w.use_qk_l2norm, out, stream)
@@ -306,7 +321,8 @@ def bench_decode(args, gdn, W):
                    "state": "float32", "in_place": True, "l2norm": w.use_qk_l2norm},
         "kernel_ms": round(kern_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "decode_kernel",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SRCS), "kernel": DECODE_KERNEL,
                      "algorithmic_bytes": byts, "device_copy_gbs": round(copy_gbs, 1)},
         "cpu_baseline": None,
     }
@@ -377,6 +393,13 @@ def main():
 
     gdn.load()
     if args.decode:
+        if args.summarize_pmc:
+            cmds = json.loads(args.pmc_commands)
+            summarize_pmc(args.summarize_pmc, cmds.get("fetch", "?"), cmds.get("write", "?"),
+                          cmds.get("copy_fetch", "?"), cmds.get("copy_write", "?"),
+                          decode_bytes(W.decode_batch(device="cpu")), kernel=DECODE_KERNEL,
+                          out_path=DECODE_TRAFFIC_FILE, srcs=DECODE_SRCS, title=DECODE_TRAFFIC_TITLE)
+            return
         bench_decode(args, gdn, W)
         return
     w = W.make(args.workload, device="cuda", variant=args.variant)
