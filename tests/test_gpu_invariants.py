@@ -217,6 +217,16 @@ def test_split_path_no_states(gdn):
     assert nerr(out, ro) <= BF16_TOL
 
 
+def test_split_path_odd_heads(gdn):
+    """3 q/k heads, 6 value heads: the fix-up's (sequence, head) pairs (6) and the
+    scan's (item, q/k head) pairs are not multiples of the 8 XCDs."""
+    w = W.build([9000, 300], 3, 6, torch.bfloat16, seed=34, gate="long")
+    say("[gpu] split path, odd head counts")
+    out, fin = run_gpu(gdn, w, False)
+    ro, rf = run_oracle(w)
+    assert nerr(out, ro) <= BF16_TOL and nerr(fin, rf) <= BF16_TOL
+
+
 def test_split_path_bf16_states(gdn):
     w = W.build([10000, 0, 2400], 2, 4, torch.bfloat16, seed=34, state_in=torch.bfloat16,
                 state_out=torch.bfloat16, gate="long")

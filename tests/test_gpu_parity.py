@@ -75,10 +75,18 @@ def test_ragged_lengths_fp32(gdn):
     check(gdn, w, F32_TOL, True)
 
 
-@pytest.mark.parametrize("r", [1, 4])
+@pytest.mark.parametrize("r", [1, 4, 8])
 def test_head_ratios(gdn, r):
     w = W.build([100, 37], 4, 4 * r, torch.bfloat16, seed=9, name=f"ratio{r}")
     check(gdn, w, BF16_TOL, True)
+
+
+@pytest.mark.parametrize("bi", [True, False])
+def test_odd_head_counts(gdn, bi):
+    """3 q/k heads, 6 value heads, 3 sequences: 9 (sequence, q/k head) pairs, not
+    a multiple of the 8 XCDs the workgroup mapping groups by."""
+    w = W.build([100, 37, 64], 3, 6, torch.bfloat16, seed=12, name="odd_heads")
+    check(gdn, w, BF16_TOL, bi)
 
 
 def test_no_states(gdn):
