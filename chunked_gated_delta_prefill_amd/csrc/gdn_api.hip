@@ -380,14 +380,20 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     const bool bf = io == GDN_BF16;
     hipStream_t hs = static_cast<hipStream_t>(stream);
 
-    // Split path (T precompute -> MN precompute -> state fixup -> CP prefill) when
+    // Split path (T precompute -> MN precompute -> state fix-up -> CP prefill) when
     // one work item per (sequence, head) leaves the GPU under-filled and the
-    // sequences are long on average: a split sequence runs three passes over a
-    // segment (two maps, then the scan) plus the fix-up, so segments shorter than
-    // about a third of the sequence pay off; with an average below 4 shortest
-    // segments it does not (a batch of 8 sequences of ~1900 tokens: 0.43 ms split,
-    // 0.33 ms unsplit).  Never with batch_invariant (the split changes the
-    // reduction order of a sequence).
+    // sequences are long on average.  A split sequence runs three passes over each
+    // segment (two maps, then the scan) plus one fix-up step per segment boundary,
+    // and the split multiplies the work items, which may push a launch from one
+    // to two workgroups per CU.  The two plans are compared in units of one chunk
+    // at one workgroup per CU: a launch of W items costs one unit per chunk while
+    // W <= CUs and 1.6 per round of two workgroups per CU above that (measured:
+    // 5.0 and 7.9 us per chunk), a fix-up step and the extra launches about one
+    // unit per segment.  Measured on 8 sequences of 8192 tokens (32 heads): the
+    // fixed rule used before split them into 2 segments, 1.10 ms against 0.64 ms
+    // unsplit.  Never with batch_invariant (the split changes the reduction order
+    // of a sequence).  The host knows only T and N, so the plan uses the average
+    // sequence length.
     const int64_t fill = 2 * (int64_t)cus;
     int64_t lseg = 0;
     if (!batch_invariant && N * Hv < fill && T > 0 && T >= 4 * kMinSegment * N) {
@@ -395,6 +401,17 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
         lseg = (lseg + gdn::kChunk - 1) / gdn::kChunk * gdn::kChunk;
         if (lseg < kMinSegment) lseg = kMinSegment;
         if (lseg >= T) lseg = 0;   // no sequence is long enough to split
+    }
+    if (lseg > 0) {
+        auto per_chunk = [&](int64_t items) {
+            return items <= cus ? 1.0 : 1.6 * (double)((items + fill - 1) / fill);
+        };
+        const int64_t avg = (T + N - 1) / N;
+        const int64_t P = (avg + lseg - 1) / lseg;
+        const double unsplit = (double)((avg + gdn::kChunk - 1) / gdn::kChunk) * per_chunk(N * Hv);
+        const double split = (double)(lseg / gdn::kChunk) *
+                                 (2.0 * per_chunk(N * (P - 1) * Hv) + per_chunk(N * P * Hv)) + (double)P;
+        if (!(split < unsplit)) lseg = 0;
     }
     hipError_t e;
     if (lseg == 0) {
