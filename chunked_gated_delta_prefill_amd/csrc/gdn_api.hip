@@ -415,7 +415,12 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     }
     hipError_t e;
     if (lseg == 0) {
-        e = gdn::launch_fused_scan(p, bf, gdn::kScan, hs);
+        // At most one work item per CU: the pipelined eight-wave scan (one
+        // workgroup per CU, preparation of chunk c + 1 beside the state work of
+        // chunk c); it gives bitwise the results of the four-wave scan, so the
+        // choice keeps batch_invariant results independent of the batch.
+        if (bf && !p.ck && N * Hv <= cus) e = gdn::launch_piped_scan(p, hs);
+        else e = gdn::launch_fused_scan(p, bf, gdn::kScan, hs);
         if (e != hipSuccess) return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
         return GDN_OK;
     }

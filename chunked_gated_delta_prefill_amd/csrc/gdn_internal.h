@@ -113,6 +113,9 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 // Fused chunked scan: one workgroup per (sequence or segment, value head).
 // io_bf16 selects bf16 q/k/v/out (bf16 MFMA) or fp32 (fp32 MFMA).
 hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, int mode, hipStream_t stream);
+// The eight-wave pipelined scan (bf16, scan mode, no checkpoints); same results
+// as launch_fused_scan, one workgroup per CU.
+hipError_t launch_piped_scan(const ScanParams &p, hipStream_t stream);
 
 // Split plan: cu_seqlens -> segment table of at most `cap` entries of `lseg`
 // tokens (a multiple of the chunk), one entry for an empty sequence.

@@ -28,6 +28,45 @@ def test_api_defaults_are_bitwise(gdn):
     assert torch.equal(o3, o4) and torch.equal(f3, f4)
 
 
+@pytest.mark.parametrize("gate", ["sigmoid", "strong"])
+def test_batch_invariance_across_scan_kernels(gdn, gate):
+    """Launches with at most one work item per CU run the eight-wave pipelined
+    scan, larger ones the four-wave scan; both must give bitwise the same
+    results, or batch_invariant results would depend on the batch size.  A
+    batch with more work items than CUs is compared with sequences of it run
+    alone and with a sub-batch below the threshold.  "strong" gates put half
+    of the sequences on the entry-wise exp path (chunk log-decay below -60)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Hqk, Hv = 2, 4
+    N = cus // Hv + 9
+    gen = torch.Generator().manual_seed(61)
+    lens = torch.randint(0, 300, (N,), generator=gen).tolist()
+    lens[0], lens[5], lens[7] = 0, 64, 1000
+    w = W.build(lens, Hqk, Hv, torch.bfloat16, seed=62)
+    if gate == "strong":
+        t = torch.arange(w.T)
+        seq = torch.searchsorted(w.cu_seqlens.to(torch.int64)[1:], t, right=True)
+        w = W.Workload(**{**w.__dict__, "g": torch.where((seq % 2 == 1).unsqueeze(1), torch.full_like(w.g, 0.2), w.g)})
+    say(f"[gpu] batch invariance across kernels: {N * Hv} work items ({cus} CUs), gate={gate}")
+    out, fin = run_gpu(gdn, w, True)
+    cu = w.cu_seqlens.tolist()
+    for n in (0, 5, 7, 11, N - 1):
+        sub = W.slice_item(w, n, range(w.Hv))
+        sub = W.Workload(**{**sub.__dict__, "q": w.q[cu[n]:cu[n + 1]], "k": w.k[cu[n]:cu[n + 1]]})
+        o1, f1 = run_gpu(gdn, sub, True)
+        assert torch.equal(o1, out[cu[n]:cu[n + 1]]), n
+        assert torch.equal(f1[0], fin[n]), n
+    m = cus // Hv - 3   # a leading sub-batch below the threshold
+    head = W.Workload(**{**w.__dict__, "q": w.q[:cu[m]], "k": w.k[:cu[m]], "v": w.v[:cu[m]], "g": w.g[:cu[m]],
+                         "beta": w.beta[:cu[m]], "cu_seqlens": w.cu_seqlens[:m + 1],
+                         "initial_state": w.initial_state[:m]})
+    o2, f2 = run_gpu(gdn, head, True)
+    assert torch.equal(o2, out[:cu[m]])
+    assert torch.equal(f2, fin[:m])
+    ro, rf = run_oracle(head)
+    assert nerr(o2, ro) <= BF16_TOL and nerr(f2, rf) <= BF16_TOL
+
+
 def test_run_to_run_bitwise(gdn):
     w = _w(seed=22)
     say("[gpu] run-to-run determinism")
