@@ -143,61 +143,69 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
 
-    // The two roles run separate loops with the same barriers (five per
-    // iteration), so each role's registers are allocated for its own code only.
+    // The two roles run separate loops with the same barriers (one more before
+    // the loop, five per iteration), so each role's registers are allocated for
+    // its own code only.  Iteration c:
+    //   interval  state waves                             preparation waves
+    //   1         V staging, Z', Vnew, ub of chunk c      A and P of chunk c + 1, row factors
+    //   2         output products and staging (c)         diagonal inverses (c + 1)
+    //   3         output stores, state update (c);        16 -> 32 merges (c + 1); gate rows of c + 2
+    //             V loads of chunk c + 1
+    //   4         K S~^T, S~ Q^T of chunk c + 1 (first    32 -> 64 merge (c + 1); K, Q of c + 2 staged
+    //             half of the contraction)
+    //   5         the second half                         Gram tiles and norms of chunk c + 2
     // sigma: scale of the true state (sigma S~) at the start of the wave's chunk;
     // the preparation waves track it one chunk ahead with the same arithmetic.
     if (is_state) {
         float sigma = 1.f;
+        f32x16 X[2] = {zero16(), zero16()}, Y[2] = {zero16(), zero16()};
+        // X = K S~^T and Y = S~ Q^T of chunk x over contraction steps k0 .. k0 + 3
+        // (the next step's fragments read while the current one runs)
+        auto xy_half = [&](auto k0c, int x, int lane) {
+            constexpr int k0 = decltype(k0c)::value;
+            const int h32 = lane >> 5, l32 = lane & 31;
+            const bf16 *Ks = kbuf(x), *Qs = qbuf(x);
+            frag fk[2][2], fq[2][2];
+            auto load = [&](int k, int st) {
+                fk[st][0] = ld_kq(Ks, l32, k, h32);
+                fk[st][1] = ld_kq(Ks, 32 + l32, k, h32);
+                fq[st][0] = ld_kq(Qs, l32, k, h32);
+                fq[st][1] = ld_kq(Qs, 32 + l32, k, h32);
+            };
+            load(k0, 0);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int k = k0 + kk, cur = kk & 1;
+                if (kk + 1 < 4) load(k + 1, cur ^ 1);
+                const frag sf = acc_frag<bf16>(S[k / S32], k % S32);
+                X[0] = M::run(fk[cur][0], sf, X[0]);
+                X[1] = M::run(fk[cur][1], sf, X[1]);
+                Y[0] = M::run(sf, fq[cur][0], Y[0]);
+                Y[1] = M::run(sf, fq[cur][1], Y[1]);
+            }
+        };
+        __syncthreads();   // (the preparation's Gram tiles of chunk 0)
         for (int c = -1; c < nchunks; ++c) {
-            const int x = c;   // state work of chunk c
-            const bool on = c >= 0;
             int tid_o = threadIdx.x;
             asm volatile("" : "+v"(tid_o));
             const int tid = tid_o, lane = tid & 63;
             const int ws = __builtin_amdgcn_readfirstlane(tid >> 6);
             const int h32 = lane >> 5, l32 = lane & 31;
-            auto rf = [&](int which) { return rows(which, x); };
+            const bool on = c >= 0;
+            auto rf = [&](int which) { return rows(which, c); };
             const float gLc =
-                __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gamma_l(x))));
+                __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gamma_l(c))));
             const float sig_next = sigma * gLc;
             const bool renorm = !(sig_next >= kRenorm);
             const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                                   int, rf(RG_)[C - 1]))) > kFastDecay;
-            const bf16 *Ks = kbuf(x);
-            const bf16 *Qs = qbuf(x);
-            const ChunkRef ch = chunk_at(bos, eos, x);
+            const ChunkRef ch = chunk_at(bos, eos, c);
             const int Lc = ch.L;
+            const bf16 *Ks = kbuf(c);
+            bf16 *Ow = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + ws * (C * 32);
 
-            // ---- interval 1: state: X = K S~^T, Y = S~ Q^T (own rows); preparation:
-            // Gram tiles (transposed, lane = row i, registers = column j) and row norms.
-            // The preparation waves keep their Gram tiles in X.
-            f32x16 X[2] = {zero16(), zero16()}, Y[2] = {zero16(), zero16()};
-            if (on) {
-                constexpr int NK = 4 * S32;
-                frag fk[2][2], fq[2][2];
-                auto load = [&](int k, int st) {
-                    fk[st][0] = ld_kq(Ks, l32, k, h32);
-                    fk[st][1] = ld_kq(Ks, 32 + l32, k, h32);
-                    fq[st][0] = ld_kq(Qs, l32, k, h32);
-                    fq[st][1] = ld_kq(Qs, 32 + l32, k, h32);
-                };
-                load(0, 0);
-#pragma unroll
-                for (int k = 0; k < NK; ++k) {
-                    const int cur = k & 1;
-                    if (k + 1 < NK) load(k + 1, cur ^ 1);
-                    const frag sf = acc_frag<bf16>(S[k / S32], k % S32);
-                    X[0] = M::run(fk[cur][0], sf, X[0]);
-                    X[1] = M::run(fk[cur][1], sf, X[1]);
-                    Y[0] = M::run(sf, fq[cur][0], Y[0]);
-                    Y[1] = M::run(sf, fq[cur][1], Y[1]);
-                }
-            }
-            __syncthreads();
-
-            // ---- interval 2: state: Z', Vnew, ub and the output products of chunk c;
-            // preparation: A (fp32) and P of chunk c + 1, the row factors of [D]
+            // ---- interval 1: Z' = V - FZ o X, Vnew = T' Z', ub = FU o Vnew (slow
+            // path: the output products with their own Vnew operand)
             frag ub[2][S32];
             if (on) {
                 frag zb[2][S32];
@@ -205,17 +213,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     // V through this wave's 4 KB, back as 4 consecutive tokens of one
                     // column (transposing reads): registers 4q .. 4q+3 of tile ib
                     float vv[2][16];
-                    bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + ws * (C * 32);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        *reinterpret_cast<i32x4 *>(Vw + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = pf.kq[0][j];
+                        *reinterpret_cast<i32x4 *>(Ow + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = pf.kq[0][j];
                     const int i = lane & 15, g16 = (lane >> 4) & 1;
                     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const bf16 *src = Vw + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
+                            const bf16 *src = Ow + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
                             const bf16x4 xv =
                                 __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src));
 #pragma unroll
@@ -275,7 +282,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int s = 0; s < S32; ++s) ub[ib][s] = acc_frag<bf16>(Vn[ib], s);
                 }
+            }
+            __syncthreads();
+
+            // ---- interval 2: fast path output O^T = FY_t [S~ Q^T + ub^T P^T]; the
+            // output tile staged through this wave's 4 KB: rows t of its 32 columns
+            // (64 B), 16-byte granules of row t rotated by (t / 4) % 4 against bank
+            // conflicts
+            if (on) {
                 if (fast) {
+                    const bf16 *Ps = pbuf(c);
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
@@ -289,10 +305,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
                     }
                 }
-                // output tile staged through this wave's 4 KB (the V values are read):
-                // rows t of its 32 columns (64 B), 16-byte granules of row t rotated by
-                // (t / 4) % 4 against bank conflicts; stored in interval 3
-                bf16 *Ow = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + ws * (C * 32);
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -305,18 +317,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             __syncthreads();
 
-            // ---- interval 3: state: output staging, stores and the state update of
-            // chunk c, then the next chunk's V; preparation: each wave inverts one
-            // 16x16 diagonal block of I + A for chunk c + 1
+            // ---- interval 3: S~ += K^T ub (after the renorm fold), one 16-row group
+            // of output stores per step; then the next chunk's V
             if (on) {
-                const bf16 *Ow = reinterpret_cast<const bf16 *>(smem + L::VO_OFF) + ws * (C * 32);
                 if (renorm) {
 #pragma unroll
                     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) S[bb][rr] *= sig_next;
                 }
-                // S~ += K^T ub, one 16-row group of output stores per step
                 constexpr int NU = 2 * S32;
                 frag kt[2][4];
                 auto load_kt = [&](int k, frag (&f)[4]) {
@@ -346,7 +355,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     pf.kq[0][j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * j * p.v_st, 0, 0);
             }
             __syncthreads();
-            __syncthreads();   // intervals 4 and 5: preparation only
+
+            // ---- interval 4: X and Y of chunk c + 1 from the updated state (interval 5
+            // leaves the LDS to the preparation's Gram pass)
+            if (c + 1 < nchunks) {
+                X[0] = X[1] = Y[0] = Y[1] = zero16();
+                xy_half(std::integral_constant<int, 0>{}, c + 1, lane);
+                xy_half(std::integral_constant<int, 4>{}, c + 1, lane);
+            }
+            __syncthreads();
             __syncthreads();
             if (on) sigma = renorm ? 1.f : sig_next;
         }
@@ -354,9 +371,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // ---- final state
         if (p.s_out && srow >= 0) {
             if (sigma != 1.f) {
-    #pragma unroll
+#pragma unroll
                 for (int bb = 0; bb < 4; ++bb)
-    #pragma unroll
+#pragma unroll
                     for (int rr = 0; rr < 16; ++rr) S[bb][rr] *= sigma;
             }
             const int lane = threadIdx.x & 63, h32 = lane >> 5, v0 = ws0 * 32 + (lane & 31);
@@ -364,14 +381,97 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     } else {
         float sigma = 1.f;
+        const int pw = ws0 & 3;   // role within the preparation waves
+        // Gram tiles of the chunk being prepared (transposed: lane = row i,
+        // registers = column j), kept from interval 5 to the next interval 1
+        f32x16 X[2] = {zero16(), zero16()};
+        // Gram tiles and row norms of chunk x; tiles as in the four-wave scan:
+        // 0: A(0,0) (even / odd steps), norms of K_0 and Q_1; 1: A(1,0), P(1,1),
+        // norm of K_1; 2: A(1,1) (even / odd); 3: P(0,0), P(1,0), norm of Q_0
+        auto gram = [&](int x, int lane) {
+            const int h32 = lane >> 5, l32 = lane & 31;
+            const bf16 *Ks = kbuf(x), *Qs = qbuf(x);
+            // 1 / |row| (or 1 without the norm); a K row's factor also goes into
+            // its 1 / gamma entry, which only the A tiles read
+            auto put_norm = [&](float ss, int which, int blk) {
+                ss += __shfl_xor(ss, 32);
+                if (h32 == 0) {
+                    const int row = 32 * blk + l32;
+                    const float rr = p.l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;
+                    rows(which, x)[row] = rr;
+                    if (which == RK_) rows(IG_, x)[row] *= rr;
+                }
+            };
+            X[0] = X[1] = zero16();
+            auto pass = [&](auto role) {
+                constexpr int R = decltype(role)::value;
+                constexpr int NK = 4 * S32;
+                frag fa[2][3];
+                auto load = [&](int k, int st) {
+                    if constexpr (R == 0) {
+                        fa[st][0] = ld_kq(Ks, l32, k, h32);
+                        fa[st][1] = ld_kq(Qs, 32 + l32, k, h32);
+                    } else if constexpr (R == 1) {
+                        fa[st][0] = ld_kq(Ks, l32, k, h32);
+                        fa[st][1] = ld_kq(Ks, 32 + l32, k, h32);
+                        fa[st][2] = ld_kq(Qs, 32 + l32, k, h32);
+                    } else if constexpr (R == 2) {
+                        fa[st][0] = ld_kq(Ks, 32 + l32, k, h32);
+                    } else {
+                        fa[st][0] = ld_kq(Ks, l32, k, h32);
+                        fa[st][1] = ld_kq(Qs, l32, k, h32);
+                        fa[st][2] = ld_kq(Qs, 32 + l32, k, h32);
+                    }
+                };
+                float ssa = 0.f, ssb = 0.f;
+                load(0, 0);
+#pragma unroll
+                for (int k = 0; k < NK; ++k) {
+                    const int cur = k & 1;
+                    if (k + 1 < NK) load(k + 1, cur ^ 1);
+                    if constexpr (R == 0) {   // k0, q1
+                        X[cur] = M::run(fa[cur][0], fa[cur][0], X[cur]);
+                        ssa += sumsq8_acc(fa[cur][0], 0.f);
+                        ssb += sumsq8_acc(fa[cur][1], 0.f);
+                    } else if constexpr (R == 1) {   // k0, k1, q1
+                        X[0] = M::run(fa[cur][0], fa[cur][1], X[0]);
+                        ssa += sumsq8_acc(fa[cur][1], 0.f);
+                        X[1] = M::run(fa[cur][1], fa[cur][2], X[1]);
+                    } else if constexpr (R == 2) {   // k1
+                        X[cur] = M::run(fa[cur][0], fa[cur][0], X[cur]);
+                    } else {   // k0, q0, q1
+                        X[0] = M::run(fa[cur][0], fa[cur][1], X[0]);
+                        X[1] = M::run(fa[cur][0], fa[cur][2], X[1]);
+                        ssb += sumsq8_acc(fa[cur][1], 0.f);
+                    }
+                }
+                if constexpr (R == 0) {
+                    X[0] += X[1];
+                    put_norm(ssa, RK_, 0);
+                    put_norm(ssb, RQ_, 1);
+                } else if constexpr (R == 1) {
+                    put_norm(ssa, RK_, 1);
+                } else if constexpr (R == 2) {
+                    X[0] += X[1];
+                } else {
+                    put_norm(ssb, RQ_, 0);
+                }
+            };
+            if (pw == 0) pass(std::integral_constant<int, 0>{});
+            else if (pw == 1) pass(std::integral_constant<int, 1>{});
+            else if (pw == 2) pass(std::integral_constant<int, 2>{});
+            else pass(std::integral_constant<int, 3>{});
+        };
+        if (nchunks > 0) gram(0, threadIdx.x & 63);
+        __syncthreads();
         for (int c = -1; c < nchunks; ++c) {
-            const int x = c + 1;   // preparation of chunk c + 1
-            const bool on = c + 1 < nchunks;
             int tid_o = threadIdx.x;
             asm volatile("" : "+v"(tid_o));
             const int tid = tid_o, lane = tid & 63;
             const int ws = __builtin_amdgcn_readfirstlane(tid >> 6);
             const int h32 = lane >> 5, l32 = lane & 31;
+            const int x = c + 1;   // the chunk being prepared
+            const bool on = x < nchunks, on2 = c + 2 < nchunks;
             auto rf = [&](int which) { return rows(which, x); };
             const float gLc =
                 __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gamma_l(x))));
@@ -379,97 +479,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const bool renorm = !(sig_next >= kRenorm);
             const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                                   int, rf(RG_)[C - 1]))) > kFastDecay;
-            const bf16 *Ks = kbuf(x);
-            const bf16 *Qs = qbuf(x);
-            const int pw = ws & 3;   // role within the preparation waves
+            bf16 *Ts = tbuf(x);
 
-            // ---- interval 1: state: X = K S~^T, Y = S~ Q^T (own rows); preparation:
-            // Gram tiles (transposed, lane = row i, registers = column j) and row norms.
-            // The preparation waves keep their Gram tiles in X.
-            f32x16 X[2] = {zero16(), zero16()};
+            // ---- interval 1: A (fp32) and P of chunk x from the Gram tiles, row
+            // factors of the state work.  Lane row i = 32 bi + l32; register 4 jj + t
+            // is column j = 32 bj + 8 jj + 4 h32 + t.
+            //   A = b_i rk_i rk_j (k_i . k_j) exp(G_i - G_j)   for j < i   (fp32)
+            //   P = c rq_i rk_j (q_i . k_j) exp(G_i - G_j)      for j <= i  (slow)
+            //   P = (q_i . k_j) / sigma' (renorm only)          for j <= i  (fast)
             if (on) {
-                constexpr int NK = 4 * S32;
-                // 1 / |row| (or 1 without the norm); a K row's factor also goes into
-                // its 1 / gamma entry, which only the A tiles read
-                auto put_norm = [&](float ss, int which, int blk) {
-                    ss += __shfl_xor(ss, 32);
-                    if (h32 == 0) {
-                        const int row = 32 * blk + l32;
-                        const float rr = p.l2norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.f;
-                        rf(which)[row] = rr;
-                        if (which == RK_) rf(IG_)[row] *= rr;
-                    }
-                };
-                // roles as in the four-wave scan: 0: A(0,0) (even / odd steps), norms
-                // of K_0 and Q_1; 1: A(1,0), P(1,1), norm of K_1; 2: A(1,1) (even /
-                // odd); 3: P(0,0), P(1,0), norm of Q_0
-                auto pass = [&](auto role) {
-                    constexpr int R = decltype(role)::value;
-                    frag fa[2][3];
-                    auto load = [&](int k, int st) {
-                        if constexpr (R == 0) {
-                            fa[st][0] = ld_kq(Ks, l32, k, h32);
-                            fa[st][1] = ld_kq(Qs, 32 + l32, k, h32);
-                        } else if constexpr (R == 1) {
-                            fa[st][0] = ld_kq(Ks, l32, k, h32);
-                            fa[st][1] = ld_kq(Ks, 32 + l32, k, h32);
-                            fa[st][2] = ld_kq(Qs, 32 + l32, k, h32);
-                        } else if constexpr (R == 2) {
-                            fa[st][0] = ld_kq(Ks, 32 + l32, k, h32);
-                        } else {
-                            fa[st][0] = ld_kq(Ks, l32, k, h32);
-                            fa[st][1] = ld_kq(Qs, l32, k, h32);
-                            fa[st][2] = ld_kq(Qs, 32 + l32, k, h32);
-                        }
-                    };
-                    float ssa = 0.f, ssb = 0.f;
-                    load(0, 0);
-#pragma unroll
-                    for (int k = 0; k < NK; ++k) {
-                        const int cur = k & 1;
-                        if (k + 1 < NK) load(k + 1, cur ^ 1);
-                        if constexpr (R == 0) {   // k0 = fa[0], q1 = fa[1]
-                            X[cur] = M::run(fa[cur][0], fa[cur][0], X[cur]);
-                            ssa += sumsq8_acc(fa[cur][0], 0.f);
-                            ssb += sumsq8_acc(fa[cur][1], 0.f);
-                        } else if constexpr (R == 1) {   // k0, k1, q1
-                            X[0] = M::run(fa[cur][0], fa[cur][1], X[0]);
-                            ssa += sumsq8_acc(fa[cur][1], 0.f);
-                            X[1] = M::run(fa[cur][1], fa[cur][2], X[1]);
-                        } else if constexpr (R == 2) {   // k1
-                            X[cur] = M::run(fa[cur][0], fa[cur][0], X[cur]);
-                        } else {   // k0, q0, q1
-                            X[0] = M::run(fa[cur][0], fa[cur][1], X[0]);
-                            X[1] = M::run(fa[cur][0], fa[cur][2], X[1]);
-                            ssb += sumsq8_acc(fa[cur][1], 0.f);
-                        }
-                    }
-                    if constexpr (R == 0) {
-                        X[0] += X[1];
-                        put_norm(ssa, RK_, 0);
-                        put_norm(ssb, RQ_, 1);
-                    } else if constexpr (R == 1) {
-                        put_norm(ssa, RK_, 1);
-                    } else if constexpr (R == 2) {
-                        X[0] += X[1];
-                    } else {
-                        put_norm(ssb, RQ_, 0);
-                    }
-                };
-                if (pw == 0) pass(std::integral_constant<int, 0>{});
-                else if (pw == 1) pass(std::integral_constant<int, 1>{});
-                else if (pw == 2) pass(std::integral_constant<int, 2>{});
-                else pass(std::integral_constant<int, 3>{});
-            }
-            __syncthreads();
-
-            // ---- interval 2: state: Z', Vnew, ub and the output products of chunk c;
-            // preparation: A (fp32) and P of chunk c + 1, the row factors of [D]
-            if (on) {
-                // Lane row i = 32 bi + l32; register 4 jj + t is column j = 32 bj + 8 jj + 4 h32 + t.
-                //   A = b_i rk_i rk_j (k_i . k_j) exp(G_i - G_j)   for j < i   (fp32)
-                //   P = c rq_i rk_j (q_i . k_j) exp(G_i - G_j)      for j <= i  (slow)
-                //   P = (q_i . k_j) / sigma' (renorm only)          for j <= i  (fast)
                 bf16 *Ps = pbuf(x);
                 const float cP = renorm ? 1.f / sig_next : 1.f;
                 const int dlane = l32 - 4 * h32;
@@ -562,31 +580,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             __syncthreads();
 
-            // ---- interval 3: state: output staging, stores and the state update of
-            // chunk c, then the next chunk's V; preparation: each wave inverts one
-            // 16x16 diagonal block of I + A for chunk c + 1
+            // ---- interval 2: D = (I + N)^-1 for the strictly lower 16x16 diagonal
+            // block N of rows 16 pw .. 16 pw + 15, by forward substitution (lane =
+            // column cc and row class rq; the pivot is broadcast inside the lane quad)
             if (on) {
-                // D = (I + N)^-1 for the strictly lower 16x16 diagonal block N of rows
-                // 16 pw .. 16 pw + 15, by forward substitution (lane = column cc and row
-                // class rq; the pivot is broadcast inside the lane quad)
-                bf16 *Ts = tbuf(x);
                 const int cc = lane >> 2, rq = lane & 3;
                 const float *nt = NT + pw * L::NTS + 4 * rq;
                 float xs[4];
-    #pragma unroll
+#pragma unroll
                 for (int k = 0; k < 4; ++k) xs[k] = rq + 4 * k == cc ? 1.f : 0.f;
                 f32x4 ncol[2];
                 ncol[0] = ld4(nt);
-    #pragma unroll
+#pragma unroll
                 for (int m = 0; m < 15; ++m) {
                     if (m + 1 < 15) ncol[(m + 1) & 1] = ld4(nt + (m + 1) * 16);
                     const float xm = quad_bcast(xs[m >> 2], m & 3);
-    #pragma unroll
+#pragma unroll
                     for (int k = 0; k < 4; ++k) xs[k] = fmaf(-ncol[m & 1][k], xm, xs[k]);
                 }
                 const float bcol = rf(FB_)[16 * pw + cc];
                 float *blk = Af + (16 * pw) * L::FLD + 16 * pw;
-    #pragma unroll
+#pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int i = rq + 4 * k;
                     blk[i * L::FLD + cc] = xs[k];
@@ -596,12 +610,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             __syncthreads();
 
-            // ---- interval 4: preparation: 16 -> 32 merges (waves 4, 5) of chunk c + 1:
-            // T'_{2x+1,2x} = -D_{2x+1} A_{2x+1,2x} D_{2x}; K, Q and gate rows of chunk
-            // c + 2 staged (their buffers were last read by the state work of chunk c);
-            // loads of chunk c + 3
+            // ---- interval 3: 16 -> 32 merges (waves 4, 5): T'_{2x+1,2x} =
+            // -D_{2x+1} A_{2x+1,2x} D_{2x}; the gate rows of chunk c + 2 (their row
+            // set was last read by the state work of chunk c) and the gate loads of
+            // chunk c + 3
             if (on && pw < 2) {
-                bf16 *Ts = tbuf(x);
                 const int g = lane >> 4, nn = lane & 15;
                 const int lo = 32 * pw, hi = 32 * pw + 16;
                 f32x4 R = {0.f, 0.f, 0.f, 0.f};
@@ -617,29 +630,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     Ts[i * L::OLD + lo + nn] = (bf16)(-Tq[rr] * bcol);
                 }
             }
-            if (c + 2 < nchunks) {
-                const int tp = tid - 256;
-                const int rq4 = tp >> 4, cg = tp & 15;
-#pragma unroll
-                for (int mat = 0; mat < 2; ++mat)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        *reinterpret_cast<i32x4 *>((mat ? qbuf(c + 2) : kbuf(c + 2)) + kq_off(4 * rq4 + t, 8 * cg)) =
-                            pf.kq[mat][t];
-                if (ws == kGateW) gate_rows(pf, chunk_at(bos, eos, c + 2).L, c + 2, lane);
-                if (c + 3 < nchunks) {
-                    issue_loads<bf16>(pf, p, chunk_at(bos, eos, c + 3), hq, h, tp, lane, ws);
-                    if (ws == kGateW) issue_gates(pf, p, chunk_at(bos, eos, c + 3), h, lane);
-                }
+            if (on2 && ws == kGateW) {
+                gate_rows(pf, chunk_at(bos, eos, c + 2).L, c + 2, lane);
+                if (c + 3 < nchunks) issue_gates(pf, p, chunk_at(bos, eos, c + 3), h, lane);
             }
-        
             __syncthreads();
 
-            // ---- interval 5: preparation: 32 -> 64 merge of chunk c + 1 on the four
-            // waves, wave (r, cc) forming block (r, cc) of T''_21 = -T'_22 A_21 T''_11
-            // (T''_11 read as its column-scaled copy with transposing loads)
+            // ---- interval 4: 32 -> 64 merge on the four waves, wave (r, cc) forming
+            // block (r, cc) of T''_21 = -T'_22 A_21 T''_11 (T''_11 read as its
+            // column-scaled copy with transposing loads); K and Q of chunk c + 2
+            // staged (their buffers were last read by the state update of chunk c),
+            // half of the loads of chunk c + 3
             if (on) {
-                bf16 *Ts = tbuf(x);
                 const int rr2 = pw >> 1, cc = pw & 1;
                 const int g = lane >> 4, nn = lane & 15;
                 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                   (bf16)bq[3]};
                 };
                 f32x4 R[2];
-    #pragma unroll
+#pragma unroll
                 for (int rp = 0; rp < 2; ++rp)
                     R[rp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row8(32 + 16 * rp + nn, 8 * g, 8 * g + 4), tb,
                                                                    f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -661,8 +663,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                    (bf16)R[1][0], (bf16)R[1][1], (bf16)R[1][2], (bf16)R[1][3]};
                 const f32x4 T21 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row8(32 + 16 * rr2 + nn, 32 + 4 * g, 48 + 4 * g),
                                                                          rb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    #pragma unroll
+#pragma unroll
                 for (int q = 0; q < 4; ++q) Ts[(32 + 16 * rr2 + 4 * g + q) * L::OLD + 16 * cc + nn] = (bf16)(-T21[q]);
+            }
+            const int tp = tid - 256;
+            if (on2) {
+                const int rq4 = tp >> 4, cg = tp & 15;
+#pragma unroll
+                for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        *reinterpret_cast<i32x4 *>((mat ? qbuf(c + 2) : kbuf(c + 2)) + kq_off(4 * rq4 + t, 8 * cg)) =
+                            pf.kq[mat][t];
+            }
+            if (c + 3 < nchunks) {
+                issue_kq_part(pf, p, chunk_at(bos, eos, c + 3), hq, tp, 0);
+                issue_kq_part(pf, p, chunk_at(bos, eos, c + 3), hq, tp, 1);
+            }
+            __syncthreads();
+
+            // ---- interval 5: Gram tiles and norms of chunk c + 2; the other half of
+            // the loads of chunk c + 3
+            if (on2) gram(c + 2, lane);
+            if (c + 3 < nchunks) {
+                issue_kq_part(pf, p, chunk_at(bos, eos, c + 3), hq, tp, 2);
+                issue_kq_part(pf, p, chunk_at(bos, eos, c + 3), hq, tp, 3);
             }
             __syncthreads();
             if (on) sigma = renorm ? 1.f : sig_next;
