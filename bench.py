@@ -62,6 +62,30 @@ def algorithmic(w):
     return flops, byts
 
 
+def scan_kernels(w, batch_invariant, cus, checkpoints=False):
+    """Kernels one prefill call launches: the host plan of gdn_api.hip (split
+    path when its cost model favours it, else one scan launch: the eight-wave
+    pipelined scan for bf16 with at most one work item per CU)."""
+    import torch
+    N, T, Hv = w.N, w.T, w.Hv
+    fill, lseg = 2 * cus, 0
+    if not batch_invariant and N * Hv < fill and T > 0 and T >= 4 * 1024 * N:
+        lseg = max(1024, -(-(-(-T * Hv // fill)) // 64) * 64)
+        if lseg >= T:
+            lseg = 0
+    if lseg:
+        per_chunk = lambda items: 1.0 if items <= cus else 1.6 * (-(-items // fill))
+        avg = -(-T // N)
+        P = -(-avg // lseg)
+        unsplit = -(-avg // 64) * per_chunk(N * Hv)
+        split = lseg // 64 * (2 * per_chunk(N * (P - 1) * Hv) + per_chunk(N * P * Hv)) + P
+        if split < unsplit:
+            return "split: plan_kernel, fused_scan_kernel (maps N, M), fixup_kernel, fused_scan_kernel"
+    if w.q.dtype == torch.bfloat16 and not checkpoints and N * Hv <= cus:
+        return "piped_scan_kernel"
+    return KERNEL
+
+
 def kernel_source_sha(srcs=None):
     h = hashlib.sha256()
     for f in srcs or KERNEL_SRCS:
@@ -476,7 +500,10 @@ def main():
                               round(sorted(launch_ms)[int(0.8 * (len(launch_ms) - 1))], 4)],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": KERNEL, "algorithmic_bytes": byts, "algorithmic_flops": flops},
+                     "kernel": scan_kernels(w, args.batch_invariant,
+                                            torch.cuda.get_device_properties(0).multi_processor_count,
+                                            bool(ck_every)),
+                     "algorithmic_bytes": byts, "algorithmic_flops": flops},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -1,4 +1,4 @@
-// Device helpers shared by the scan kernels (gdn_scan.hip, gdn_pair.hip):
+// Device helpers shared by the scan kernels (gdn_scan.hip, gdn_scan_piped.hip):
 // MFMA operand layouts, LDS operand reads, buffer loads of one chunk, gate
 // decoding, DPP reductions and state I/O.  Internal; included by .hip files only.
 #pragma once

@@ -13,26 +13,20 @@
 //   state work   (needs the state): K S~^T and S~ Q^T, Z', Vnew = T' Z', the
 //                output and the state update.
 // In the four-wave kernel both run one after the other on the same waves, so a
-// chunk costs the sum of the two chains (~12.9 K cycles with one workgroup per
+// chunk costs the sum of the two chains (~11.9 K cycles with one workgroup per
 // CU).  Here waves 4..7 prepare chunk c + 1 while waves 0..3 (each owning 32
 // state rows, as before) run the state work of chunk c; K, Q, P, T' and the
 // row factors are double-buffered by chunk parity.  Each SIMD holds one wave
 // of each role, so one role's MFMA and LDS latencies overlap the other's work.
-// One iteration has five barrier intervals:
-//
-//   interval  preparation (chunk c + 1)          state work (chunk c)
-//   1         Gram tiles, norms                  K S~^T, S~ Q^T
-//   2         A (fp32) and P, row factors        V staging, Z', Vnew, ub, output products
-//   3         diagonal inverses                  output staging and stores, state update
-//   4         16 -> 32 merges; K, Q of chunk     (V of chunk c + 1 in flight)
-//             c + 2 and its gate rows staged
-//   5         32 -> 64 merge                     -
+// The iteration's five barrier intervals and what fills them are listed at the
+// role loops below; one iteration takes ~9.8 K cycles (measured per interval
+// with s_memtime), bound by the preparation's chain of five dependent steps.
 //
 // 147.5 KB of LDS, so one workgroup per CU: chosen when the launch has at most
 // one work item per CU.  With more, two four-wave workgroups per CU overlap
 // in the same way and the part runs at its power limit, where the extra LDS
-// reads of the unfused Gram pass would cost.  bf16 q/k/v only, no checkpoints,
-// not in the split path's map modes.
+// reads of the separate Gram pass would cost.  bf16 q/k/v only, no
+// checkpoints, not in the split path's map modes.
 #include <hip/hip_runtime.h>
 
 #include "gdn_device.h"
