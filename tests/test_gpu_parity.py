@@ -94,6 +94,18 @@ def test_no_states(gdn):
     check(gdn, w, BF16_TOL, True)
 
 
+@pytest.mark.parametrize("gate", ["sigmoid", "long"])
+def test_bf16_states_few_items(gdn, gate):
+    """bf16 initial and final states on a launch with fewer work items than CUs
+    (the pipelined scan), ragged lengths with an empty sequence; the empty one
+    passes its bf16 state through bitwise."""
+    w = W.build([200, 0, 64, 1, 333], 2, 4, torch.bfloat16, seed=12, gate=gate, state_in=torch.bfloat16,
+                state_out=torch.bfloat16, name="bf16_states_small")
+    check(gdn, w, BF16_TOL, True)
+    _, fin = run_gpu(gdn, w, False)
+    assert torch.equal(fin[1].cpu(), w.initial_state[1])
+
+
 def test_all_empty_batch(gdn):
     w = W.build([0, 0, 0], 2, 4, torch.bfloat16, seed=11, name="all_empty")
     out, fin = run_gpu(gdn, w, True)
