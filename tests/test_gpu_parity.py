@@ -106,6 +106,22 @@ def test_bf16_states_few_items(gdn, gate):
     assert torch.equal(fin[1].cpu(), w.initial_state[1])
 
 
+@pytest.mark.parametrize("many", [False, True])
+def test_prenormalized_bf16_without_kernel_norm(gdn, many):
+    """bf16 q/k normalised on the host, use_qk_l2norm off (row factors 1): a
+    launch below one work item per CU (pipelined scan) and one above it
+    (four-wave scan)."""
+    if many:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        gen = torch.Generator().manual_seed(13)
+        lens = torch.randint(1, 200, (cus // 4 + 5,), generator=gen).tolist()
+    else:
+        lens = [300, 17, 128]
+    w = W.build(lens, 2, 4, torch.bfloat16, seed=14, gate="long", use_qk_l2norm=False, prenormalize=True,
+                name="prenorm_bf16")
+    check(gdn, w, BF16_TOL, True)
+
+
 def test_all_empty_batch(gdn):
     w = W.build([0, 0, 0], 2, 4, torch.bfloat16, seed=11, name="all_empty")
     out, fin = run_gpu(gdn, w, True)
