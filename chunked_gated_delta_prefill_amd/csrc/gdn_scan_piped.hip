@@ -145,9 +145,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     //   2         output products and staging (c)         diagonal inverses (c + 1)
     //   3         output stores, state update (c);        16 -> 32 merges (c + 1); gate rows of c + 2
     //             V loads of chunk c + 1
-    //   4         K S~^T, S~ Q^T of chunk c + 1 (first    32 -> 64 merge (c + 1); K, Q of c + 2 staged
-    //             half of the contraction)
-    //   5         the second half                         Gram tiles and norms of chunk c + 2
+    //   4         K S~^T, S~ Q^T of chunk c + 1           32 -> 64 merge (c + 1); K, Q of c + 2 staged
+    //   5         -                                       Gram tiles and norms of chunk c + 2
     // sigma: scale of the true state (sigma S~) at the start of the wave's chunk;
     // the preparation waves track it one chunk ahead with the same arithmetic.
     if (is_state) {
