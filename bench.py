@@ -505,6 +505,8 @@ def main():
                                             bool(ck_every)),
                      "algorithmic_bytes": byts, "algorithmic_flops": flops},
         "cpu_baseline": None,
+        # the realised sequence boundaries of the seeded workload
+        "cu_seqlens": [int(x) for x in w.cu_seqlens.cpu().tolist()],
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs)

@@ -1,0 +1,62 @@
+"""Host-side pieces of bench.py (no GPU): the plan mirror that names the
+kernels a prefill call launches, and the one-GPU guard."""
+import os
+import subprocess
+import sys
+
+import torch
+
+from types import SimpleNamespace
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _shape(lengths, Hv, dtype=torch.bfloat16):
+    """What the plan reads: N, T, Hv and the q dtype (no data generated)."""
+    return SimpleNamespace(N=len(lengths), T=sum(lengths), Hv=Hv, q=torch.empty(0, dtype=dtype))
+
+
+# sequence lengths of the five workloads (the varlen and many-short ones only
+# need their count and total here)
+SHAPES = {
+    "tiny_fp32": _shape([37, 91], 2, torch.float32),
+    "varlen_bf16": _shape([1904] * 7 + [1902], 32),
+    "long_single": _shape([65536], 32),
+    "many_short": _shape([126] * 256, 32),
+    "large_batch": _shape([8192] * 32, 32),
+}
+
+
+def test_scan_kernel_labels_of_the_five_workloads():
+    cus = 256
+    expect = {   # (batch_invariant 0, batch_invariant 1)
+        "tiny_fp32": ("fused_scan_kernel", "fused_scan_kernel"),        # fp32 q/k/v
+        "varlen_bf16": ("piped_scan_kernel", "piped_scan_kernel"),      # 256 work items <= CUs
+        "many_short": ("fused_scan_kernel", "fused_scan_kernel"),       # 8192 work items
+        "large_batch": ("fused_scan_kernel", "fused_scan_kernel"),      # 1024 work items
+    }
+    for name, (k0, k1) in expect.items():
+        w = SHAPES[name]
+        assert bench.scan_kernels(w, 0, cus) == k0, name
+        assert bench.scan_kernels(w, 1, cus) == k1, name
+    w = SHAPES["long_single"]
+    assert bench.scan_kernels(w, 0, cus).startswith("split")           # one sequence on 32 heads
+    assert bench.scan_kernels(w, 1, cus) == "piped_scan_kernel"
+    assert bench.scan_kernels(w, 1, cus, checkpoints=True) == "fused_scan_kernel"
+
+
+def test_split_cost_model_keeps_eight_long_sequences_unsplit():
+    """8 x 8192 tokens on 32 heads: two segments per sequence would cost two maps
+    and a scan at two workgroups per CU, more than the unsplit scan."""
+    assert bench.scan_kernels(_shape([8192] * 8, 32), 0, 256) == "piped_scan_kernel"
+    w = _shape([32768] * 2, 32)
+    assert bench.scan_kernels(w, 0, 256).startswith("split")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
