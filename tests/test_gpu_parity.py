@@ -64,6 +64,17 @@ def test_large_batch_sampled(gdn, bi):
     _sampled(gdn, w, [(0, [0, 1]), (17, [12, 30]), (31, [31])], bi)
 
 
+@pytest.mark.parametrize("lengths,label", [([8192] * 34, "four-wave"), ([34816] * 8, "pipelined")])
+def test_offsets_beyond_2gib_sampled(gdn, lengths, label):
+    """278,528 tokens: the v and out rows of the last sequences (Hv 32, bf16,
+    8 KB per token) lie beyond 2^31 bytes from the buffer start, on both scan
+    kernels (1088 work items, and 256 = one per CU)."""
+    w = W.build(lengths, 16, 32, torch.bfloat16, seed=71, device="cuda", name=f"beyond_2gib_{label}")
+    assert (w.T - 1) * w.Hv * 128 * 2 >= 2 ** 31
+    last = len(lengths) - 1
+    _sampled(gdn, w, [(last, [0, 31]), (last - 1, [15])], True)
+
+
 @pytest.mark.parametrize("lengths", [[1], [63], [64], [65], [1, 127, 128, 129, 0, 200]])
 def test_ragged_lengths(gdn, lengths):
     w = W.build(lengths, 2, 4, torch.bfloat16, seed=7, gate="long", name=f"ragged{lengths}")
