@@ -201,6 +201,11 @@ constexpr int kRowsTotal = NROWF + kGateRows;
 constexpr int kGateWave = 2;                  // the wave that loads and converts the gates
 constexpr float kFastDecay = -60.f;   // G_L above this: exp(G_i - G_j) = gamma_i / gamma_j is safe
 constexpr float kRenorm = 0x1p-40f;   // sigma below this is folded back into the state
+// A chunk takes the shared-Vnew (fast) path only when its lazy scale after the
+// chunk, sigma' = sigma gamma_L, is at least this: a renormalising chunk scales
+// its P tile by 1 / sigma', which must stay far from the bf16 and fp32 limits
+// (sigma' can reach 2^-40 e^-60 when sigma sits at the threshold).
+constexpr float kFastMinScale = 0x1p-100f;
 
 
 // Element e of each lane quad, broadcast to the quad (DPP quad_perm [e, e, e, e]).

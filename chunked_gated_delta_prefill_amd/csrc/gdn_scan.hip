@@ -240,7 +240,8 @@ fused_scan_kernel(const ScanParams p) {
         const float sig_next = sigma * gLc;
         const bool renorm = !(sig_next >= kRenorm);
         const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                              int, rf(RG_)[C - 1]))) > kFastDecay;
+                              int, rf(RG_)[C - 1]))) > kFastDecay &&
+                          sig_next >= kFastMinScale;
         // Gram tiles (bi, bj) = (0,0) (1,0) (1,1) of K K^T ("A" tiles) and Q K^T ("P"
         // tiles), each computed transposed: register rows are the column index
         // j = 32 bj + acc_row, the lane is the row index i = 32 bi + l32.

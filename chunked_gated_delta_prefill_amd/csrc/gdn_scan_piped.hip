@@ -191,7 +191,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const float sig_next = sigma * gLc;
             const bool renorm = !(sig_next >= kRenorm);
             const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                                  int, rf(RG_)[C - 1]))) > kFastDecay;
+                                  int, rf(RG_)[C - 1]))) > kFastDecay &&
+                          sig_next >= kFastMinScale;
             const ChunkRef ch = chunk_at(bos, eos, c);
             const int Lc = ch.L;
             const bf16 *Ks = kbuf(c);
@@ -471,7 +472,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const float sig_next = sigma * gLc;
             const bool renorm = !(sig_next >= kRenorm);
             const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                                  int, rf(RG_)[C - 1]))) > kFastDecay;
+                                  int, rf(RG_)[C - 1]))) > kFastDecay &&
+                          sig_next >= kFastMinScale;
             bf16 *Ts = tbuf(x);
 
             // ---- interval 1: A (fp32) and P of chunk x from the Gram tiles, row

@@ -194,6 +194,31 @@ def test_decay_regime_alternating_by_chunk(gdn, lengths, bi):
     assert nerr(out, ro) <= BF16_TOL and nerr(fin, rf) <= BF16_TOL
 
 
+@pytest.mark.parametrize("bi", [True, False])
+def test_renorm_chunk_with_extreme_decay(gdn, bi):
+    """Chunk 0 leaves the lazy decay scale just above the renormalisation
+    threshold (log-decay -27.5 over the chunk, sigma ~1.1e-12 > 2^-40); chunk 1
+    has a log-decay of -59, still above the entry-wise exp limit of -60, so the
+    chunk renormalises with sigma' = sigma gamma_L ~ 3e-38.  Factors of 1 / sigma'
+    must not reach the output products (they would overflow bf16 and fp32).
+    Raw q/k with the in-kernel norm, so q.k is not bounded by 1."""
+    w = _w(lengths=(300, 64 * 3 + 5), Hqk=2, Hv=4, seed=37)
+    t = torch.arange(w.T)
+    starts = w.cu_seqlens.to(torch.int64)
+    seq = torch.searchsorted(starts[1:], t, right=True)
+    chunk = ((t - starts[seq]) // 64).unsqueeze(1)
+    g = torch.where(chunk == 0, torch.full_like(w.g, float(np.exp(-27.5 / 64))),
+                    torch.where(chunk == 1, torch.full_like(w.g, float(np.exp(-59.0 / 64))), w.g))
+    w = W.Workload(**{**w.__dict__, "g": g})
+    say(f"[gpu] renormalising chunk with log-decay -59 after -27.5, batch_invariant={bi}")
+    out, fin = run_gpu(gdn, w, bi)
+    assert torch.isfinite(out).all() and torch.isfinite(fin).all()
+    ro, rf = run_oracle(w)
+    e1, e2 = nerr(out, ro), nerr(fin, rf)
+    say(f"      out {e1:.3e} state {e2:.3e}")
+    assert e1 <= BF16_TOL and e2 <= BF16_TOL
+
+
 def test_bf16_gates_and_fp16_gate(gdn):
     w = _w(seed=29)
     say("[gpu] gate dtypes")
