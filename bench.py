@@ -63,27 +63,12 @@ def algorithmic(w):
 
 
 def scan_kernels(w, batch_invariant, cus, checkpoints=False):
-    """Kernels one prefill call launches: the host plan of gdn_api.hip (split
-    path when its cost model favours it, else one scan launch: the eight-wave
-    pipelined scan for bf16 with at most one work item per CU)."""
-    import torch
-    N, T, Hv = w.N, w.T, w.Hv
-    fill, lseg = 2 * cus, 0
-    if not batch_invariant and N * Hv < fill and T > 0 and T >= 4 * 1024 * N:
-        lseg = max(1024, -(-(-(-T * Hv // fill)) // 64) * 64)
-        if lseg >= T:
-            lseg = 0
-    if lseg:
-        per_chunk = lambda items: 1.0 if items <= cus else 1.6 * (-(-items // fill))
-        avg = -(-T // N)
-        P = -(-avg // lseg)
-        unsplit = -(-avg // 64) * per_chunk(N * Hv)
-        split = lseg // 64 * (2 * per_chunk(N * (P - 1) * Hv) + per_chunk(N * P * Hv)) + P
-        if split < unsplit:
-            return "split: plan_kernel, fused_scan_kernel (maps N, M), fixup_kernel, fused_scan_kernel"
-    if w.q.dtype == torch.bfloat16 and not checkpoints and N * Hv <= cus:
-        return "piped_scan_kernel"
-    return KERNEL
+    """Kernels one prefill call launches, from the library's own host plan
+    (gdn_prefill_plan, no device needed)."""
+    import chunked_gated_delta_prefill_amd as gdn
+    kind, _ = gdn.prefill_plan(w.N, w.T, w.Hv, w.q.dtype, checkpoints, batch_invariant, cus)
+    return {"scan": KERNEL, "pipelined_scan": "piped_scan_kernel",
+            "split": "split: plan_kernel, fused_scan_kernel (maps N, M), fixup_kernel, fused_scan_kernel"}[kind]
 
 
 def kernel_source_sha(srcs=None):

@@ -79,6 +79,10 @@ def load():
         lib.gdn_last_error.restype = ctypes.c_char_p
         lib.gdn_release_workspace.argtypes = []
         lib.gdn_release_workspace.restype = None
+        lib.gdn_prefill_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                         ctypes.POINTER(ctypes.c_int64)]
+        lib.gdn_prefill_plan.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -225,6 +229,22 @@ def gdn_decode_step_pooled(q, k, v, g, beta, scale, state_pool, state_indices, u
                                      describe(state_indices), use_qk_l2norm, describe(out), stream)
     if rc != 0:
         raise GdnError(rc, msg)
+
+
+PLAN_NAMES = {0: "scan", 1: "pipelined_scan", 2: "split"}
+
+
+def prefill_plan(num_seqs, num_tokens, num_v_heads, io_dtype, checkpoints, batch_invariant, num_cus):
+    """gdn_prefill_plan: (plan name, segment length) of a prefill call with these
+    sizes on a device with num_cus CUs (host only, no device needed)."""
+    lib = load()
+    kind, seg = ctypes.c_int(-1), ctypes.c_int64(-1)
+    rc = lib.gdn_prefill_plan(int(num_seqs), int(num_tokens), int(num_v_heads), _dtype_code(io_dtype),
+                              int(bool(checkpoints)), int(bool(batch_invariant)), int(num_cus), ctypes.byref(kind),
+                              ctypes.byref(seg))
+    if rc != 0:
+        raise RuntimeError(f"gdn_prefill_plan failed ({rc}): {(lib.gdn_last_error() or b'').decode()}")
+    return PLAN_NAMES[kind.value], seg.value
 
 
 def release_workspace():

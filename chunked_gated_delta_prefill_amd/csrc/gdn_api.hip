@@ -190,6 +190,55 @@ extern "C" void gdn_release_workspace(void) {
 
 namespace {
 
+// The host plan of one prefill call, from host-known sizes only (no device
+// reads, so a call stays graph-capturable).
+struct Plan {
+    int kind;       // enum gdn_plan_kind
+    int64_t lseg;   // segment length of the split path (0 without a split)
+};
+Plan make_plan(int64_t N, int64_t T, int64_t Hv, bool bf, bool ck, bool batch_invariant, int cus) {
+    // Split path (T precompute -> MN precompute -> state fix-up -> CP prefill) when
+    // one work item per (sequence, head) leaves the GPU under-filled and the
+    // sequences are long on average.  A split sequence runs three passes over each
+    // segment (two maps, then the scan) plus one fix-up step per segment boundary,
+    // and the split multiplies the work items, which may push a launch from one
+    // to two workgroups per CU.  The two plans are compared in units of one chunk
+    // at one workgroup per CU: a launch of W items costs one unit per chunk while
+    // W <= CUs and 1.6 per round of two workgroups per CU above that (measured:
+    // 5.0 and 7.9 us per chunk), a fix-up step and the extra launches about one
+    // unit per segment.  Measured on 8 sequences of 8192 tokens (32 heads): the
+    // fixed rule used before split them into 2 segments, 1.10 ms against 0.64 ms
+    // unsplit.  Never with batch_invariant (the split changes the reduction order
+    // of a sequence).  The host knows only T and N, so the plan uses the average
+    // sequence length.
+    const int64_t fill = 2 * (int64_t)cus;
+    int64_t lseg = 0;
+    if (!batch_invariant && N * Hv < fill && T > 0 && T >= 4 * kMinSegment * N) {
+        lseg = (T * Hv + fill - 1) / fill;
+        lseg = (lseg + gdn::kChunk - 1) / gdn::kChunk * gdn::kChunk;
+        if (lseg < kMinSegment) lseg = kMinSegment;
+        if (lseg >= T) lseg = 0;   // no sequence is long enough to split
+    }
+    if (lseg > 0) {
+        auto per_chunk = [&](int64_t items) {
+            return items <= cus ? 1.0 : 1.6 * (double)((items + fill - 1) / fill);
+        };
+        const int64_t avg = (T + N - 1) / N;
+        const int64_t P = (avg + lseg - 1) / lseg;
+        const double unsplit = (double)((avg + gdn::kChunk - 1) / gdn::kChunk) * per_chunk(N * Hv);
+        const double split = (double)(lseg / gdn::kChunk) *
+                                 (2.0 * per_chunk(N * (P - 1) * Hv) + per_chunk(N * P * Hv)) + (double)P;
+        if (!(split < unsplit)) lseg = 0;
+    }
+    if (lseg > 0) return {GDN_PLAN_SPLIT, lseg};
+    // At most one work item per CU: the pipelined eight-wave scan (one workgroup
+    // per CU, preparation of chunk c + 1 beside the state work of chunk c); it
+    // gives bitwise the results of the four-wave scan, so the choice keeps
+    // batch_invariant results independent of the batch.
+    if (bf && !ck && N * Hv <= cus) return {GDN_PLAN_PIPELINED_SCAN, 0};
+    return {GDN_PLAN_SCAN, 0};
+}
+
 int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, const gdn_tensor *g,
                  const gdn_tensor *beta, float scale, const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
                  const gdn_tensor *output_state, int use_qk_l2norm, int batch_invariant, const gdn_tensor *ckpt,
@@ -380,46 +429,11 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     const bool bf = io == GDN_BF16;
     hipStream_t hs = static_cast<hipStream_t>(stream);
 
-    // Split path (T precompute -> MN precompute -> state fix-up -> CP prefill) when
-    // one work item per (sequence, head) leaves the GPU under-filled and the
-    // sequences are long on average.  A split sequence runs three passes over each
-    // segment (two maps, then the scan) plus one fix-up step per segment boundary,
-    // and the split multiplies the work items, which may push a launch from one
-    // to two workgroups per CU.  The two plans are compared in units of one chunk
-    // at one workgroup per CU: a launch of W items costs one unit per chunk while
-    // W <= CUs and 1.6 per round of two workgroups per CU above that (measured:
-    // 5.0 and 7.9 us per chunk), a fix-up step and the extra launches about one
-    // unit per segment.  Measured on 8 sequences of 8192 tokens (32 heads): the
-    // fixed rule used before split them into 2 segments, 1.10 ms against 0.64 ms
-    // unsplit.  Never with batch_invariant (the split changes the reduction order
-    // of a sequence).  The host knows only T and N, so the plan uses the average
-    // sequence length.
-    const int64_t fill = 2 * (int64_t)cus;
-    int64_t lseg = 0;
-    if (!batch_invariant && N * Hv < fill && T > 0 && T >= 4 * kMinSegment * N) {
-        lseg = (T * Hv + fill - 1) / fill;
-        lseg = (lseg + gdn::kChunk - 1) / gdn::kChunk * gdn::kChunk;
-        if (lseg < kMinSegment) lseg = kMinSegment;
-        if (lseg >= T) lseg = 0;   // no sequence is long enough to split
-    }
-    if (lseg > 0) {
-        auto per_chunk = [&](int64_t items) {
-            return items <= cus ? 1.0 : 1.6 * (double)((items + fill - 1) / fill);
-        };
-        const int64_t avg = (T + N - 1) / N;
-        const int64_t P = (avg + lseg - 1) / lseg;
-        const double unsplit = (double)((avg + gdn::kChunk - 1) / gdn::kChunk) * per_chunk(N * Hv);
-        const double split = (double)(lseg / gdn::kChunk) *
-                                 (2.0 * per_chunk(N * (P - 1) * Hv) + per_chunk(N * P * Hv)) + (double)P;
-        if (!(split < unsplit)) lseg = 0;
-    }
+    const Plan plan = make_plan(N, T, Hv, bf, p.ck != nullptr, batch_invariant != 0, cus);
+    const int64_t lseg = plan.lseg;
     hipError_t e;
     if (lseg == 0) {
-        // At most one work item per CU: the pipelined eight-wave scan (one
-        // workgroup per CU, preparation of chunk c + 1 beside the state work of
-        // chunk c); it gives bitwise the results of the four-wave scan, so the
-        // choice keeps batch_invariant results independent of the batch.
-        if (bf && !p.ck && N * Hv <= cus) e = gdn::launch_piped_scan(p, hs);
+        if (plan.kind == GDN_PLAN_PIPELINED_SCAN) e = gdn::launch_piped_scan(p, hs);
         else e = gdn::launch_fused_scan(p, bf, gdn::kScan, hs);
         if (e != hipSuccess) return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
         return GDN_OK;
@@ -634,4 +648,23 @@ extern "C" int gdn_decode_step_pooled(const gdn_tensor *q, const gdn_tensor *k, 
         return GDN_ERR_INVALID_ARGUMENT;
     }
     return decode_impl(q, k, v, g, beta, scale, state_pool, state_pool, state_indices, use_qk_l2norm, out, stream);
+}
+
+extern "C" int gdn_prefill_plan(int64_t num_seqs, int64_t num_tokens, int64_t num_v_heads, int io_dtype,
+                                int checkpoints, int batch_invariant, int num_cus, int *kind,
+                                int64_t *segment_length) {
+    if (!kind || !segment_length) {
+        g_last_error = "kind and segment_length are required";
+        return GDN_ERR_INVALID_ARGUMENT;
+    }
+    if (num_seqs < 0 || num_tokens < 0 || num_v_heads < 1 || num_cus < 1 ||
+        (io_dtype != GDN_F32 && io_dtype != GDN_BF16)) {
+        g_last_error = "invalid sizes or dtype";
+        return GDN_ERR_INVALID_ARGUMENT;
+    }
+    const Plan plan = make_plan(num_seqs, num_tokens, num_v_heads, io_dtype == GDN_BF16, checkpoints != 0,
+                                batch_invariant != 0, num_cus);
+    *kind = plan.kind;
+    *segment_length = plan.lseg;
+    return GDN_OK;
 }

@@ -211,6 +211,32 @@ int gdn_decode_step_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_t
                            const gdn_tensor *state_pool, const gdn_tensor *state_indices,
                            int use_qk_l2norm, const gdn_tensor *out, void *stream);
 
+/* What a gdn_chunk_prefill call (or its checkpointed and pooled forms) runs,
+ * decided on the host from host-known sizes only (the "split/segment plan" of
+ * "flashinfer.gdn_prefill", Cake GDN CP context-parallel backend: T precompute
+ * -> MN precompute -> state fixup -> CP prefill, taken here only when splitting
+ * few long sequences pays off, and never with batch_invariant).
+ *   GDN_PLAN_SCAN            one launch of the four-wave fused scan
+ *   GDN_PLAN_PIPELINED_SCAN  one launch of the eight-wave pipelined scan (bf16,
+ *                            no checkpoints, at most one work item per CU);
+ *                            bitwise the results of GDN_PLAN_SCAN
+ *   GDN_PLAN_SPLIT           segment table, the two segment maps, the state
+ *                            fix-up and the per-segment scan, with segments
+ *                            of *segment_length tokens
+ */
+enum gdn_plan_kind { GDN_PLAN_SCAN = 0, GDN_PLAN_PIPELINED_SCAN = 1, GDN_PLAN_SPLIT = 2 };
+
+/* The plan for num_seqs sequences of num_tokens tokens in total, num_v_heads
+ * value heads, q/k/v of io_dtype (GDN_F32 or GDN_BF16), with or without
+ * checkpoints, on a device with num_cus compute units.  A pure host function
+ * (no device needed).  Writes *kind (enum gdn_plan_kind) and *segment_length
+ * (0 unless GDN_PLAN_SPLIT).  Returns GDN_OK, or GDN_ERR_INVALID_ARGUMENT for
+ * NULL outputs, negative sizes, num_v_heads or num_cus below 1, or another
+ * dtype. */
+int gdn_prefill_plan(int64_t num_seqs, int64_t num_tokens, int64_t num_v_heads, int io_dtype,
+                     int checkpoints, int batch_invariant, int num_cus, int *kind,
+                     int64_t *segment_length);
+
 /* Message for the last non-zero return of a gdn_* call on this thread
  * ("" if none).  The pointer stays valid until the next call on the thread. */
 const char *gdn_last_error(void);

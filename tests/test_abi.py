@@ -26,7 +26,8 @@ def _declared_functions():
 def test_exports_every_declared_function():
     names = _declared_functions()
     assert names == ["gdn_chunk_prefill", "gdn_chunk_prefill_checkpointed", "gdn_chunk_prefill_pooled",
-                     "gdn_decode_step", "gdn_decode_step_pooled", "gdn_last_error", "gdn_release_workspace"]
+                     "gdn_decode_step", "gdn_decode_step_pooled", "gdn_last_error", "gdn_prefill_plan",
+                     "gdn_release_workspace"]
     L = lib.load()
     for n in names:
         assert hasattr(L, n), n

@@ -1,0 +1,53 @@
+"""The library's host plan (gdn_prefill_plan, no GPU): which kernels a prefill
+call runs for the five workloads and around the thresholds of the split cost
+model and the pipelined scan."""
+import pytest
+import torch
+
+import chunked_gated_delta_prefill_amd as gdn
+
+BF, F32 = torch.bfloat16, torch.float32
+
+
+def plan(N, T, Hv, dt=BF, ck=False, bi=False, cus=256):
+    return gdn.prefill_plan(N, T, Hv, dt, ck, bi, cus)
+
+
+def test_the_five_workloads():
+    assert plan(2, 128, 2, F32) == ("scan", 0)                      # fp32 q/k/v: four-wave scan
+    assert plan(8, 15230, 32) == ("pipelined_scan", 0)              # 256 work items = CUs
+    assert plan(1, 65536, 32) == ("split", 4096)                    # one long sequence: 16 segments
+    assert plan(1, 65536, 32, bi=True) == ("pipelined_scan", 0)     # batch_invariant: never split
+    assert plan(256, 32280, 32) == ("scan", 0)                      # 8192 work items
+    assert plan(32, 262144, 32) == ("scan", 0)                      # the 32 x 8192 batch
+
+
+def test_split_cost_model():
+    # 8 x 8192 on 32 heads: two segments per sequence cost more than the unsplit scan
+    assert plan(8, 8 * 8192, 32)[0] == "pipelined_scan"
+    # 4 x 16384: four segments, the maps and the scan at two workgroups per CU: still unsplit
+    assert plan(4, 4 * 16384, 32)[0] == "pipelined_scan"
+    # 2 x 32768: eight segments pay off
+    assert plan(2, 2 * 32768, 32) == ("split", 4096)
+    # an average below four shortest segments is never split
+    assert plan(1, 4 * 1024 - 64, 4)[0] == "pipelined_scan"
+    assert plan(1, 4 * 1024, 4) == ("split", 1024)
+
+
+def test_pipelined_scan_threshold_and_exclusions():
+    assert plan(64, 64 * 100, 4)[0] == "pipelined_scan"             # 256 work items
+    assert plan(65, 65 * 100, 4)[0] == "scan"                       # 260 work items
+    assert plan(64, 64 * 100, 4, cus=128)[0] == "scan"              # fewer CUs
+    assert plan(8, 800, 4, dt=F32)[0] == "scan"                     # fp32 q/k/v
+    assert plan(8, 800, 4, ck=True)[0] == "scan"                    # checkpoints
+    assert plan(0, 0, 4) == ("pipelined_scan", 0)                   # empty batch: no work items
+
+
+@pytest.mark.parametrize("args", [(-1, 0, 4), (1, -1, 4), (1, 64, 0)])
+def test_invalid_sizes_are_rejected(args):
+    with pytest.raises(RuntimeError):
+        gdn.prefill_plan(*args, BF, False, False, 256)
+    with pytest.raises(RuntimeError):
+        gdn.prefill_plan(1, 64, 4, torch.float16, False, False, 256)
+    with pytest.raises(RuntimeError):
+        gdn.prefill_plan(1, 64, 4, BF, False, False, 0)
