@@ -213,7 +213,7 @@ Plan make_plan(int64_t N, int64_t T, int64_t Hv, bool bf, bool ck, bool batch_in
     // sequence length.
     const int64_t fill = 2 * (int64_t)cus;
     int64_t lseg = 0;
-    if (!batch_invariant && N * Hv < fill && T > 0 && T >= 4 * kMinSegment * N) {
+    if (!batch_invariant && N > 0 && N * Hv < fill && T > 0 && T >= 4 * kMinSegment * N) {
         lseg = (T * Hv + fill - 1) / fill;
         lseg = (lseg + gdn::kChunk - 1) / gdn::kChunk * gdn::kChunk;
         if (lseg < kMinSegment) lseg = kMinSegment;

@@ -41,6 +41,7 @@ def test_pipelined_scan_threshold_and_exclusions():
     assert plan(8, 800, 4, dt=F32)[0] == "scan"                     # fp32 q/k/v
     assert plan(8, 800, 4, ck=True)[0] == "scan"                    # checkpoints
     assert plan(0, 0, 4) == ("pipelined_scan", 0)                   # empty batch: no work items
+    assert plan(0, 100000, 4) == ("pipelined_scan", 0)              # no sequences: never split
 
 
 @pytest.mark.parametrize("args", [(-1, 0, 4), (1, -1, 4), (1, 64, 0)])
