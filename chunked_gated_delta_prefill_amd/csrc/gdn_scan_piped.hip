@@ -566,7 +566,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     p_tile(X[1], 1, 0);
                 }
                 if (pw == 1) p_tile(X[1], 1, 1);
-                if (pw == 0) {   // row factors of the state work, lane = token
+                if (pw == 3) {   // row factors of the state work (the wave with no A tile), lane = token
                     const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
                     rf(FZ_)[lane] = sigma * gam * rk;
                     rf(FU_)[lane] = renorm ? rk * dec : rk * dec / sig_next;
