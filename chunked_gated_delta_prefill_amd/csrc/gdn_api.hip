@@ -14,6 +14,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -87,6 +88,27 @@ bool aligned16(const void *p, size_t esz, const int64_t *strides, int n) {
     return true;
 }
 
+// No two elements of a written tensor share an address: its dims, taken in
+// order of increasing stride (size-1 dims skipped), each start past the whole
+// extent of the dims before them.
+bool no_self_overlap(const gdn_tensor *t) {
+    int order[4];
+    int n = 0;
+    for (int i = 0; i < t->ndim; ++i) {
+        if (t->sizes[i] == 0) return true;   // no elements
+        if (t->sizes[i] > 1) order[n++] = i;
+    }
+    for (int a = 1; a < n; ++a)   // insertion sort by stride
+        for (int b = a; b > 0 && t->strides[order[b]] < t->strides[order[b - 1]]; --b) std::swap(order[b], order[b - 1]);
+    int64_t extent = 1;   // elements spanned by the dims taken so far
+    for (int a = 0; a < n; ++a) {
+        const int d = order[a];
+        if (t->strides[d] < extent) return false;
+        extent = t->strides[d] * (t->sizes[d] - 1) + extent;
+    }
+    return true;
+}
+
 constexpr int64_t kMinSegment = 1024;   // shortest segment of the split path (16 chunks)
 
 std::mutex g_dev_mu;
@@ -131,36 +153,50 @@ int check_device(std::string &msg, int *dev_out, int *cus_out) {
     return GDN_OK;
 }
 
-// Workspace of the split path: cached per (device, stream), grown on demand.
-// Growing synchronises the stream once (the old buffer may still be in use);
-// after a warm-up call of the largest shape no call allocates.
+// Workspace of the split path: cached per (device, stream), grown on demand
+// (the cached shape-specific workspace of "flashinfer.gdn_prefill", Cake GDN CP
+// section).  A superseded buffer is never freed while the library may still
+// use it: work enqueued earlier on the stream, or a HIP graph captured from an
+// earlier call, keeps its address in kernel arguments.  Superseded buffers are
+// kept on a retired list until gdn_release_workspace.  Growth is refused while
+// the stream is capturing (an allocation is not capturable): an eager call of
+// the largest shape on the stream sizes the workspace first.  Growth rounds up
+// by half again, so a run of slowly growing calls retires few buffers.
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<int, void *>> g_ws_retired;   // (device, buffer)
 
 int get_workspace(int dev, hipStream_t st, size_t need, void **out, std::string &msg) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     Workspace &w = g_ws[{dev, st}];
     if (w.bytes < need) {
-        if (w.ptr) {
-            if (hipStreamSynchronize(st) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
-                (void)hipGetLastError();
-                msg = "workspace release failed";
-                return GDN_ERR_HIP;
-            }
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        if (hipMalloc(&w.ptr, need) != hipSuccess) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
             (void)hipGetLastError();
-            w.ptr = nullptr;
-            msg = "workspace allocation of " + std::to_string(need) + " bytes failed";
+            msg = "hipStreamIsCapturing failed";
             return GDN_ERR_HIP;
         }
-        w.bytes = need;
+        if (cs != hipStreamCaptureStatusNone) {
+            msg = "the split path needs " + std::to_string(need) + " bytes of workspace on this stream but has " +
+                  std::to_string(w.bytes) + "; it cannot grow during graph capture (run one eager call of the "
+                  "largest shape on the capture stream first)";
+            return GDN_ERR_UNSUPPORTED;
+        }
+        const size_t grow = w.bytes + w.bytes / 2;
+        const size_t bytes = need > grow ? need : grow;
+        void *fresh = nullptr;
+        if (hipMalloc(&fresh, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            msg = "workspace allocation of " + std::to_string(bytes) + " bytes failed";
+            return GDN_ERR_HIP;
+        }
+        if (w.ptr) g_ws_retired.push_back({dev, w.ptr});
+        w.ptr = fresh;
+        w.bytes = bytes;
     }
     *out = w.ptr;
     return GDN_OK;
@@ -174,17 +210,22 @@ extern "C" const char *gdn_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" void gdn_release_workspace(void) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
     for (auto &kv : g_ws) {
         if (kv.second.ptr) {
-            int cur = 0;
-            (void)hipGetDevice(&cur);
             (void)hipSetDevice(kv.first.first);
             (void)hipStreamSynchronize(kv.first.second);
             (void)hipFree(kv.second.ptr);
-            (void)hipSetDevice(cur);
         }
     }
+    for (auto &r : g_ws_retired) {   // their users were enqueued before the current buffers' users
+        (void)hipSetDevice(r.first);
+        (void)hipFree(r.second);
+    }
+    (void)hipSetDevice(cur);
     g_ws.clear();
+    g_ws_retired.clear();
     (void)hipGetLastError();
 }
 
@@ -279,6 +320,11 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     const size_t esz = dt_size(io);
     if (T > 0 && (!aligned16(q->data, esz, q->strides, 2) || !aligned16(k->data, esz, k->strides, 2)))
         return fail(GDN_ERR_UNSUPPORTED, "q and k rows must be 16-byte aligned (pointer and token/head strides)");
+    // v rows are read and out rows written in 16-byte pieces
+    if (T > 0 && (!aligned16(v->data, esz, v->strides, 2) || !aligned16(out->data, esz, out->strides, 2)))
+        return fail(GDN_ERR_UNSUPPORTED, "v and out rows must be 16-byte aligned (pointer and token/head strides)");
+    if (!no_self_overlap(out))
+        return fail(GDN_ERR_UNSUPPORTED, "out must not overlap itself (e.g. a head stride below 128 elements)");
 
     // Per-row offsets inside one 64-token chunk are 32-bit; rows must not overlap.
     const int64_t kRowLimit = ((int64_t)1 << 31) / (gdn::kChunk + 1);
@@ -342,6 +388,8 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
             return fail(GDN_ERR_UNSUPPORTED, std::string(st_name[i]) +
                                                  ": rows must be 16-byte aligned, >= 128 elements apart (pointer and strides)");
     }
+    if (output_state && !no_self_overlap(output_state))
+        return fail(GDN_ERR_UNSUPPORTED, "output_state must not overlap itself");
     if (!state_indices && initial_state && output_state && initial_state->data == output_state->data && N > 0)
         return fail(GDN_ERR_ALIAS, "output_state must not alias initial_state");
     if (state_indices) {
@@ -368,6 +416,8 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
         if (N > 0 && (!aligned16(ckpt->data, (size_t)se, ckpt->strides, 3) || ckpt->strides[2] < gdn::kHeadDim ||
                       ckpt->strides[2] * se * gdn::kHeadDim >= kRowLimit))
             return fail(GDN_ERR_UNSUPPORTED, "checkpoints: rows must be 16-byte aligned, >= 128 elements apart");
+        if (!no_self_overlap(ckpt))
+            return fail(GDN_ERR_UNSUPPORTED, "checkpoints must not overlap itself");
         if (N > 0 && ((initial_state && ckpt->data == initial_state->data) ||
                       (output_state && ckpt->data == output_state->data)))
             return fail(GDN_ERR_ALIAS, "checkpoints must not alias initial_state or output_state");
@@ -661,6 +711,12 @@ extern "C" int gdn_prefill_plan(int64_t num_seqs, int64_t num_tokens, int64_t nu
         (io_dtype != GDN_F32 && io_dtype != GDN_BF16)) {
         g_last_error = "invalid sizes or dtype";
         return GDN_ERR_INVALID_ARGUMENT;
+    }
+    // the size limits gdn_chunk_prefill applies (a plan only for a call it would accept)
+    if (num_tokens > ((int64_t)1 << 40) || num_v_heads > 65536 || num_seqs > ((int64_t)1 << 24) ||
+        (num_seqs + 8) * num_v_heads > ((int64_t)1 << 30)) {
+        g_last_error = "problem too large";
+        return GDN_ERR_UNSUPPORTED;
     }
     const Plan plan = make_plan(num_seqs, num_tokens, num_v_heads, io_dtype == GDN_BF16, checkpoints != 0,
                                 batch_invariant != 0, num_cus);

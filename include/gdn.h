@@ -36,8 +36,13 @@ enum gdn_dtype {
     GDN_I64 = 4
 };
 
-/* Return codes.  A non-zero code means nothing was enqueued and nothing was
- * written; gdn_last_error() then describes the reason. */
+/* Return codes.  Invalid inputs and unsupported configurations fail closed,
+ * with no fallback to another implementation ("flashinfer.gdn_prefill", Cake
+ * GDN CP context-parallel backend: invalid inputs and unsupported
+ * architectures fail closed); like the engine that declines a graph it cannot
+ * serve while the reason is logged ("flashinfer.cudnn", Linear attention), a
+ * refused call returns a code and gdn_last_error() gives the reason.  A
+ * non-zero code means nothing was enqueued and nothing was written. */
 enum gdn_status {
     GDN_OK = 0,
     GDN_ERR_INVALID_ARGUMENT = 1, /* NULL required tensor, bad ndim/shape/stride/dtype */
@@ -63,8 +68,12 @@ typedef struct gdn_tensor {
  *
  * Argument meanings follow "flashinfer.cudnn.cudnn_chunk_gated_delta_rule",
  * Parameters (T = total tokens, N = sequences, d = 128):
- *   q, k            [T, Hqk, 128], F32 or BF16 (both the same); any
- *                   non-negative token/head strides, innermost contiguous.
+ *   q, k            [T, Hqk, 128], F32 or BF16 (both the same), innermost
+ *                   contiguous.  Token and head strides: non-negative, a
+ *                   multiple of 16 bytes, the token stride at least 128
+ *                   elements and below 32 MiB; data 16-byte aligned (the
+ *                   pages pass any strides through; these limits come from
+ *                   the 16-byte row loads here, GDN_ERR_UNSUPPORTED).
  *   v               [T, Hv, 128], q's dtype, same stride rule; Hv % Hqk == 0.
  *   g               NULL (all ones) or [T, Hv] forget gate in linear space,
  *                   F32, BF16 or F16, innermost stride 1 not required.
@@ -78,7 +87,8 @@ typedef struct gdn_tensor {
  *                   an unchecked precondition (they are never read on the
  *                   host); empty sequences are allowed.
  *   initial_state   NULL (zero state) or [N, Hv, 128, 128] F32 or BF16,
- *                   V-major, innermost (K) stride 1, other strides free.
+ *                   V-major, innermost (K) stride 1; data and the other
+ *                   strides 16-byte aligned, rows at least 128 elements apart.
  *   output_state    NULL (no state written at all) or the same shape, F32 or
  *                   BF16 (each state buffer carries its own dtype; the scan
  *                   accumulates in fp32).  Must not overlap initial_state:
@@ -94,7 +104,10 @@ typedef struct gdn_tensor {
  *                   (segment scan, then a state fix-up), which may change the
  *                   last bits.
  *   out             [T, Hv, 128], q's dtype, written in place (the library
- *                   allocates no output).
+ *                   allocates no output); strides as for q, and no two
+ *                   elements at one address (e.g. a head stride below 128
+ *                   elements is rejected, GDN_ERR_UNSUPPORTED).  Overlap of
+ *                   out with q, k, v, g or beta is an unchecked precondition.
  *   stream          a hipStream_t (NULL = the default stream).  The call is
  *                   asynchronous: it validates on the host, enqueues on
  *                   `stream` and returns without synchronising.
@@ -102,6 +115,14 @@ typedef struct gdn_tensor {
  * Ownership: every tensor is caller-owned device memory; the library writes
  * only `out`, `output_state` and its own workspace (cached per device and
  * stream, grown on demand; see gdn_release_workspace).
+ * Graph capture: a call whose plan (gdn_prefill_plan) is GDN_PLAN_SPLIT uses
+ * the workspace of its stream; after one eager call of the largest shape on
+ * that stream, calls enqueue kernels only and can be captured.  A call that
+ * would grow the workspace while the stream is capturing is refused with
+ * GDN_ERR_UNSUPPORTED.  A captured graph keeps the capture stream's workspace
+ * address: its replays share that memory with eager split calls on the
+ * capture stream, so the two must not run at the same time, and growing the
+ * workspace later keeps the old buffer alive for the graph.
  * Errors: validation happens before any enqueue; an invalid call writes
  * nothing and returns a gdn_status (no fallback path exists).
  */
@@ -230,19 +251,27 @@ enum gdn_plan_kind { GDN_PLAN_SCAN = 0, GDN_PLAN_PIPELINED_SCAN = 1, GDN_PLAN_SP
  * value heads, q/k/v of io_dtype (GDN_F32 or GDN_BF16), with or without
  * checkpoints, on a device with num_cus compute units.  A pure host function
  * (no device needed).  Writes *kind (enum gdn_plan_kind) and *segment_length
- * (0 unless GDN_PLAN_SPLIT).  Returns GDN_OK, or GDN_ERR_INVALID_ARGUMENT for
+ * (0 unless GDN_PLAN_SPLIT).  Returns GDN_OK, GDN_ERR_INVALID_ARGUMENT for
  * NULL outputs, negative sizes, num_v_heads or num_cus below 1, or another
- * dtype. */
+ * dtype, and GDN_ERR_UNSUPPORTED for sizes gdn_chunk_prefill refuses (more
+ * than 2^40 tokens, 65536 value heads or 2^24 sequences, or a grid of
+ * (sequence, value head) work items beyond one launch). */
 int gdn_prefill_plan(int64_t num_seqs, int64_t num_tokens, int64_t num_v_heads, int io_dtype,
                      int checkpoints, int batch_invariant, int num_cus, int *kind,
                      int64_t *segment_length);
 
-/* Message for the last non-zero return of a gdn_* call on this thread
- * ("" if none).  The pointer stays valid until the next call on the thread. */
+/* The reason for the last non-zero return of a gdn_* call on this thread
+ * ("" if none): the counterpart of the per-engine reason that the frontend
+ * logs when an engine declines a graph ("flashinfer.cudnn", Linear attention).
+ * The pointer stays valid until the next call on the thread. */
 const char *gdn_last_error(void);
 
-/* Frees every cached workspace (all devices and streams).  The caller must
- * ensure no enqueued gdn work is still running. */
+/* Frees every cached workspace, current and superseded, on all devices and
+ * streams (the workspace the dispatcher caches with the shape-specific plan,
+ * "flashinfer.gdn_prefill", Cake GDN CP context-parallel backend; nothing is
+ * kept for the process lifetime unless the caller keeps calling).  The caller
+ * must ensure that no enqueued gdn work is still running and that no graph
+ * captured from a split-path call is replayed afterwards. */
 void gdn_release_workspace(void);
 
 #ifdef __cplusplus

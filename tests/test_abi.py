@@ -89,6 +89,17 @@ CASES = {
     "null_data": (dict(v=_t([100, 4, 128], ptr=None)), INVALID),
     "out_dtype": (dict(out=_t([100, 4, 128], GDN_F32)), INVALID),
     "bad_dtype_code": (dict(g=_t([100, 4], 17)), INVALID),
+    # v and out move in 16-byte pieces: pointer and token/head byte strides must be multiples of 16
+    "misaligned_v": (dict(v=_t([100, 4, 128], ptr=FAKE + 8)), UNSUPPORTED),
+    "misaligned_v_stride": (dict(v=_t([100, 4, 128], strides=[516, 129, 1])), UNSUPPORTED),
+    "misaligned_out": (dict(out=_t([100, 4, 128], ptr=FAKE + (1 << 32) + 2)), UNSUPPORTED),
+    "misaligned_out_stride": (dict(out=_t([100, 4, 128], GDN_BF16, FAKE + (1 << 32), strides=[520, 130, 1])), UNSUPPORTED),
+    # out must not overlap itself: heads 64 elements apart, or heads of one token running into the next
+    "out_head_stride_below_128": (dict(out=_t([100, 4, 128], GDN_BF16, FAKE + (1 << 32), strides=[512, 64, 1])), UNSUPPORTED),
+    "out_tokens_overlap_heads": (dict(out=_t([100, 4, 128], GDN_BF16, FAKE + (1 << 32), strides=[128, 128, 1])), UNSUPPORTED),
+    "out_broadcast_heads": (dict(out=_t([100, 4, 128], GDN_BF16, FAKE + (1 << 32), strides=[128, 0, 1])), UNSUPPORTED),
+    "output_state_overlap": (dict(s1=_t([2, 4, 128, 128], GDN_F32, FAKE + (1 << 31),
+                                         strides=[4 * 16384, 128 * 64, 128, 1])), UNSUPPORTED),
 }
 
 
@@ -98,6 +109,17 @@ def test_rejected_before_any_device_access(name):
     rc, msg = _call(_args(**over))
     assert rc == code, (rc, msg)
     assert msg, "a failed call must leave a message"
+
+
+def test_interleaved_out_layouts_validate():
+    """Non-overlapping out layouts other than the contiguous one pass validation
+    (token-major with padding, head-major): no device exists, so the call stops
+    at the device check."""
+    if _has_gpu():
+        pytest.skip("a valid descriptor with fake pointers must not reach a real GPU")
+    for st in ([1024, 128, 1], [128, 100 * 128, 1]):
+        rc, msg = _call(_args(out=_t([100, 4, 128], GDN_BF16, FAKE + (1 << 32), strides=st)))
+        assert rc == NO_DEVICE, (st, rc, msg)
 
 
 def test_fp32_inputs_and_bf16_state_validate():

@@ -78,3 +78,72 @@ def test_two_streams_concurrently(gdn):
     for (o, f), (eo, ef) in zip(got, res):
         assert torch.equal(o, eo) and torch.equal(f, ef)
     say("[gpu] two streams: both results bitwise equal to the single-stream runs")
+
+
+def test_graph_survives_workspace_growth(gdn):
+    """A graph captured from a small split-path call keeps its workspace after a
+    larger eager split call on the same stream grows the cached workspace: the
+    superseded buffer is retired, not freed, so replays still write the small
+    call's results bitwise."""
+    small = W.build([8200, 100], 1, 4, torch.bfloat16, seed=55, gate="long").to(DEV)
+    large = W.build([40000, 3000], 1, 4, torch.bfloat16, seed=56, gate="long").to(DEV)
+    assert gdn.prefill_plan(small.N, small.T, small.Hv, small.q.dtype, False, False, 256)[0] == "split"
+    assert gdn.prefill_plan(large.N, large.T, large.Hv, large.q.dtype, False, False, 256)[0] == "split"
+
+    def bufs(w):
+        return (torch.empty(w.T, w.Hv, 128, dtype=w.q.dtype, device=DEV),
+                torch.empty(w.N, w.Hv, 128, 128, dtype=torch.float32, device=DEV))
+
+    def call(w, out, fin):
+        gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, 0.0, w.cu_seqlens, w.initial_state, fin, True, False, out)
+
+    so, sf = bufs(small)
+    lo, lf = bufs(large)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(small, so, sf)                 # sizes the stream's workspace for the small call
+        s.synchronize()
+        ref = (so.clone(), sf.clone())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            call(small, so, sf)
+        call(large, lo, lf)                 # grows the workspace (eager, same stream)
+        s.synchronize()
+        for r in range(3):
+            so.fill_(float("nan"))
+            sf.fill_(float("nan"))
+            g.replay()
+            s.synchronize()
+            assert torch.equal(so, ref[0]) and torch.equal(sf, ref[1]), f"replay {r} after growth differs"
+            call(large, lo, lf)             # eager work on the stream between replays
+            s.synchronize()
+    say("[gpu] graph replays after workspace growth: bitwise equal")
+
+
+def test_growth_during_capture_is_refused(gdn):
+    """A split call that would have to grow the workspace while its stream is
+    capturing is refused (UNSUPPORTED) and enqueues nothing."""
+    w = W.build([8200, 100], 1, 4, torch.bfloat16, seed=57, gate="long").to(DEV)
+    out = torch.zeros(w.T, w.Hv, 128, dtype=w.q.dtype, device=DEV)
+    fin = torch.zeros(w.N, w.Hv, 128, 128, dtype=torch.float32, device=DEV)
+    # the library's one-time device query happens here, outside the capture
+    gdn.gdn_chunk_prefill(w.q[:64], w.k[:64], w.v[:64], w.g[:64], w.beta[:64], 0.0,
+                          torch.tensor([0, 64], dtype=torch.int32, device=DEV), None, None, True, True, out[:64])
+    torch.cuda.synchronize()
+    out.zero_()
+    s = torch.cuda.Stream()                 # a new stream: no workspace yet
+    code = None
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            try:
+                gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, 0.0, w.cu_seqlens, w.initial_state, fin, True,
+                                      False, out)
+            except gdn.GdnError as e:
+                code = e.code
+            out.add_(1.0)                   # keep the captured graph non-empty
+        g.replay()
+        s.synchronize()
+    assert code == 2, code
+    assert torch.equal(out, torch.ones_like(out)) and torch.equal(fin, torch.zeros_like(fin))
+    say("[gpu] workspace growth during capture: refused")

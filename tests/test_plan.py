@@ -52,3 +52,16 @@ def test_invalid_sizes_are_rejected(args):
         gdn.prefill_plan(1, 64, 4, torch.float16, False, False, 256)
     with pytest.raises(RuntimeError):
         gdn.prefill_plan(1, 64, 4, BF, False, False, 0)
+
+
+@pytest.mark.parametrize("args", [(1, (1 << 40) + 64, 4), (1, 1 << 20, 65537), ((1 << 24) + 1, 1 << 24, 1),
+                                  (1 << 20, 1 << 30, 4096), (1, 1 << 62, 4)])
+def test_sizes_the_prefill_refuses_get_no_plan(args):
+    """The planner applies the prefill's own size limits (UNSUPPORTED), so no
+    plan exists for a call the prefill would reject, and T * Hv cannot overflow."""
+    L = gdn.load()
+    import ctypes
+    kind, seg = ctypes.c_int(-1), ctypes.c_int64(-1)
+    rc = L.gdn_prefill_plan(*args, gdn.GDN_BF16, 0, 0, 256, ctypes.byref(kind), ctypes.byref(seg))
+    assert rc == 2, rc
+    assert kind.value == -1 and seg.value == -1
