@@ -192,6 +192,9 @@ __device__ __forceinline__ float gate_value(uint32_t bits, int dt) {
 //   RK  rk_i, RQ rq_i  (1 without L2 norm; computed with the Gram tiles, which also fold rk_i into IG)
 //   FZ  sigma gamma_i rk_i   (rows of K S~^T)     FY  c sigma gamma_i rq_i  (output rows)
 //   FU  rk_i exp(G_L - G_i) / sigma'   (state update; without / sigma' on renorm)
+//   (FY is c gamma_i rq_i / gamma_L on a renormalising chunk of the fast path, whose
+//   output takes the state term as (S~ Q^T) sigma gamma_L: no factor of 1 / sigma',
+//   which can reach 2^40 e^60, meets the raw q.k of the output tile)
 // The gate rows RG .. FB come in two sets, for chunks of even and odd index:
 // one wave writes the next chunk's set while the current one is in use.  Row
 // `which` of set 1 sits at NROWF + which; after all rows, gamma_L of each set.
@@ -201,11 +204,6 @@ constexpr int kRowsTotal = NROWF + kGateRows;
 constexpr int kGateWave = 2;                  // the wave that loads and converts the gates
 constexpr float kFastDecay = -60.f;   // G_L above this: exp(G_i - G_j) = gamma_i / gamma_j is safe
 constexpr float kRenorm = 0x1p-40f;   // sigma below this is folded back into the state
-// A chunk takes the shared-Vnew (fast) path only when its lazy scale after the
-// chunk, sigma' = sigma gamma_L, is at least this: a renormalising chunk scales
-// its P tile by 1 / sigma', which must stay far from the bf16 and fp32 limits
-// (sigma' can reach 2^-40 e^-60 when sigma sits at the threshold).
-constexpr float kFastMinScale = 0x1p-100f;
 
 
 // Element e of each lane quad, broadcast to the quad (DPP quad_perm [e, e, e, e]).

@@ -103,6 +103,7 @@ fused_scan_kernel(const ScanParams p) {
     // factor row `which`, gate rows of set `set`; gamma_L of a set
     auto rf_set = [&](int which, int set) { return RF + (which < kGateRows ? which + set * NROWF : which) * C; };
     auto gamma_l = [&](int set) -> float & { return RF[kRowsTotal * C + set]; };
+    auto igamma_l = [&](int set) -> float & { return RF[kRowsTotal * C + 2 + set]; };   // 1 / gamma_L
 
     // ---- work item: XCD-aware so the r value heads of one q/k head meet in one L2
     const int r = p.r;
@@ -176,6 +177,7 @@ fused_scan_kernel(const ScanParams p) {
         rf_set(DC_, set)[lane] = __expf(GL - G);
         rf_set(FB_, set)[lane] = valid ? gb : 0.f;
         gamma_l(set) = __expf(GL);   // the same value from every lane
+        igamma_l(set) = __expf(-GL);
     };
     // The gates run two chunks ahead of K and Q: chunk c + 1's gate rows are
     // written during chunk c (phase [A], gate wave), from values loaded during
@@ -240,8 +242,7 @@ fused_scan_kernel(const ScanParams p) {
         const float sig_next = sigma * gLc;
         const bool renorm = !(sig_next >= kRenorm);
         const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                              int, rf(RG_)[C - 1]))) > kFastDecay &&
-                          sig_next >= kFastMinScale;
+                              int, rf(RG_)[C - 1]))) > kFastDecay;
         // Gram tiles (bi, bj) = (0,0) (1,0) (1,1) of K K^T ("A" tiles) and Q K^T ("P"
         // tiles), each computed transposed: register rows are the column index
         // j = 32 bj + acc_row, the lane is the row index i = 32 bi + l32.
@@ -361,14 +362,13 @@ fused_scan_kernel(const ScanParams p) {
             // Lane row i = 32 bi + l32; register 4 jj + t is column j = 32 bj + 8 jj + 4 h32 + t.
             //   A = b_i rk_i rk_j (k_i . k_j) exp(G_i - G_j)   for j < i   (fp32)
             //   P = c rq_i rk_j (q_i . k_j) exp(G_i - G_j)      for j <= i  (slow)
-            //   P = (q_i . k_j) / sigma'(renorm only)          for j <= i  (fast: the row
+            //   P = q_i . k_j                                  for j <= i  (fast: the row
             //       and column factors move to the output rows and to the shared Vnew
             //       operand, see [D])
             // Four consecutive columns are stored at once; every factor read is
             // issued before the first store.
             // Wave w < 3 holds A tile (0,0), (1,0), (1,1); wave 1 also P tile (1,1) and
             // wave 3 P tiles (0,0) and (1,0); the map modes need no P.
-            const float cP = renorm ? 1.f / sig_next : 1.f;
             // diagonal tiles only (bi == bj): row - column = l32 - 4 h32 - 8 jj - t
             const int dlane = l32 - 4 * h32;
             auto mask_row = [&](f32x4 &v, int jj, int keep_diag) {
@@ -424,7 +424,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[jj][t] = cP * acc[4 * jj + t];
+                        for (int t = 0; t < 4; ++t) v[jj][t] = acc[4 * jj + t];
                 } else {
                     const float fi = p.scale * rf(RQ_)[i], Gi = rf(RG_)[i];
                     f32x4 rk[4], G4[4];
@@ -465,9 +465,14 @@ fused_scan_kernel(const ScanParams p) {
             }
             if (ws == 0) {   // row factors of [D], lane = token
                 const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
-                rf(FZ_)[lane] = sigma * gam * rk;
-                rf(FU_)[lane] = renorm ? rk * dec : rk * dec / sig_next;
-                if constexpr (OUT) rf(FY_)[lane] = sigma * gam * rf(RQ_)[lane] * p.scale;
+                rf(FZ_)[lane] = sigma * (gam * rk);
+                rf(FU_)[lane] = renorm ? rk * dec : (rk * dec) / sig_next;
+                if constexpr (OUT) {
+                    // a renormalising fast chunk carries its state term as (Y sigma) gamma_L,
+                    // so its output rows take 1 / gamma_L instead of sigma (see [D])
+                    const float base = (p.scale * gam) * rf(RQ_)[lane];
+                    rf(FY_)[lane] = fast && renorm ? base * igamma_l(gset) : sigma * base;
+                }
             }
         }
         __syncthreads();
@@ -594,7 +599,9 @@ fused_scan_kernel(const ScanParams p) {
         //   Z' = V - FZ o (K S~^T)       Vnew = T' Z'   (T' = T diag(b))
         //   ub = FU o Vnew  (bf16 operand of the state update S~ += K^T ub)
         //   output, computed transposed (lane = token t, registers = 4 consecutive v):
-        //     fast: O^T = FY_t [ (S~ Q^T) + ub^T P^T ]   (P = masked q.k, see [B])
+        //     fast: O^T = FY_t [ (S~ Q^T) + ub^T P^T ]   (P = masked q.k, see [B]); on a
+        //           renormalising chunk ub carries no 1 / sigma', so the state term
+        //           enters as (S~ Q^T) sigma gamma_L and FY_t = c gamma_t rq_t / gamma_L
         //     slow: O^T = FY_t (S~ Q^T) + Vnew^T P^T
         // Z' = V - FZ o X, as the bf16 operand of Vnew = T' Z'
         frag zb[2][S32];
@@ -678,6 +685,12 @@ fused_scan_kernel(const ScanParams p) {
         }
         if constexpr (OUT) {
             if (fast) {
+                if (renorm) {   // sigma and gamma_L are both normal numbers; their product may not be
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) Y[ib][rr] = (Y[ib][rr] * sigma) * gLc;
+                }
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll

@@ -75,6 +75,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto tbuf = [&](int x) { return reinterpret_cast<bf16 *>(smem + L::T_OFF + (x & 1) * L::OB); };
     auto rows = [&](int which, int x) { return RF + ((x & 1) * NROWF + which) * C; };
     auto gamma_l = [&](int x) -> float & { return RF[2 * NROWF * C + (x & 1)]; };
+    auto igamma_l = [&](int x) -> float & { return RF[2 * NROWF * C + 2 + (x & 1)]; };   // 1 / gamma_L
 
     // ---- work item (XCD-aware as in the four-wave scan)
     const int r = p.r;
@@ -104,6 +105,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         rows(DC_, x)[lane] = __expf(GL - G);
         rows(FB_, x)[lane] = valid ? gb : 0.f;
         gamma_l(x) = __expf(GL);
+        igamma_l(x) = __expf(-GL);
     };
     constexpr int kGateW = 4 + kGateWave;   // the preparation wave that forms the gate rows
 
@@ -191,8 +193,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const float sig_next = sigma * gLc;
             const bool renorm = !(sig_next >= kRenorm);
             const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                                  int, rf(RG_)[C - 1]))) > kFastDecay &&
-                          sig_next >= kFastMinScale;
+                                  int, rf(RG_)[C - 1]))) > kFastDecay;
             const ChunkRef ch = chunk_at(bos, eos, c);
             const int Lc = ch.L;
             const bf16 *Ks = kbuf(c);
@@ -279,12 +280,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             __syncthreads();
 
-            // ---- interval 2: fast path output O^T = FY_t [S~ Q^T + ub^T P^T]; the
-            // output tile staged through this wave's 4 KB: rows t of its 32 columns
-            // (64 B), 16-byte granules of row t rotated by (t / 4) % 4 against bank
-            // conflicts
+            // ---- interval 2: fast path output O^T = FY_t [S~ Q^T + ub^T P^T] (a
+            // renormalising chunk: the state term as (S~ Q^T) sigma gamma_L, and FY_t
+            // with 1 / gamma_L); the output tile staged through this wave's 4 KB: rows
+            // t of its 32 columns (64 B), 16-byte granules of row t rotated by
+            // (t / 4) % 4 against bank conflicts
             if (on) {
                 if (fast) {
+                    if (renorm) {   // sigma and gamma_L are both normal numbers; their product may not be
+#pragma unroll
+                        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                            for (int rr = 0; rr < 16; ++rr) Y[ib][rr] = (Y[ib][rr] * sigma) * gLc;
+                    }
                     const bf16 *Ps = pbuf(c);
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib) {
@@ -472,8 +480,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const float sig_next = sigma * gLc;
             const bool renorm = !(sig_next >= kRenorm);
             const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                                  int, rf(RG_)[C - 1]))) > kFastDecay &&
-                          sig_next >= kFastMinScale;
+                                  int, rf(RG_)[C - 1]))) > kFastDecay;
             bf16 *Ts = tbuf(x);
 
             // ---- interval 1: A (fp32) and P of chunk x from the Gram tiles, row
@@ -481,10 +488,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // is column j = 32 bj + 8 jj + 4 h32 + t.
             //   A = b_i rk_i rk_j (k_i . k_j) exp(G_i - G_j)   for j < i   (fp32)
             //   P = c rq_i rk_j (q_i . k_j) exp(G_i - G_j)      for j <= i  (slow)
-            //   P = (q_i . k_j) / sigma' (renorm only)          for j <= i  (fast)
+            //   P = q_i . k_j                                  for j <= i  (fast)
             if (on) {
                 bf16 *Ps = pbuf(x);
-                const float cP = renorm ? 1.f / sig_next : 1.f;
                 const int dlane = l32 - 4 * h32;
                 auto mask_row = [&](f32x4 &v, int jj, int keep_diag) {
 #pragma unroll
@@ -538,7 +544,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) v[jj][t] = cP * acc[4 * jj + t];
+                            for (int t = 0; t < 4; ++t) v[jj][t] = acc[4 * jj + t];
                     } else {
                         const float fi = p.scale * rf(RQ_)[i], Gi = rf(RG_)[i];
                         f32x4 rk[4], G4[4];
@@ -568,9 +574,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 if (pw == 1) p_tile(X[1], 1, 1);
                 if (pw == 3) {   // row factors of the state work (the wave with no A tile), lane = token
                     const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
-                    rf(FZ_)[lane] = sigma * gam * rk;
-                    rf(FU_)[lane] = renorm ? rk * dec : rk * dec / sig_next;
-                    rf(FY_)[lane] = sigma * gam * rf(RQ_)[lane] * p.scale;
+                    rf(FZ_)[lane] = sigma * (gam * rk);
+                    rf(FU_)[lane] = renorm ? rk * dec : (rk * dec) / sig_next;
+                    const float base = (p.scale * gam) * rf(RQ_)[lane];
+                    rf(FY_)[lane] = fast && renorm ? base * igamma_l(x) : sigma * base;
                 }
             }
             __syncthreads();
