@@ -27,7 +27,9 @@ on "flashinfer.cudnn.cudnn_chunk_gated_delta_rule", Parameters):
                  updated in place; gates as varlen_bf16.
 
 Variant "alt_gates" (long_single, many_short, large_batch) draws
-g ~ U[0.9, 1) and beta ~ U(0, 1) instead.
+g ~ U[0.9, 1) and beta ~ U(0, 1) instead; variant "long_memory" of
+long_single draws g ~ U[0.999, 1] (a memory of ~1000 tokens, so errors of the
+state carried across chunks and segments are not hidden by fast decay).
 
 Draw order per recipe: lengths, q, k, v, g source, beta source, state, from
 torch.Generator(device).manual_seed(1000 + index).
@@ -161,9 +163,10 @@ def make(config, *, device="cpu", variant=None):
                      gate_dtype=torch.bfloat16 if variant == "gates_bf16" else torch.float32,
                      name=CONFIG_NAMES[1] + (f"/{variant}" if variant else ""))
     if idx == 2:
+        gate = "uniform" if alt else ("long" if variant == "long_memory" else "sigmoid")
         return build([65536], 16, 32, torch.bfloat16, seed=seed, device=device,
-                     cu_dtype=torch.int64, gate="uniform" if alt else "sigmoid",
-                     name=CONFIG_NAMES[2] + ("/alt_gates" if alt else ""))
+                     cu_dtype=torch.int64, gate=gate,
+                     name=CONFIG_NAMES[2] + (f"/{variant}" if variant else ""))
     if idx == 3:
         gen = _gen(seed, "cpu")
         lengths = torch.randint(0, 257, (256,), generator=gen)

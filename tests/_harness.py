@@ -17,6 +17,15 @@ def say(*a):
     sys.stdout.flush()
 
 
+# (label, out error, state error, tolerance) of every oracle comparison in the
+# session; printed at the end of the run (tests/conftest.py)
+RECORDS = []
+
+
+def record(label, e_out, e_state, tol):
+    RECORDS.append((label, float(e_out), None if e_state is None else float(e_state), tol))
+
+
 def run_gpu(gdn, w: W.Workload, batch_invariant=True, out=None, output_state=None, stream=None):
     """Runs the HIP scan on device copies of w; returns (out, final_state) on the device."""
     dev = torch.device("cuda", 0)
@@ -54,6 +63,23 @@ def check(gdn, w, tol, batch_invariant=True, label=""):
     e_out = nerr(out, ref_out)
     e_fin = nerr(fin, ref_fin) if fin is not None else 0.0
     say(f"      max normalised error: out {e_out:.3e}  state {e_fin:.3e}  (tol {tol:g})")
+    record(f"{label or w.name} bi={int(bool(batch_invariant))}", e_out, e_fin if fin is not None else None, tol)
     assert np.isfinite(e_out) and e_out <= tol, f"out error {e_out}"
     assert np.isfinite(e_fin) and e_fin <= tol, f"final state error {e_fin}"
     return out, fin
+
+
+def nerr_dev(gpu, ref):
+    """nerr for large tensors: gpu (a device tensor) against ref (a host fp64
+    array), compared on the device in fp64 slices."""
+    if ref.size == 0:
+        return 0.0
+    g = gpu.reshape(-1)
+    r = np.ascontiguousarray(ref).reshape(-1)
+    step = 1 << 26
+    num, den = 0.0, 0.0
+    for i in range(0, r.size, step):
+        rr = torch.from_numpy(r[i:i + step]).to(g.device)
+        num = max(num, float((g[i:i + step].double() - rr).abs().max()))
+        den = max(den, float(rr.abs().max()))
+    return num / max(den, 1e-12)

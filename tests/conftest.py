@@ -26,3 +26,19 @@ def gdn():
     import chunked_gated_delta_prefill_amd as lib
     lib.load()
     return lib
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Every oracle comparison of the session, with its max normalised errors."""
+    mod = sys.modules.get("_harness")
+    recs = getattr(mod, "RECORDS", None)
+    if not recs:
+        return
+    tr = terminalreporter
+    tr.section("parity against the oracle (max normalised error)")
+    worst = 0.0
+    for label, eo, es, tol in recs:
+        st = "-" if es is None else f"{es:.2e}"
+        tr.write_line(f"{label:<58} out {eo:.2e}  state {st:>8}  tol {tol:g}")
+        worst = max(worst, eo / tol, (es or 0.0) / tol)
+    tr.write_line(f"{len(recs)} comparisons; worst error / tolerance = {worst:.3f}")

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import gdn_workloads as W
-from _harness import BF16_TOL, F32_TOL, nerr, run_gpu, run_oracle, say
+from _harness import BF16_TOL, F32_TOL, nerr, record, run_gpu, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -215,6 +215,7 @@ def test_renorm_chunk_with_extreme_decay(gdn, bi):
     assert torch.isfinite(out).all() and torch.isfinite(fin).all()
     ro, rf = run_oracle(w)
     e1, e2 = nerr(out, ro), nerr(fin, rf)
+    record(f"renorm chunk, extreme decay bi={int(bi)}", e1, e2, BF16_TOL)
     say(f"      out {e1:.3e} state {e2:.3e}")
     assert e1 <= BF16_TOL and e2 <= BF16_TOL
 
@@ -254,6 +255,7 @@ def test_split_path_matches_oracle(gdn, gate):
     out, fin = run_gpu(gdn, w, False)
     ro, rf = run_oracle(w)
     e1, e2 = nerr(out, ro), nerr(fin, rf)
+    record(f"split path bf16 gate={gate} bi=0", e1, e2, BF16_TOL)
     say(f"      split: out {e1:.3e} state {e2:.3e}")
     assert e1 <= BF16_TOL and e2 <= BF16_TOL
     assert torch.equal(fin[2].cpu(), w.initial_state[2])
@@ -269,6 +271,7 @@ def test_split_path_fp32(gdn):
     out, fin = run_gpu(gdn, w, False)
     ro, rf = run_oracle(w)
     e1, e2 = nerr(out, ro), nerr(fin, rf)
+    record("split path fp32 bi=0", e1, e2, F32_TOL)
     say(f"      split fp32: out {e1:.3e} state {e2:.3e}")
     assert e1 <= F32_TOL and e2 <= F32_TOL
 
