@@ -97,12 +97,13 @@ def read_traffic(path=TRAFFIC_FILE, srcs=None):
 
 
 def cpu_baseline(w, max_seqs):
-    """The oracle (fp64 C recurrence, all host cores) on the first sequences."""
+    """The oracle as it stands (the fp32 token-by-token C recurrence, all host
+    cores) timed on the first max_seqs sequences (0: all of them).  Returns the
+    baseline record and the oracle's (out, final_state) for that sample."""
     import gdn_workloads as W
     import oracle
     import torch
-    lens = w.lengths()
-    take = min(max_seqs, w.N)
+    take = w.N if max_seqs <= 0 else min(max_seqs, w.N)
     cu = w.cu_seqlens.cpu().to(torch.int64)
     end = int(cu[take])
     sub = W.Workload("sample", w.q[:end].cpu(), w.k[:end].cpu(), w.v[:end].cpu(),
@@ -111,14 +112,69 @@ def cpu_baseline(w, max_seqs):
                      None if w.initial_state is None else w.initial_state[:take].cpu(),
                      w.state_dtype, w.use_qk_l2norm, w.scale)
     threads = oracle.default_threads()
-    oracle.run(sub.q[:1], sub.k[:1], sub.v[:1], None, None, 0.0, [0, 1], None, False, nthreads=1)  # load
+    oracle.run(sub.q[:1], sub.k[:1], sub.v[:1], None, None, 0.0, [0, 1], None, False, precision="f32",
+               nthreads=1)   # load the library
     t = time.perf_counter()
-    oracle.run(sub.q, sub.k, sub.v, sub.g, sub.beta, sub.scale, sub.cu_seqlens, sub.initial_state,
-               sub.use_qk_l2norm, nthreads=threads)
+    ref = oracle.run(sub.q, sub.k, sub.v, sub.g, sub.beta, sub.scale, sub.cu_seqlens, sub.initial_state,
+                     sub.use_qk_l2norm, precision="f32", nthreads=threads)
     dt = time.perf_counter() - t
-    return {"value": end / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {take} of {w.N} sequences ({end} tokens, all {w.Hv} v-heads), fp64 oracle, "
-                      f"{dt:.1f} s wall"}
+    part = "all" if take == w.N else f"the first {take} of"
+    rec = {"value": round(end / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{part} {w.N} sequences ({end} tokens, all {w.Hv} v-heads), fp32 token-by-token "
+                     f"oracle, {dt:.1f} s wall"}
+    return rec, ref, take, end
+
+
+def max_norm_err(got, ref):
+    """max_i |got_i - ref_i| / max_i |ref_i| over a whole tensor; got on the
+    device, ref a host array (compared on the device, in slices)."""
+    import numpy as np
+    import torch
+    if ref.size == 0:
+        return 0.0
+    flat_g = got.reshape(-1)
+    flat_r = np.ascontiguousarray(ref).reshape(-1)
+    step = 1 << 27
+    num, den = 0.0, 0.0
+    for i in range(0, flat_r.size, step):
+        r = torch.from_numpy(flat_r[i:i + step]).to(got.device, dtype=torch.float32)
+        num = max(num, float((flat_g[i:i + step].float() - r).abs().max()))
+        den = max(den, float(r.abs().max()))
+    return num / max(den, 1e-12)
+
+
+def achievable_peaks():
+    """Measured in the bench process: a large bf16 GEMM (torch.mm, 8192^3) and a
+    1 GiB device-to-device copy (read + write bytes)."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    reps = 10
+    for _ in range(reps):
+        torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    mm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del a, b
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_mm_tflops": round(mm_tflops, 1), "copy_gbs": round(copy_gbs, 1)}
 
 
 def copy_calibration():
@@ -359,7 +415,7 @@ def main():
     ap.add_argument("--workload", default="large_batch")
     ap.add_argument("--variant", default=None)
     ap.add_argument("--batch-invariant", type=int, default=0)
-    ap.add_argument("--cpu-sample-seqs", type=int, default=24)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=0, help="sequences the oracle runs (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", default=None)
@@ -493,8 +549,20 @@ def main():
         # the realised sequence boundaries of the seeded workload
         "cu_seqlens": [int(x) for x in w.cu_seqlens.cpu().tolist()],
     }
+    peaks = achievable_peaks()
+    res["achievable"] = {**peaks, "mfma_frac_of_mm": round(flops / (ms_step / 1e3) / 1e12 / peaks["bf16_mm_tflops"], 4),
+                         "hbm_frac_of_copy": round(achieved / peaks["copy_gbs"], 4)}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs)
+        rec, (ro, rf), take, end = cpu_baseline(w, args.cpu_sample_seqs)
+        res["cpu_baseline"] = rec
+        # the timed run's own output and final state against the oracle (same sample)
+        if args.pooled:   # the pool is updated in place by every step: no fixed reference
+            res["max_norm_err"] = None
+        else:
+            res["max_norm_err"] = {"out": max_norm_err(out[:end], ro),
+                                   "state": None if fin is None else max_norm_err(fin[:take], rf),
+                                   "reference": "fp32 oracle", "sample": rec["sample"].split(" (")[0]}
+        del ro, rf
     print(json.dumps(res), flush=True)
 
 

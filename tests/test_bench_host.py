@@ -52,3 +52,12 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_max_norm_err_on_host_tensors():
+    """bench.max_norm_err: max |got - ref| / max |ref| over the whole tensor."""
+    import numpy as np
+    ref = np.array([[1.0, -4.0], [2.0, 0.5]])
+    got = torch.tensor([[1.0, -3.9], [2.2, 0.5]])
+    assert abs(bench.max_norm_err(got, ref) - 0.2 / 4.0) < 1e-6
+    assert bench.max_norm_err(got[:0], ref[:0]) == 0.0
