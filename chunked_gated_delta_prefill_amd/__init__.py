@@ -10,6 +10,9 @@ The entry points mirror the C functions::
     gdn_chunk_prefill(q, k, v, g, beta, scale, cu_seqlens, initial_state,
                       output_state, use_qk_l2norm, batch_invariant, out,
                       stream=None)
+    gdn_chunk_prefill_noalloc(q, k, v, g, beta, scale, cu_seqlens, initial_state,
+                              output_state, use_qk_l2norm, batch_invariant, out,
+                              stream=None)
     gdn_chunk_prefill_checkpointed(q, k, v, g, beta, scale, cu_seqlens,
                                    initial_state, output_state, use_qk_l2norm,
                                    batch_invariant, checkpoints,
@@ -63,6 +66,8 @@ def load():
         lib.gdn_chunk_prefill.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int,
                                           ctypes.c_int, P, ctypes.c_void_p]
         lib.gdn_chunk_prefill.restype = ctypes.c_int
+        lib.gdn_chunk_prefill_noalloc.argtypes = lib.gdn_chunk_prefill.argtypes
+        lib.gdn_chunk_prefill_noalloc.restype = ctypes.c_int
         lib.gdn_chunk_prefill_checkpointed.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_int,
                                                        ctypes.c_int, P, ctypes.c_int32, ctypes.c_int64, P,
                                                        ctypes.c_void_p]
@@ -142,6 +147,22 @@ def gdn_chunk_prefill(q, k, v, g, beta, scale, cu_seqlens, initial_state, output
                        batch_invariant, describe(out), stream)
     if rc != 0:
         raise GdnError(rc, msg)
+
+
+def gdn_chunk_prefill_noalloc(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state,
+                              use_qk_l2norm, batch_invariant, out, stream=None):
+    """gdn_chunk_prefill without any device allocation (the split path's workspace
+    is the library's fixed scratch array)."""
+    stream = _stream_handle(stream, q)
+    lib = load()
+    ref = lambda d: None if d is None else ctypes.byref(d)
+    rc = lib.gdn_chunk_prefill_noalloc(ref(describe(q)), ref(describe(k)), ref(describe(v)), ref(describe(g)),
+                                       ref(describe(beta)), ctypes.c_float(0.0 if scale is None else float(scale)),
+                                       ref(describe(cu_seqlens)), ref(describe(initial_state)),
+                                       ref(describe(output_state)), int(bool(use_qk_l2norm)),
+                                       int(bool(batch_invariant)), ref(describe(out)), stream)
+    if rc != 0:
+        raise GdnError(rc, (lib.gdn_last_error() or b"").decode())
 
 
 def call_checkpointed_raw(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, use_qk_l2norm,

@@ -204,6 +204,39 @@ int get_workspace(int dev, hipStream_t st, size_t need, void **out, std::string 
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Scratch of the no-allocation entry point (gdn_chunk_prefill_noalloc): the
+// split path's workspace in one fixed device array.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is looked
+// up once per device (hipGetSymbolAddress, with the device current) and only
+// that address is passed to kernels.  On a 256-CU gfx950 part every split plan
+// needs at most 120 MiB.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_dev[64];   // device address of `scratch` per device (nullptr: not looked up yet)
+
+int scratch_address(int dev, void **out, std::string &msg) {
+    if (dev < 0 || dev >= 64) {
+        msg = "device index out of range for the no-allocation scratch";
+        return GDN_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            msg = std::string("hipGetSymbolAddress of the scratch array failed: ") + hipGetErrorString(e);
+            return GDN_ERR_HIP;
+        }
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" const char *gdn_last_error(void) { return g_last_error.c_str(); }
@@ -284,7 +317,7 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
                  const gdn_tensor *beta, float scale, const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
                  const gdn_tensor *output_state, int use_qk_l2norm, int batch_invariant, const gdn_tensor *ckpt,
                  int32_t ck_per_seq, int64_t ck_interval, const gdn_tensor *state_indices, const gdn_tensor *out,
-                 void *stream) {
+                 void *stream, bool noalloc = false) {
     g_last_error.clear();
     std::string msg;
     int rc;
@@ -492,8 +525,17 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     const size_t seg_bytes = align_up((size_t)cap * sizeof(gdn::SegEntry), 256);
     const size_t first_bytes = align_up((size_t)(N + 2) * sizeof(int32_t), 256);
     const size_t map_bytes = (size_t)cap * (size_t)Hv * gdn::kHeadDim * gdn::kHeadDim * sizeof(float);
+    const size_t ws_bytes = seg_bytes + first_bytes + 3 * map_bytes;
     void *wsp = nullptr;
-    if ((rc = get_workspace(dev, hs, seg_bytes + first_bytes + 3 * map_bytes, &wsp, msg))) return fail(rc, msg);
+    if (noalloc) {
+        if (ws_bytes > kScratchBytes)
+            return fail(GDN_ERR_UNSUPPORTED, "the split plan needs " + std::to_string(ws_bytes) +
+                                                 " bytes of scratch; the no-allocation entry point holds " +
+                                                 std::to_string(kScratchBytes));
+        if ((rc = scratch_address(dev, &wsp, msg))) return fail(rc, msg);
+    } else if ((rc = get_workspace(dev, hs, ws_bytes, &wsp, msg))) {
+        return fail(rc, msg);
+    }
     char *w = static_cast<char *>(wsp);
     gdn::SegEntry *segs = reinterpret_cast<gdn::SegEntry *>(w);
     int32_t *seg_first = reinterpret_cast<int32_t *>(w + seg_bytes);
@@ -529,6 +571,15 @@ extern "C" int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const
                                  int batch_invariant, const gdn_tensor *out, void *stream) {
     return prefill_impl(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, use_qk_l2norm,
                         batch_invariant, nullptr, 0, 0, nullptr, out, stream);
+}
+
+extern "C" int gdn_chunk_prefill_noalloc(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                                         const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                                         const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                                         const gdn_tensor *output_state, int use_qk_l2norm,
+                                         int batch_invariant, const gdn_tensor *out, void *stream) {
+    return prefill_impl(q, k, v, g, beta, scale, cu_seqlens, initial_state, output_state, use_qk_l2norm,
+                        batch_invariant, nullptr, 0, 0, nullptr, out, stream, true);
 }
 
 extern "C" int gdn_chunk_prefill_checkpointed(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,

@@ -133,6 +133,26 @@ int gdn_chunk_prefill(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor
                       int batch_invariant, const gdn_tensor *out, void *stream);
 
 /*
+ * gdn_chunk_prefill_noalloc - gdn_chunk_prefill for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, plan, kernels and
+ * results; the split path's workspace is a fixed 128 MiB array in the
+ * library's device memory instead of a cached allocation, so no call
+ * allocates or frees anything.  Every GPU holds its own copy of the array
+ * from its first use to the end of the process.  On a 256-CU gfx950 part
+ * every split plan fits (at most 120 MiB); a plan needing more is refused
+ * with GDN_ERR_UNSUPPORTED.  All calls on one GPU share the array: calls
+ * that overlap in time on one GPU (other streams, or another thread) race
+ * and must be serialised by the caller.  Ownership and errors otherwise as
+ * for gdn_chunk_prefill.
+ */
+int gdn_chunk_prefill_noalloc(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                              const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                              const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                              const gdn_tensor *output_state, int use_qk_l2norm,
+                              int batch_invariant, const gdn_tensor *out, void *stream);
+
+/*
  * gdn_chunk_prefill_checkpointed - gdn_chunk_prefill that also writes the
  * state at fixed token intervals of every sequence (the state checkpointing
  * that "flashinfer.cudnn", Linear attention, lists among the arguments the

@@ -25,7 +25,8 @@ def _declared_functions():
 
 def test_exports_every_declared_function():
     names = _declared_functions()
-    assert names == ["gdn_chunk_prefill", "gdn_chunk_prefill_checkpointed", "gdn_chunk_prefill_pooled",
+    assert names == ["gdn_chunk_prefill", "gdn_chunk_prefill_checkpointed", "gdn_chunk_prefill_noalloc",
+                     "gdn_chunk_prefill_pooled",
                      "gdn_decode_step", "gdn_decode_step_pooled", "gdn_last_error", "gdn_prefill_plan",
                      "gdn_release_workspace"]
     L = lib.load()
