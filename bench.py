@@ -62,12 +62,15 @@ def algorithmic(w):
     return flops, byts
 
 
-def scan_kernels(w, batch_invariant, cus, checkpoints=False):
+def scan_kernels(w, batch_invariant, cus, checkpoints=False, noalloc=False):
     """Kernels one prefill call launches, from the library's own host plan
     (gdn_prefill_plan, no device needed)."""
     import chunked_gated_delta_prefill_amd as gdn
     kind, _ = gdn.prefill_plan(w.N, w.T, w.Hv, w.q.dtype, checkpoints, batch_invariant, cus)
+    if noalloc and kind == "prepared_scan":   # the no-allocation entry point runs the pipelined scan
+        kind = "pipelined_scan"
     return {"scan": KERNEL, "pipelined_scan": "piped_scan_kernel",
+            "prepared_scan": "prepared: plan_kernel, fused_scan_kernel (preparation), prepared_scan_kernel",
             "split": "split: plan_kernel, fused_scan_kernel (maps N, M), fixup_kernel, fused_scan_kernel"}[kind]
 
 
@@ -424,6 +427,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 --pmc output dirs; the last argument is the output file")
     ap.add_argument("--decode", action="store_true", help="time the decode step instead of the prefill")
+    ap.add_argument("--noalloc", action="store_true",
+                    help="time gdn_chunk_prefill_noalloc (no workspace: the pipelined scan where the allocating "
+                         "entry point prepares chunks)")
     ap.add_argument("--pooled", action="store_true",
                     help="states in an indexed pool (gdn_chunk_prefill_pooled, reversed index order)")
     ap.add_argument("--checkpoint-interval", type=int, default=0,
@@ -497,8 +503,9 @@ def main():
                                                fin, w.use_qk_l2norm, bool(args.batch_invariant), ck, per_seq,
                                                ck_every, out, stream)
         else:
-            gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin,
-                                  w.use_qk_l2norm, bool(args.batch_invariant), out, stream)
+            fn = gdn.gdn_chunk_prefill_noalloc if args.noalloc else gdn.gdn_chunk_prefill
+            fn(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin, w.use_qk_l2norm,
+               bool(args.batch_invariant), out, stream)
 
     for _ in range(args.warmup):
         step()
@@ -520,7 +527,8 @@ def main():
     value = w.T / (ms_step / 1e3)
     achieved = byts / (kern_ms / 1e3) / 1e9
     # the counters were taken on the unsplit 32 x 8192 batch: no other workload carries them
-    profiled = args.workload == "large_batch" and args.variant is None and not (ck_every or args.pooled)
+    profiled = (args.workload == "large_batch" and args.variant is None and not (ck_every or args.pooled)
+                and not args.noalloc)
     traffic = read_traffic() if profiled else None
     res = {
         "metric": "GDN prefill tokens/s and TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU",
@@ -533,6 +541,7 @@ def main():
                    if w.initial_state is not None else None, "l2norm": w.use_qk_l2norm,
                    "batch_invariant": bool(args.batch_invariant),
                    **({"checkpoint_interval": ck_every} if ck_every else {}),
+                   **({"entry": "gdn_chunk_prefill_noalloc"} if args.noalloc else {}),
                    **({"pooled": True} if args.pooled else {})},
         "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
         "mfma_frac": round(flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -543,7 +552,7 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": scan_kernels(w, args.batch_invariant,
                                             torch.cuda.get_device_properties(0).multi_processor_count,
-                                            bool(ck_every)),
+                                            bool(ck_every), args.noalloc),
                      "algorithmic_bytes": byts, "algorithmic_flops": flops},
         "cpu_baseline": None,
         # the realised sequence boundaries of the seeded workload

@@ -252,7 +252,7 @@ def gdn_decode_step_pooled(q, k, v, g, beta, scale, state_pool, state_indices, u
         raise GdnError(rc, msg)
 
 
-PLAN_NAMES = {0: "scan", 1: "pipelined_scan", 2: "split"}
+PLAN_NAMES = {0: "scan", 1: "pipelined_scan", 2: "split", 3: "prepared_scan"}
 
 
 def prefill_plan(num_seqs, num_tokens, num_v_heads, io_dtype, checkpoints, batch_invariant, num_cus):

@@ -269,6 +269,7 @@ namespace {
 struct Plan {
     int kind;       // enum gdn_plan_kind
     int64_t lseg;   // segment length of the split path (0 without a split)
+    int np;         // prepared scan: blocks of 32 state rows per workgroup (1 or 2)
 };
 Plan make_plan(int64_t N, int64_t T, int64_t Hv, bool bf, bool ck, bool batch_invariant, int cus) {
     // Split path (T precompute -> MN precompute -> state fix-up -> CP prefill) when
@@ -304,13 +305,21 @@ Plan make_plan(int64_t N, int64_t T, int64_t Hv, bool bf, bool ck, bool batch_in
                                  (2.0 * per_chunk(N * (P - 1) * Hv) + per_chunk(N * P * Hv)) + (double)P;
         if (!(split < unsplit)) lseg = 0;
     }
-    if (lseg > 0) return {GDN_PLAN_SPLIT, lseg};
-    // At most one work item per CU: the pipelined eight-wave scan (one workgroup
-    // per CU, preparation of chunk c + 1 beside the state work of chunk c); it
-    // gives bitwise the results of the four-wave scan, so the choice keeps
-    // batch_invariant results independent of the batch.
-    if (bf && !ck && N * Hv <= cus) return {GDN_PLAN_PIPELINED_SCAN, 0};
-    return {GDN_PLAN_SCAN, 0};
+    if (lseg > 0) return {GDN_PLAN_SPLIT, lseg, 0};
+    // At most one work item per CU: the chain of chunks of one work item bounds
+    // the call.  With CUs to spare for two or four per (sequence, head), the
+    // state-independent preparation of every chunk runs first, in parallel over
+    // all chunks ("T precompute"), and the scan that consumes it spreads each
+    // head's state rows over 4 / np CUs.  Otherwise the pipelined scan prepares
+    // chunk c + 1 beside the state work of chunk c.  Both give bitwise the results
+    // of the four-wave scan, so the choice keeps batch_invariant results
+    // independent of the batch.
+    if (bf && !ck && N * Hv <= cus) {
+        if (N * Hv * 4 <= cus) return {GDN_PLAN_PREPARED_SCAN, 0, 1};
+        if (N * Hv * 2 <= cus) return {GDN_PLAN_PREPARED_SCAN, 0, 2};
+        return {GDN_PLAN_PIPELINED_SCAN, 0, 0};
+    }
+    return {GDN_PLAN_SCAN, 0, 0};
 }
 
 int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, const gdn_tensor *g,
@@ -512,9 +521,43 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     const bool bf = io == GDN_BF16;
     hipStream_t hs = static_cast<hipStream_t>(stream);
 
-    const Plan plan = make_plan(N, T, Hv, bf, p.ck != nullptr, batch_invariant != 0, cus);
+    Plan plan = make_plan(N, T, Hv, bf, p.ck != nullptr, batch_invariant != 0, cus);
+    // the no-allocation entry point has no room for prepared chunks: the
+    // pipelined scan gives the same results without a workspace
+    if (noalloc && plan.kind == GDN_PLAN_PREPARED_SCAN) plan.kind = GDN_PLAN_PIPELINED_SCAN;
     const int64_t lseg = plan.lseg;
     hipError_t e;
+    if (plan.kind == GDN_PLAN_PREPARED_SCAN) {
+        // table of segments of kPrepChunks chunks (the split path's plan kernel), the
+        // prepared chunks (one preparation work item per segment and head), then
+        // the scan over them
+        const int64_t lprep = (int64_t)gdn::kChunk * gdn::kPrepChunks;
+        const int64_t cap = T / lprep + N + 1;
+        const size_t seg_bytes = align_up((size_t)cap * sizeof(gdn::SegEntry), 256);
+        const size_t first_bytes = align_up((size_t)(N + 2) * sizeof(int32_t), 256);
+        const size_t prep_bytes = (size_t)cap * gdn::kPrepChunks * (size_t)Hv * gdn::kPrepSlot;
+        void *wsp = nullptr;
+        if ((rc = get_workspace(dev, hs, seg_bytes + first_bytes + prep_bytes, &wsp, msg))) return fail(rc, msg);
+        char *w = static_cast<char *>(wsp);
+        gdn::SegEntry *segs = reinterpret_cast<gdn::SegEntry *>(w);
+        int32_t *seg_first = reinterpret_cast<int32_t *>(w + seg_bytes);
+        int32_t *nsegs = seg_first + (N + 1);
+        gdn::ScanParams pp = p;
+        pp.segs = segs;
+        pp.nsegs = nsegs;
+        pp.seg_cap = (int32_t)cap;
+        pp.prep = w + seg_bytes + first_bytes;
+        pp.prep_cps = gdn::kPrepChunks;
+        gdn::ScanParams ps = p;
+        ps.prep = pp.prep;
+        ps.prep_cps = gdn::kPrepChunks;
+        ps.seg_first = seg_first;
+        if ((e = gdn::launch_plan(p.cu, p.cu_i64, (int)N, lprep, segs, nsegs, seg_first, (int)cap, hs)) != hipSuccess ||
+            (e = gdn::launch_prep(pp, hs)) != hipSuccess ||
+            (e = gdn::launch_prepared_scan(ps, plan.np, hs)) != hipSuccess)
+            return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return GDN_OK;
+    }
     if (lseg == 0) {
         if (plan.kind == GDN_PLAN_PIPELINED_SCAN) e = gdn::launch_piped_scan(p, hs);
         else e = gdn::launch_fused_scan(p, bf, gdn::kScan, hs);

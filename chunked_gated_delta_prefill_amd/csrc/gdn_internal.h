@@ -22,8 +22,25 @@ struct SegEntry {
 
 // Kernel modes: the scan proper, or one of the two segment maps of the split
 // path (S_end = S_start M + N): N = scan from a zero state, M = scan of the
-// identity with v = 0.  Map modes write no output rows.
-enum ScanMode { kScan = 0, kMapN = 1, kMapM = 2 };
+// identity with v = 0.  Map modes write no output rows.  kPrep runs only the
+// state-independent preparation of single chunks (one work item per chunk
+// entry of the table) and writes it to the prepared-chunk workspace.
+enum ScanMode { kScan = 0, kMapN = 1, kMapM = 2, kPrep = 3 };
+
+constexpr int kPrepChunks = 8;   // chunks per work item of the preparation pass
+
+// One prepared chunk of one value head (bf16 q/k/v), as kPrep writes it and the
+// prepared scan reads it.  T' = (I + A)^-1 diag(b) and the output tile P are
+// stored as 16-byte pieces of their used blocks (rows 0..31: columns 0..31;
+// rows 32..63: columns 0..63), row-major bf16 (a row of 64 holds 8 pieces);
+// then the sigma-free row factors and the chunk's decay scalars.
+constexpr int kPrepPieces = 32 * 4 + 32 * 8;                 // 16-byte pieces of one tile
+constexpr int kPrepT = 0;                                     // T' pieces
+constexpr int kPrepP = kPrepT + kPrepPieces * 16;             // P pieces
+constexpr int kPrepRows = kPrepP + kPrepPieces * 16;          // [64] each: gamma_i rk_i, c gamma_i rq_i, rk_i exp(G_L - G_i)
+constexpr int kPrepScalars = kPrepRows + 3 * kChunk * 4;      // gamma_L, 1 / gamma_L, G_L
+constexpr int kPrepSlot = 13312;                              // bytes per (chunk, value head)
+static_assert(kPrepScalars + 16 <= kPrepSlot && kPrepSlot % 256 == 0, "prepared slot");
 
 // Everything one scan launch needs.  Per-row strides are in bytes and fit in
 // 32 bits with 64 rows of headroom (the host checks); per-head and
@@ -68,6 +85,13 @@ struct ScanParams {
     const void *sidx;
     int32_t sidx_i64;
     int64_t pool_rows;
+    // prepared chunks: chunk c of sequence n is slot ((seg_first[n] * prep_cps + c)
+    // * Hv + h) * kPrepSlot, where the table (the split path's plan kernel) holds
+    // segments of prep_cps chunks; kPrep writes the chunks of one segment per
+    // work item
+    char *prep;
+    const int32_t *seg_first;
+    int32_t prep_cps;
 };
 
 // Fix-up of the split path: per (sequence, value head), serially over its
@@ -116,6 +140,11 @@ hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, int mode, hipStr
 // The eight-wave pipelined scan (bf16, scan mode, no checkpoints); same results
 // as launch_fused_scan, one workgroup per CU.
 hipError_t launch_piped_scan(const ScanParams &p, hipStream_t stream);
+// The preparation of every chunk (kPrep over the chunk table, bf16), then the
+// scan that consumes it; same results as launch_fused_scan.
+hipError_t launch_prep(const ScanParams &p, hipStream_t stream);
+// np = blocks of 32 state rows per workgroup (1 or 2): 4 / np workgroups per value head.
+hipError_t launch_prepared_scan(const ScanParams &p, int np, hipStream_t stream);
 
 // Split plan: cu_seqlens -> segment table of at most `cap` entries of `lseg`
 // tokens (a multiple of the chunk), one entry for an empty sequence.

@@ -83,7 +83,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(is_bf<IO>::
                                                                     is_bf<IO>::value ? 2 : 1))) void
 fused_scan_kernel(const ScanParams p) {
     constexpr bool OUT = MODE == kScan;     // map modes produce no output rows
-    constexpr bool HASV = MODE != kMapM;    // the M map scans v = 0
+    constexpr bool PREP = MODE == kPrep;    // preparation only: no state, no v
+    constexpr bool USEQ = OUT || PREP;      // q, its norms and the output tile P
+    constexpr bool HASV = MODE != kMapM && !PREP;   // the M map scans v = 0
     using L = Smem<IO>;
     using M = Mma<IO>;
     using frag = typename M::frag;
@@ -125,7 +127,7 @@ fused_scan_kernel(const ScanParams p) {
         eos = e.eos;
         first = e.first != 0;
         last = e.last != 0;
-        if (MODE != kScan && last) return;   // maps are needed for all but the last segment
+        if ((MODE == kMapN || MODE == kMapM) && last) return;   // maps: all but the last segment
     } else {
         n = item;
         bos = load_cu(p.cu, n, p.cu_i64);
@@ -290,7 +292,7 @@ fused_scan_kernel(const ScanParams p) {
                 auto load = [&](int k, int st) {
                     fk[st][0] = frag_at(Ks, 0, k);
                     fk[st][1] = frag_at(Ks, 1, k);
-                    if constexpr (OUT) {
+                    if constexpr (USEQ) {
                         fq[st][0] = frag_at(Qs, 0, k);
                         fq[st][1] = frag_at(Qs, 1, k);
                     }
@@ -301,25 +303,27 @@ fused_scan_kernel(const ScanParams p) {
                 for (int k = 0; k < NK; ++k) {
                     const int cur = k & 1;
                     if (k + 1 < NK) load(k + 1, cur ^ 1);
-                    const frag sf = acc_frag<IO>(S[k / S32], k % S32);
                     const frag k0 = fk[cur][0], k1 = fk[cur][1];
-                    X[0] = M::run(k0, sf, X[0]);
-                    X[1] = M::run(k1, sf, X[1]);
-                    if constexpr (OUT) {
-                        Y[0] = M::run(sf, fq[cur][0], Y[0]);
-                        Y[1] = M::run(sf, fq[cur][1], Y[1]);
+                    if constexpr (!PREP) {
+                        const frag sf = acc_frag<IO>(S[k / S32], k % S32);
+                        X[0] = M::run(k0, sf, X[0]);
+                        X[1] = M::run(k1, sf, X[1]);
+                        if constexpr (OUT) {
+                            Y[0] = M::run(sf, fq[cur][0], Y[0]);
+                            Y[1] = M::run(sf, fq[cur][1], Y[1]);
+                        }
                     }
                     if constexpr (R == 0) {
                         gt[cur] = M::run(k0, k0, gt[cur]);
                         ssa += sq(k0);
-                        if constexpr (OUT) ssb += sq(fq[cur][1]);
+                        if constexpr (USEQ) ssb += sq(fq[cur][1]);
                     } else if constexpr (R == 1) {
                         gt[0] = M::run(k0, k1, gt[0]);
                         ssa += sq(k1);
-                        if constexpr (OUT) gt[1] = M::run(k1, fq[cur][1], gt[1]);
+                        if constexpr (USEQ) gt[1] = M::run(k1, fq[cur][1], gt[1]);
                     } else if constexpr (R == 2) {
                         gt[cur] = M::run(k1, k1, gt[cur]);
-                    } else if constexpr (OUT) {
+                    } else if constexpr (USEQ) {
                         gt[0] = M::run(k0, fq[cur][0], gt[0]);
                         gt[1] = M::run(k0, fq[cur][1], gt[1]);
                         ssb += sq(fq[cur][0]);
@@ -328,12 +332,12 @@ fused_scan_kernel(const ScanParams p) {
                 if constexpr (R == 0) {
                     gt[0] += gt[1];
                     put_norm(ssa, RK_, 0);
-                    if constexpr (OUT) put_norm(ssb, RQ_, 1);
+                    if constexpr (USEQ) put_norm(ssb, RQ_, 1);
                 } else if constexpr (R == 1) {
                     put_norm(ssa, RK_, 1);
                 } else if constexpr (R == 2) {
                     gt[0] += gt[1];
-                } else if constexpr (OUT) {
+                } else if constexpr (USEQ) {
                     put_norm(ssb, RQ_, 0);
                 }
             };
@@ -451,7 +455,7 @@ fused_scan_kernel(const ScanParams p) {
                 }
             };
             if (ws < 3) a_tile(gt[0], ws > 0, ws == 2);
-            if constexpr (OUT) {
+            if constexpr (USEQ) {
                 if (ws == 3) {
                     p_tile(gt[0], 0, 0);
                     p_tile(gt[1], 1, 0);
@@ -463,7 +467,12 @@ fused_scan_kernel(const ScanParams p) {
                 issue_kq_part(pf, p, next, hq, tid, 3);
                 if (ws == kGateWave) issue_gates(pf, p, chunk_at(bos, eos, c + 2), h, lane);
             }
-            if (ws == 0) {   // row factors of [D], lane = token
+            if (PREP && ws == 0) {   // the row factors without the lazy scale, lane = token
+                const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
+                rf(FZ_)[lane] = gam * rk;
+                rf(FU_)[lane] = rk * dec;
+                rf(FY_)[lane] = (p.scale * gam) * rf(RQ_)[lane];
+            } else if (ws == 0) {   // row factors of [D], lane = token
                 const float rk = rf(RK_)[lane], gam = rf(GM_)[lane], dec = rf(DC_)[lane];
                 rf(FZ_)[lane] = sigma * (gam * rk);
                 rf(FU_)[lane] = renorm ? rk * dec : (rk * dec) / sig_next;
@@ -594,6 +603,30 @@ fused_scan_kernel(const ScanParams p) {
             for (int rr = 0; rr < 16; ++rr) Ts[(32 + acc_row(rr, h32)) * L::OLD + l32] = (IO)(-T21[rr] * bcol);
         }
         __syncthreads();
+
+        if constexpr (PREP) {
+            // T', P (their used blocks, as 16-byte pieces), the row factors without
+            // the lazy scale and the chunk's decay scalars into its workspace slot
+            static_assert(!PREP || BF, "prepared chunks are bf16");
+            char *slot = p.prep + (((int64_t)item * p.prep_cps + c) * p.Hv + h) * kPrepSlot;
+            for (int u = tid; u < kPrepPieces; u += 256) {
+                const int row = u < 128 ? u >> 2 : 32 + ((u - 128) >> 3);
+                const int pc = u < 128 ? (u & 3) : ((u - 128) & 7);
+                // rows of the LDS tiles are 8-byte aligned: two 8-byte reads per piece
+                const u32x2 t0 = *reinterpret_cast<const u32x2 *>(Ts + row * L::OLD + 8 * pc);
+                const u32x2 t1 = *reinterpret_cast<const u32x2 *>(Ts + row * L::OLD + 8 * pc + 4);
+                const u32x2 p0 = *reinterpret_cast<const u32x2 *>(Ps + row * L::OLD + 8 * pc);
+                const u32x2 p1 = *reinterpret_cast<const u32x2 *>(Ps + row * L::OLD + 8 * pc + 4);
+                *reinterpret_cast<i32x4 *>(slot + kPrepT + 16 * u) =
+                    i32x4{(int)t0[0], (int)t0[1], (int)t1[0], (int)t1[1]};
+                *reinterpret_cast<i32x4 *>(slot + kPrepP + 16 * u) =
+                    i32x4{(int)p0[0], (int)p0[1], (int)p1[0], (int)p1[1]};
+            }
+            if (tid < 3 * C) reinterpret_cast<float *>(slot + kPrepRows)[tid] = rf(FZ_ + tid / C)[tid % C];
+            if (tid == 0)
+                *reinterpret_cast<f32x4 *>(slot + kPrepScalars) =
+                    f32x4{gamma_l(gset), igamma_l(gset), rf(RG_)[C - 1], 0.f};
+        } else {
 
         // ---- [D] Vnew, output and state update for this wave's 32 state rows
         //   Z' = V - FZ o (K S~^T)       Vnew = T' Z'   (T' = T diag(b))
@@ -787,13 +820,14 @@ fused_scan_kernel(const ScanParams p) {
                 store_state<BF>(S, p.ck + slot * p.ck_n + h * p.ck_h, p.ck_v, p.ck_dt, v0, h32);
             }
         }
+        }   // !PREP
         __syncthreads();
     }
 
     // ---- final state (scan: the caller's output state, by the last segment only;
     // maps: the workspace)
     const bool write_caller = MODE == kScan && last && p.s_out && srow >= 0;
-    if (write_caller || MODE != kScan) {
+    if (write_caller || MODE == kMapN || MODE == kMapM) {
         if (sigma != 1.f) {
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
@@ -825,6 +859,8 @@ hipError_t launch(const ScanParams &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prep(const ScanParams &p, hipStream_t stream) { return launch<bf16, kPrep>(p, stream); }
 
 hipError_t launch_fused_scan(const ScanParams &p, bool io_bf16, int mode, hipStream_t stream) {
     if (io_bf16) {

@@ -1,0 +1,510 @@
+// The chunked gated delta rule scan over prepared chunks, for gfx950: the
+// state-dependent half of the scan, for launches that leave CUs to spare.
+//
+// Method and per-element steps are those of the four-wave scan in gdn_scan.hip
+// ("flashinfer.gdn_prefill": the chunked GDN scan and, in its Cake GDN CP
+// section, the stage order T precompute -> ... -> prefill; arguments as in
+// "flashinfer.cudnn.cudnn_chunk_gated_delta_rule", Parameters).  Everything of
+// a chunk that does not depend on the state (Gram tiles and norms, A, the UT
+// transform T' = (I + A)^-1 diag(b), the output tile P, the gate rows) was
+// computed for all chunks at once by the preparation pass (the kPrep mode of
+// the four-wave scan kernel) into a workspace slot per (chunk, value head).
+// What is left is a serial chain per (sequence, value head).
+//
+// The rows of the state evolve independently, so a value head's 128 state rows
+// are split over 4 / NP workgroups (NP = 1 or 2), each on its own CU, each
+// holding NP blocks of 32 rows.  A workgroup has three wave roles:
+//
+//   recurrence waves (NP, one per 32-row block; the state in MFMA accumulators):
+//     X = K S~^T,  Z' = V - FZ o X,  Vnew = T' Z',  ub = FU o Vnew,
+//     S~ += K^T ub   (after the lazy-decay renorm fold)
+//   output waves (NP, the same rows):
+//     Y = S~ Q^T (the state's bf16 operand fragments, passed through LDS),
+//     O^T = FY [Y + ub^T P^T]  (or the entry-wise form), bf16 rows to `out`
+//   loader waves (2): every global load of the coming chunks (K, Q, T', P, the
+//     row factors and the decay scalars) and their LDS staging, two chunks in
+//     flight in registers, so the compute waves issue no such loads
+//
+// Per chunk, two barrier intervals:
+//
+//   interval  recurrence                 output              loaders
+//   1         X, Z', Vnew, ub (to LDS),  Y = S~ Q^T          loads of chunk c + 2
+//             V loads of chunk c + 1
+//   2         renorm fold, update, S~    output products,    chunk c + 1 into LDS
+//             fragments (to LDS)         staging, stores
+//
+// With one or two blocks of rows per CU, each CU reads K, K^T, Q and the
+// exchange tiles for 32 or 64 state rows instead of 128: the LDS traffic per
+// CU, which bounds a chunk when one CU holds a whole head, drops 2-4 times.
+//
+// Every product is the four-wave scan's MFMA sequence with the same operands
+// in the same order and every row factor the same expression, so the results
+// are bitwise those of the four-wave and the pipelined scans.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "gdn_device.h"
+
+namespace gdn {
+namespace {
+
+using namespace dev;
+
+template <int NP> struct PreparedSmem {
+    static constexpr int KLD = kKqLd;   // K, Q rows (bf16, rows permuted, see kq_row)
+    static constexpr int OLD = 68;      // T', P rows (bf16)
+    static constexpr int KB = C * KLD * 2;
+    static constexpr int OB = C * OLD * 2;
+    static constexpr int FRAG_BYTES = 64 * 16;                 // one operand fragment of a wave
+    static constexpr int K_OFF = 0;                            // [2] by chunk parity
+    static constexpr int Q_OFF = K_OFF + 2 * KB;
+    static constexpr int T_OFF = Q_OFF + KB;
+    static constexpr int P_OFF = T_OFF + OB;                   // [2] by chunk parity
+    static constexpr int SB_OFF = P_OFF + 2 * OB;              // S~ fragments [block][8 steps]
+    static constexpr int UB_OFF = SB_OFF + NP * 8 * FRAG_BYTES;   // ub fragments [block][4]
+    static constexpr int NB_OFF = UB_OFF + NP * 4 * FRAG_BYTES;   // Vnew fragments (entry-wise path)
+    static constexpr int VO_OFF = NB_OFF + NP * 4 * FRAG_BYTES;   // 4 KB per block: V in (1), output out (2)
+    static constexpr int ROW_OFF = VO_OFF + NP * C * 32 * 2;      // FZ, FU, FY [2][64] each; scalars [2][4]
+    static constexpr int BYTES = ROW_OFF + (6 * C + 8) * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(Q_OFF % 16 == 0 && T_OFF % 16 == 0 && P_OFF % 16 == 0 && SB_OFF % 16 == 0 &&
+                  VO_OFF % 16 == 0 && ROW_OFF % 16 == 0, "align");
+};
+
+// Row and 16-byte piece of piece u of a prepared tile (rows 0..31: 4 pieces,
+// rows 32..63: 8 pieces).
+__device__ __forceinline__ int piece_row(int u) { return u < 128 ? u >> 2 : 32 + ((u - 128) >> 3); }
+__device__ __forceinline__ int piece_col(int u) { return u < 128 ? 8 * (u & 3) : 8 * ((u - 128) & 7); }
+
+__device__ __forceinline__ void put_piece(bf16 *M, int ld, int u, i32x4 x) {
+    // tile rows are 8-byte aligned: two 8-byte writes
+    bf16 *d = M + piece_row(u) * ld + piece_col(u);
+    *reinterpret_cast<u32x2 *>(d) = u32x2{(unsigned)x[0], (unsigned)x[1]};
+    *reinterpret_cast<u32x2 *>(d + 4) = u32x2{(unsigned)x[2], (unsigned)x[3]};
+}
+
+// The wave-uniform value of a float every lane holds.  (Taking the uniform
+// value of one lane of a loaded vector, readfirstlane(v[i]), is folded by this
+// compiler into readfirstlane(v[0]) for every i, so only plain floats go
+// through readfirstlane here.)
+__device__ __forceinline__ float uniform(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// One chunk in flight to the loader waves' registers (thread lt of 128).
+struct LoaderSet {
+    i32x4 k[8], q[8];   // K, Q pieces u = lt + 128 j: row u / 16, 16 bytes at column 8 (u % 16)
+    i32x4 t[3], p[3];   // T', P pieces lt + 128 j (384 pieces)
+    float bz, bu, by;   // row factors of token lt (lt < 64)
+    float gl, igl, G;   // gamma_L, 1 / gamma_L, G_L
+};
+
+template <int NP>
+__global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const ScanParams p) {
+    using L = PreparedSmem<NP>;
+    using M = Mma<bf16>;
+    using frag = M::frag;
+    constexpr int S32 = 2;          // 32x32x16 steps per 32-wide contraction block
+    constexpr int SLICES = 4 / NP;  // workgroups per value head
+
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    auto kbuf = [&](int x) { return reinterpret_cast<bf16 *>(smem + L::K_OFF + (x & 1) * L::KB); };
+    bf16 *Qs = reinterpret_cast<bf16 *>(smem + L::Q_OFF);
+    bf16 *Ts = reinterpret_cast<bf16 *>(smem + L::T_OFF);
+    auto pbuf = [&](int x) { return reinterpret_cast<bf16 *>(smem + L::P_OFF + (x & 1) * L::OB); };
+    // operand fragment f of block i in one of the exchange areas (16 bytes per lane)
+    auto xfrag = [&](int off, int nf, int i, int f, int lane) {
+        return reinterpret_cast<bf16x8 *>(smem + off + ((i * nf + f) * 64 + lane) * 16);
+    };
+    float *RW = reinterpret_cast<float *>(smem + L::ROW_OFF);
+    auto fzr = [&](int x) { return RW + (x & 1) * C; };            // FZ of chunk x
+    auto fur = [&](int x) { return RW + (2 + (x & 1)) * C; };      // FU
+    auto fyr = [&](int x) { return RW + (4 + (x & 1)) * C; };      // FY
+    auto scal = [&](int x) { return RW + 6 * C + 4 * (x & 1); };   // gamma_L, 1 / gamma_L, G_L
+
+    // ---- work item: (sequence, value head, slice of 32 NP state rows); the r value
+    // heads of a q/k head and the slices of each get workgroup ids 8 apart (one XCD)
+    const int r = p.r;
+    const int b = blockIdx.x;
+    const int group = 8 * r * SLICES;
+    const int within = b % group;
+    const int pidx = (b / group) * 8 + (within & 7);
+    if (pidx >= p.N * p.Hqk) return;
+    const int rest = within >> 3;
+    const int n = pidx / p.Hqk, hq = pidx % p.Hqk;
+    const int h = hq * r + rest % r, slice = rest / r;
+    const int64_t bos = load_cu(p.cu, n, p.cu_i64), eos = load_cu(p.cu, n + 1, p.cu_i64);
+    const int64_t srow = state_row(p.sidx, p.sidx_i64, p.pool_rows, n);
+    const int nchunks = (int)((eos - bos + C - 1) / C);
+    const int ws0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    if (ws0 < NP) {
+        // ================= recurrence waves =================
+        const int vb = slice * NP + ws0;   // this wave's block of 32 state rows
+        f32x16 S[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) S[bb] = zero16();
+        {
+            const int lane = threadIdx.x & 63, h32 = lane >> 5, v0 = 32 * vb + (lane & 31);
+            if (p.s_in && srow >= 0)
+                load_state<true>(S, p.s_in + srow * p.si_n + h * p.si_h, p.si_v, p.si_dt, v0, h32);
+        }
+        float sigma = 1.f;
+        VWide vw;
+        auto issue_v = [&](int x) {
+            const ChunkRef ch = chunk_at(bos, eos, x);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) issue_v_wide_part(vw, p, ch, h, vb, threadIdx.x & 63, j);
+        };
+        // the state's bf16 operand fragments (natural order), kept for this wave's X
+        // pass and written to LDS for its output wave
+        frag sfr[4 * S32];
+        auto state_frags = [&](int lane) {
+#pragma unroll
+            for (int k = 0; k < 4 * S32; ++k) {
+                sfr[k] = acc_frag<bf16>(S[k / S32], k % S32);
+                *xfrag(L::SB_OFF, 8, ws0, k, lane) = sfr[k];
+            }
+        };
+        if (nchunks > 0) issue_v(0);
+        state_frags(threadIdx.x & 63);
+        __syncthreads();   // chunk 0 staged by the loaders
+
+        for (int c = 0; c < nchunks; ++c) {
+            int tid_o = threadIdx.x;
+            asm volatile("" : "+v"(tid_o));
+            const int lane = tid_o & 63;
+            const int h32 = lane >> 5, l32 = lane & 31;
+            const float gLc = uniform(scal(c)[0]);
+            const float sig_next = sigma * gLc;
+            const bool renorm = !(sig_next >= kRenorm);
+            const bool fast = uniform(scal(c)[2]) > kFastDecay;
+            const bf16 *Ks = kbuf(c);
+            const float *FZr = fzr(c), *FUr = fur(c);
+            bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + ws0 * (C * 32);
+
+            // ---- interval 1: X = K S~^T (the next step's K fragments read while the
+            // current step runs), Z', Vnew, ub
+            f32x16 X[2] = {zero16(), zero16()};
+            {
+                frag fk[2][2];
+                auto load = [&](int k, int st) {
+                    fk[st][0] = ld_kq(Ks, l32, k, h32);
+                    fk[st][1] = ld_kq(Ks, 32 + l32, k, h32);
+                };
+                load(0, 0);
+#pragma unroll
+                for (int k = 0; k < 4 * S32; ++k) {
+                    const int cur = k & 1;
+                    if (k + 1 < 4 * S32) load(k + 1, cur ^ 1);
+                    X[0] = M::run(fk[cur][0], sfr[k], X[0]);
+                    X[1] = M::run(fk[cur][1], sfr[k], X[1]);
+                }
+            }
+            frag zb[2][S32];
+            {
+                // V through this wave's 4 KB, back as 4 consecutive tokens of one column
+                float vv[2][16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<i32x4 *>(Vw + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = vw.x[j];
+                const int i = lane & 15, g16 = (lane >> 4) & 1;
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bf16 *src = Vw + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
+                        const bf16x4 xv =
+                            __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src));
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) vv[ib][4 * q + t] = (float)xv[t];
+                    }
+                if (c + 1 < nchunks) issue_v(c + 1);   // the registers are free again
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const f32x4 fz = ld4(FZr + 32 * ib + 8 * jj + 4 * h32);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int rr = 4 * jj + t;
+                            X[ib][rr] = fmaf(-fz[t], X[ib][rr], vv[ib][rr]);
+                        }
+                    }
+#pragma unroll
+                    for (int st = 0; st < S32; ++st) zb[ib][st] = acc_frag<bf16>(X[ib], st);
+                }
+            }
+            // Vnew = T' Z'   (T' lower block-triangular: the upper 32x32 block is zero)
+            f32x16 Vn[2] = {zero16(), zero16()};
+#pragma unroll
+            for (int s = 0; s < S32; ++s) {
+                Vn[0] = M::run(ld_acc<bf16>(Ts, L::OLD, l32, 0, s, h32), zb[0][s], Vn[0]);
+                Vn[1] = M::run(ld_acc<bf16>(Ts, L::OLD, 32 + l32, 0, s, h32), zb[0][s], Vn[1]);
+                Vn[1] = M::run(ld_acc<bf16>(Ts, L::OLD, 32 + l32, 32, s, h32), zb[1][s], Vn[1]);
+            }
+            if (!fast) {   // the entry-wise output path takes Vnew itself
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int s = 0; s < S32; ++s)
+                        *xfrag(L::NB_OFF, 4, ws0, S32 * ib + s, lane) = acc_frag<bf16>(Vn[ib], s);
+            }
+            frag ub[2][S32];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const f32x4 fu = ld4(FUr + 32 * ib + 8 * jj + 4 * h32);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) Vn[ib][4 * jj + t] *= fu[t];
+                }
+#pragma unroll
+                for (int s = 0; s < S32; ++s) {
+                    ub[ib][s] = acc_frag<bf16>(Vn[ib], s);
+                    *xfrag(L::UB_OFF, 4, ws0, S32 * ib + s, lane) = ub[ib][s];
+                }
+            }
+            __syncthreads();
+
+            // ---- interval 2: renorm fold, S~ += K^T ub; the next chunk's S~ fragments
+            if (renorm) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) S[bb][rr] *= sig_next;
+            }
+            {
+                constexpr int NU = 2 * S32;
+                frag kt[2][4];
+                auto load_kt = [&](int k, frag (&f)[4]) {
+                    const int ib = k / S32, st = k % S32;
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) f[bb] = ld_acc_tr(Ks, 32 * bb, 32 * ib, st, lane);
+                };
+                load_kt(0, kt[0]);
+#pragma unroll
+                for (int k = 0; k < NU; ++k) {
+                    const int cur = k & 1;
+                    if (k + 1 < NU) load_kt(k + 1, kt[cur ^ 1]);
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) S[bb] = M::run(kt[cur][bb], ub[k / S32][k % S32], S[bb]);
+                }
+            }
+            sigma = renorm ? 1.f : sig_next;
+            if (c + 1 < nchunks) state_frags(lane);
+            __syncthreads();
+        }
+
+        // ---- final state (each slice writes its own rows)
+        if (p.s_out && srow >= 0) {
+            if (sigma != 1.f) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) S[bb][rr] *= sigma;
+            }
+            const int lane = threadIdx.x & 63, h32 = lane >> 5, v0 = 32 * vb + (lane & 31);
+            store_state<true>(S, p.s_out + srow * p.so_n + h * p.so_h, p.so_v, p.so_dt, v0, h32);
+        }
+    } else if (ws0 < 2 * NP) {
+        // ================= output waves =================
+        const int w = ws0 - NP;             // the block of rows (and the recurrence wave) this wave outputs
+        const int vb = slice * NP + w;
+        float sigma = 1.f;
+        __syncthreads();   // chunk 0 staged by the loaders
+
+        for (int c = 0; c < nchunks; ++c) {
+            int tid_o = threadIdx.x;
+            asm volatile("" : "+v"(tid_o));
+            const int lane = tid_o & 63;
+            const int h32 = lane >> 5, l32 = lane & 31;
+            const float gLc = uniform(scal(c)[0]);
+            const float sig_next = sigma * gLc;
+            const bool renorm = !(sig_next >= kRenorm);
+            const bool fast = uniform(scal(c)[2]) > kFastDecay;
+            const ChunkRef ch = chunk_at(bos, eos, c);
+            const int Lc = ch.L;
+
+            // ---- interval 1: Y = S~ Q^T (the state as the A operand gives its transpose:
+            // lane = token, registers = 4 consecutive v)
+            f32x16 Y[2] = {zero16(), zero16()};
+            {
+                frag fq[2][2];
+                auto load = [&](int k, int st) {
+                    fq[st][0] = ld_kq(Qs, l32, k, h32);
+                    fq[st][1] = ld_kq(Qs, 32 + l32, k, h32);
+                };
+                load(0, 0);
+#pragma unroll
+                for (int k = 0; k < 4 * S32; ++k) {
+                    const int cur = k & 1;
+                    if (k + 1 < 4 * S32) load(k + 1, cur ^ 1);
+                    const frag sf = *xfrag(L::SB_OFF, 8, w, k, lane);
+                    Y[0] = M::run(sf, fq[cur][0], Y[0]);
+                    Y[1] = M::run(sf, fq[cur][1], Y[1]);
+                }
+            }
+            __syncthreads();
+
+            // ---- interval 2: the output rows of chunk c
+            const bf16 *Ps = pbuf(c);
+            const float *FYr = fyr(c);
+            if (fast) {   // O^T = FY_t [S~ Q^T + ub^T P^T] (renormalising: the state term as (S~ Q^T) sigma gamma_L)
+                if (renorm) {
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) Y[ib][rr] = (Y[ib][rr] * sigma) * gLc;
+                }
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+                    for (int jb = 0; jb <= ib; ++jb)
+#pragma unroll
+                        for (int s = 0; s < S32; ++s)
+                            Y[ib] = M::run(*xfrag(L::UB_OFF, 4, w, S32 * jb + s, lane),
+                                           ld_acc<bf16>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), Y[ib]);
+                    const float fy = FYr[32 * ib + l32];
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
+                }
+            } else {      // FY_t (S~ Q^T) + Vnew^T P^T
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const float fy = FYr[32 * ib + l32];
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
+#pragma unroll
+                    for (int jb = 0; jb <= ib; ++jb)
+#pragma unroll
+                        for (int s = 0; s < S32; ++s)
+                            Y[ib] = M::run(*xfrag(L::NB_OFF, 4, w, S32 * jb + s, lane),
+                                           ld_acc<bf16>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), Y[ib]);
+                }
+            }
+            // staged through this block's 4 KB (rows t of the 32 columns, 16-byte granules
+            // of row t rotated by (t / 4) % 4), then 16 rows of 64 bytes per store
+            bf16 *Ow = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + w * (C * 32);
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bf16x4 b4 = {(bf16)Y[ib][4 * q], (bf16)Y[ib][4 * q + 1], (bf16)Y[ib][4 * q + 2],
+                                       (bf16)Y[ib][4 * q + 3]};
+                    *reinterpret_cast<bf16x4 *>(Ow + (32 * ib + l32) * 32 + 8 * (q ^ ((l32 >> 2) & 3)) + 4 * h32) = b4;
+                }
+            const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * 2);
+            const int gq = lane & 3;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int t = 16 * k + (lane >> 2);
+                const i32x4 o16 = *reinterpret_cast<const i32x4 *>(Ow + t * 32 + 8 * (gq ^ ((t >> 2) & 3)));
+                __builtin_amdgcn_raw_buffer_store_b128(o16, ro, t * p.o_st + (32 * vb + 8 * gq) * 2, 0, 0);
+            }
+            sigma = renorm ? 1.f : sig_next;
+            __syncthreads();
+        }
+    } else {
+        // ================= loader waves =================
+        const int lt = threadIdx.x - 128 * NP;   // 0..127
+        const int64_t slot_stride = (int64_t)p.Hv * kPrepSlot;
+        const char *slot0 =
+            p.prep + ((int64_t)(nchunks > 0 ? p.seg_first[n] : 0) * p.prep_cps * p.Hv + h) * kPrepSlot;
+        float sigma = 1.f;   // the lazy scale at the start of the chunk being staged
+        LoaderSet set0, set1;
+        auto issue = [&](LoaderSet &d, int x) {
+            const ChunkRef ch = chunk_at(bos, eos, x);
+            const auto rk = rsrc(p.k + ch.t0 * p.k_st + hq * p.k_sh, ch.L > 0 ? (ch.L - 1) * p.k_st + D * 2 : 0);
+            const auto rq = rsrc(p.q + ch.t0 * p.q_st + hq * p.q_sh, ch.L > 0 ? (ch.L - 1) * p.q_st + D * 2 : 0);
+            const auto rs = rsrc(slot0 + x * slot_stride, kPrepSlot);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int u = lt + 128 * j, row = u >> 4, col = 16 * (u & 15);
+                d.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, row * p.k_st + col, 0, 0);
+                d.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, row * p.q_st + col, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                d.t[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, kPrepT + 16 * (lt + 128 * j), 0, 0);
+                d.p[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, kPrepP + 16 * (lt + 128 * j), 0, 0);
+            }
+            if (lt < C) {
+                d.bz = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, kPrepRows + 4 * lt, 0, 0));
+                d.by = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, kPrepRows + 4 * (C + lt), 0, 0));
+                d.bu = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rs, kPrepRows + 4 * (2 * C + lt), 0, 0));
+            }
+            d.gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, kPrepScalars, 0, 0));
+            d.igl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, kPrepScalars + 4, 0, 0));
+            d.G = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, kPrepScalars + 8, 0, 0));
+        };
+        // chunk x from its register set into LDS; the row factors with the lazy scale
+        // at the chunk's start (the four-wave scan's expressions)
+        auto stage = [&](const LoaderSet &d, int x) {
+            bf16 *Ks = kbuf(x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int u = lt + 128 * j, row = u >> 4, col = 8 * (u & 15);
+                *reinterpret_cast<i32x4 *>(Ks + kq_off(row, col)) = d.k[j];
+                *reinterpret_cast<i32x4 *>(Qs + kq_off(row, col)) = d.q[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                put_piece(Ts, L::OLD, lt + 128 * j, d.t[j]);
+                put_piece(pbuf(x), L::OLD, lt + 128 * j, d.p[j]);
+            }
+            const float gL = uniform(d.gl), igL = uniform(d.igl), G = uniform(d.G);
+            const float sig_next = sigma * gL;
+            const bool renorm = !(sig_next >= kRenorm);
+            const bool fast = G > kFastDecay;
+            if (lt < C) {
+                fzr(x)[lt] = sigma * d.bz;
+                fur(x)[lt] = renorm ? d.bu : d.bu / sig_next;
+                fyr(x)[lt] = fast && renorm ? d.by * igL : sigma * d.by;
+            }
+            if (lt == 0) {
+                scal(x)[0] = gL;
+                scal(x)[1] = igL;
+                scal(x)[2] = G;
+            }
+            sigma = renorm ? 1.f : sig_next;
+        };
+        if (nchunks > 0) {
+            issue(set0, 0);
+            if (nchunks > 1) issue(set1, 1);
+            stage(set0, 0);
+        }
+        __syncthreads();
+        // Chunk c's set holds chunk c + 2 after interval 1 of chunk c; the other set
+        // (chunk c + 1, loaded an iteration earlier) is staged in interval 2.  The loop
+        // runs two chunks per trip so that each set is a fixed group of registers.
+        auto body = [&](LoaderSet &mine, LoaderSet &other, int c) {
+            if (c + 2 < nchunks) issue(mine, c + 2);
+            __syncthreads();
+            if (c + 1 < nchunks) stage(other, c + 1);
+            __syncthreads();
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            body(set0, set1, c);
+            if (c + 1 < nchunks) body(set1, set0, c + 1);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prepared_scan(const ScanParams &p, int np, hipStream_t stream) {
+    const int64_t pairs = (int64_t)p.N * p.Hqk;
+    const int64_t blocks = ((pairs + 7) / 8) * 8 * p.r * (4 / np);
+    if (blocks == 0) return hipSuccess;
+    if (np == 1)
+        hipLaunchKernelGGL(prepared_scan_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(prepared_scan_kernel<2>, dim3((unsigned)blocks), dim3(384), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

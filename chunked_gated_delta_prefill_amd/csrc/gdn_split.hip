@@ -16,10 +16,13 @@ namespace {
 using namespace dev;
 
 // Plan: cu_seqlens -> segment table.  One workgroup; sequences in tiles of 256
-// with a block-wide inclusive scan of their segment counts.
+// with a block-wide inclusive scan of their segment counts, then the entries of
+// the tile's sequences written by all threads together (one long sequence can
+// hold a thousand one-chunk entries).
 __global__ __launch_bounds__(256) void plan_kernel(const void *cu, int cu_i64, int N, int64_t lseg, SegEntry *segs,
                                                    int32_t *nsegs, int32_t *seg_first, int cap) {
-    __shared__ int32_t part[256];
+    __shared__ int32_t part[256], tfirst[256], tcnt[256];
+    __shared__ int64_t tbos[256], teos[256];
     const int tid = threadIdx.x;
     int base = 0;
     for (int n0 = 0; n0 < N; n0 += 256) {
@@ -42,17 +45,25 @@ __global__ __launch_bounds__(256) void plan_kernel(const void *cu, int cu_i64, i
         }
         const int first = base + part[tid] - cnt;
         const int tile_total = part[255];
-        if (n < N) {
-            seg_first[n] = first;
-            for (int sgi = 0; sgi < cnt; ++sgi) {
-                const int idx = first + sgi;
+        tfirst[tid] = first;
+        tcnt[tid] = cnt;
+        tbos[tid] = bos;
+        teos[tid] = eos;
+        if (n < N) seg_first[n] = first;
+        __syncthreads();
+        const int ns = N - n0 < 256 ? N - n0 : 256;
+        for (int sq = 0; sq < ns; ++sq) {
+            const int c = tcnt[sq], f = tfirst[sq];
+            const int64_t b0 = tbos[sq], e0 = teos[sq];
+            for (int sgi = tid; sgi < c; sgi += 256) {
+                const int idx = f + sgi;
                 if (idx < cap) {
                     SegEntry e;
-                    e.bos = bos + sgi * lseg;
-                    e.eos = eos < bos + (sgi + 1) * lseg ? eos : bos + (sgi + 1) * lseg;
-                    e.n = n;
+                    e.bos = b0 + sgi * lseg;
+                    e.eos = e0 < b0 + (sgi + 1) * lseg ? e0 : b0 + (sgi + 1) * lseg;
+                    e.n = n0 + sq;
                     e.first = sgi == 0;
-                    e.last = sgi == cnt - 1;
+                    e.last = sgi == c - 1;
                     e.pad = 0;
                     segs[idx] = e;
                 }

@@ -115,8 +115,8 @@ typedef struct gdn_tensor {
  * Ownership: every tensor is caller-owned device memory; the library writes
  * only `out`, `output_state` and its own workspace (cached per device and
  * stream, grown on demand; see gdn_release_workspace).
- * Graph capture: a call whose plan (gdn_prefill_plan) is GDN_PLAN_SPLIT uses
- * the workspace of its stream; after one eager call of the largest shape on
+ * Graph capture: a call whose plan (gdn_prefill_plan) is GDN_PLAN_SPLIT or
+ * GDN_PLAN_PREPARED_SCAN uses the workspace of its stream; after one eager call of the largest shape on
  * that stream, calls enqueue kernels only and can be captured.  A call that
  * would grow the workspace while the stream is capturing is refused with
  * GDN_ERR_UNSUPPORTED.  A captured graph keeps the capture stream's workspace
@@ -259,13 +259,22 @@ int gdn_decode_step_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_t
  * few long sequences pays off, and never with batch_invariant).
  *   GDN_PLAN_SCAN            one launch of the four-wave fused scan
  *   GDN_PLAN_PIPELINED_SCAN  one launch of the eight-wave pipelined scan (bf16,
- *                            no checkpoints, at most one work item per CU);
- *                            bitwise the results of GDN_PLAN_SCAN
+ *                            no checkpoints, more than half as many work items
+ *                            as CUs and at most one per CU); bitwise the
+ *                            results of GDN_PLAN_SCAN
  *   GDN_PLAN_SPLIT           segment table, the two segment maps, the state
  *                            fix-up and the per-segment scan, with segments
  *                            of *segment_length tokens
+ *   GDN_PLAN_PREPARED_SCAN   the state-independent preparation of every chunk
+ *                            in one parallel pass ("T precompute"), then the
+ *                            scan that consumes it with each head's state rows
+ *                            spread over two or four CUs (bf16, no checkpoints,
+ *                            at most half as many work items as CUs); bitwise
+ *                            the results of GDN_PLAN_SCAN.
+ *                            gdn_chunk_prefill_noalloc runs
+ *                            GDN_PLAN_PIPELINED_SCAN instead (no workspace).
  */
-enum gdn_plan_kind { GDN_PLAN_SCAN = 0, GDN_PLAN_PIPELINED_SCAN = 1, GDN_PLAN_SPLIT = 2 };
+enum gdn_plan_kind { GDN_PLAN_SCAN = 0, GDN_PLAN_PIPELINED_SCAN = 1, GDN_PLAN_SPLIT = 2, GDN_PLAN_PREPARED_SCAN = 3 };
 
 /* The plan for num_seqs sequences of num_tokens tokens in total, num_v_heads
  * value heads, q/k/v of io_dtype (GDN_F32 or GDN_BF16), with or without

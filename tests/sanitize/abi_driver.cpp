@@ -154,7 +154,7 @@ int main() {
                             const int rc = gdn_prefill_plan(N, T, Hv, dt, 0, bi, cu, &kind, &seg);
                             if (rc == GDN_OK) {
                                 ++plans;
-                                if (kind < 0 || kind > 2 || seg < 0 || (kind != GDN_PLAN_SPLIT && seg != 0) ||
+                                if (kind < 0 || kind > 3 || seg < 0 || (kind != GDN_PLAN_SPLIT && seg != 0) ||
                                     (kind == GDN_PLAN_SPLIT && (seg % 64 != 0 || bi))) {
                                     std::printf("FAIL plan N=%lld T=%lld Hv=%lld: kind %d seg %lld\n", (long long)N,
                                                 (long long)T, (long long)Hv, kind, (long long)seg);

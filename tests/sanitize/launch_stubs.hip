@@ -12,4 +12,6 @@ hipError_t launch_plan(const void *, int, int, int64_t, SegEntry *, int32_t *, i
     return hipErrorNotSupported;
 }
 hipError_t launch_fixup(const FixParams &, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_prep(const ScanParams &, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_prepared_scan(const ScanParams &, int, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace gdn

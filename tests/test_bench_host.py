@@ -29,11 +29,14 @@ SHAPES = {
 }
 
 
+PREPARED = "prepared: plan_kernel, fused_scan_kernel (preparation), prepared_scan_kernel"
+
+
 def test_scan_kernel_labels_of_the_five_workloads():
     cus = 256
     expect = {   # (batch_invariant 0, batch_invariant 1)
         "tiny_fp32": ("fused_scan_kernel", "fused_scan_kernel"),        # fp32 q/k/v
-        "varlen_bf16": ("piped_scan_kernel", "piped_scan_kernel"),      # 256 work items <= CUs
+        "varlen_bf16": ("piped_scan_kernel", "piped_scan_kernel"),      # 256 work items = CUs
         "many_short": ("fused_scan_kernel", "fused_scan_kernel"),       # 8192 work items
         "large_batch": ("fused_scan_kernel", "fused_scan_kernel"),      # 1024 work items
     }
@@ -43,7 +46,7 @@ def test_scan_kernel_labels_of_the_five_workloads():
         assert bench.scan_kernels(w, 1, cus) == k1, name
     w = SHAPES["long_single"]
     assert bench.scan_kernels(w, 0, cus).startswith("split")           # one sequence on 32 heads
-    assert bench.scan_kernels(w, 1, cus) == "piped_scan_kernel"
+    assert bench.scan_kernels(w, 1, cus) == PREPARED
     assert bench.scan_kernels(w, 1, cus, checkpoints=True) == "fused_scan_kernel"
 
 

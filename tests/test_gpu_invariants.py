@@ -30,9 +30,10 @@ def test_api_defaults_are_bitwise(gdn):
 
 @pytest.mark.parametrize("gate", ["sigmoid", "strong"])
 def test_batch_invariance_across_scan_kernels(gdn, gate):
-    """Launches with at most one work item per CU run the eight-wave pipelined
-    scan, larger ones the four-wave scan; both must give bitwise the same
-    results, or batch_invariant results would depend on the batch size.  A
+    """Launches with at most half as many work items as CUs run the prepared
+    scan, with at most one per CU the eight-wave pipelined scan, larger ones the
+    four-wave scan; all must give bitwise the same results, or batch_invariant
+    results would depend on the batch size.  A
     batch with more work items than CUs is compared with sequences of it run
     alone and with a sub-batch below the threshold.  "strong" gates put half
     of the sequences on the entry-wise exp path (chunk log-decay below -60)."""
@@ -65,6 +66,15 @@ def test_batch_invariance_across_scan_kernels(gdn, gate):
     assert torch.equal(f2, fin[:m])
     ro, rf = run_oracle(head)
     assert nerr(o2, ro) <= BF16_TOL and nerr(f2, rf) <= BF16_TOL
+    # sub-batches that take the prepared scan with 2 and 4 CUs per head
+    for m in (cus // (2 * Hv), cus // (4 * Hv)):
+        head = W.Workload(**{**w.__dict__, "q": w.q[:cu[m]], "k": w.k[:cu[m]], "v": w.v[:cu[m]], "g": w.g[:cu[m]],
+                             "beta": w.beta[:cu[m]], "cu_seqlens": w.cu_seqlens[:m + 1],
+                             "initial_state": w.initial_state[:m]})
+        assert gdn.prefill_plan(m, cu[m], Hv, torch.bfloat16, False, True, cus)[0] == "prepared_scan"
+        o3, f3 = run_gpu(gdn, head, True)
+        assert torch.equal(o3, out[:cu[m]]), m
+        assert torch.equal(f3, fin[:m]), m
 
 
 def test_run_to_run_bitwise(gdn):
@@ -302,3 +312,27 @@ def test_split_path_bf16_states(gdn):
     ro, rf = run_oracle(w)
     assert nerr(out, ro) <= BF16_TOL and nerr(fin, rf) <= BF16_TOL
     assert torch.equal(fin[1].cpu(), w.initial_state[1])
+
+
+@pytest.mark.parametrize("case", ["long_single", "four_8192"])
+def test_prepared_plan_equals_pipelined_scan(gdn, case):
+    """The prepared plan (every chunk's preparation in one parallel pass, then
+    the scan over it with each head's state rows spread over 4 CUs for the
+    65,536-token sequence, over 2 CUs for 4 x 8192 tokens on 32 heads) and the
+    pipelined scan (the no-allocation entry point's plan for the same launch)
+    give bitwise the same output and final state."""
+    if case == "long_single":
+        w = W.make(2, device="cuda")
+    else:
+        w = W.build([8192] * 4, 16, 32, torch.bfloat16, seed=64, device="cuda", name="four_8192")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert gdn.prefill_plan(w.N, w.T, w.Hv, w.q.dtype, False, True, cus)[0] == "prepared_scan"
+    res = []
+    for fn in (gdn.gdn_chunk_prefill, gdn.gdn_chunk_prefill_noalloc):
+        out = torch.full((w.T, w.Hv, 128), float("nan"), dtype=w.q.dtype, device=DEV)
+        fin = torch.full((w.N, w.Hv, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+        fn(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin, w.use_qk_l2norm, True, out)
+        torch.cuda.synchronize()
+        res.append((out, fin))
+    say(f"[gpu] prepared plan vs pipelined scan, {w.name}")
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])

@@ -15,9 +15,9 @@ def plan(N, T, Hv, dt=BF, ck=False, bi=False, cus=256):
 
 def test_the_five_workloads():
     assert plan(2, 128, 2, F32) == ("scan", 0)                      # fp32 q/k/v: four-wave scan
-    assert plan(8, 15230, 32) == ("pipelined_scan", 0)              # 256 work items = CUs
+    assert plan(8, 15230, 32) == ("pipelined_scan", 0)             # 256 work items = CUs
     assert plan(1, 65536, 32) == ("split", 4096)                    # one long sequence: 16 segments
-    assert plan(1, 65536, 32, bi=True) == ("pipelined_scan", 0)     # batch_invariant: never split
+    assert plan(1, 65536, 32, bi=True) == ("prepared_scan", 0)     # batch_invariant: never split
     assert plan(256, 32280, 32) == ("scan", 0)                      # 8192 work items
     assert plan(32, 262144, 32) == ("scan", 0)                      # the 32 x 8192 batch
 
@@ -26,22 +26,26 @@ def test_split_cost_model():
     # 8 x 8192 on 32 heads: two segments per sequence cost more than the unsplit scan
     assert plan(8, 8 * 8192, 32)[0] == "pipelined_scan"
     # 4 x 16384: four segments, the maps and the scan at two workgroups per CU: still unsplit
-    assert plan(4, 4 * 16384, 32)[0] == "pipelined_scan"
+    assert plan(4, 4 * 16384, 32)[0] == "prepared_scan"                 # 128 work items: 2 CUs each
     # 2 x 32768: eight segments pay off
     assert plan(2, 2 * 32768, 32) == ("split", 4096)
     # an average below four shortest segments is never split
-    assert plan(1, 4 * 1024 - 64, 4)[0] == "pipelined_scan"
+    assert plan(1, 4 * 1024 - 64, 4)[0] == "prepared_scan"
     assert plan(1, 4 * 1024, 4) == ("split", 1024)
 
 
-def test_pipelined_scan_threshold_and_exclusions():
-    assert plan(64, 64 * 100, 4)[0] == "pipelined_scan"             # 256 work items
-    assert plan(65, 65 * 100, 4)[0] == "scan"                       # 260 work items
-    assert plan(64, 64 * 100, 4, cus=128)[0] == "scan"              # fewer CUs
-    assert plan(8, 800, 4, dt=F32)[0] == "scan"                     # fp32 q/k/v
-    assert plan(8, 800, 4, ck=True)[0] == "scan"                    # checkpoints
-    assert plan(0, 0, 4) == ("pipelined_scan", 0)                   # empty batch: no work items
-    assert plan(0, 100000, 4) == ("pipelined_scan", 0)              # no sequences: never split
+def test_prepared_scan_threshold_and_exclusions():
+    assert plan(16, 16 * 100, 4)[0] == "prepared_scan"             # 64 work items: 4 CUs each
+    assert plan(32, 32 * 100, 4)[0] == "prepared_scan"             # 128 work items: 2 CUs each
+    assert plan(33, 33 * 100, 4)[0] == "pipelined_scan"            # 132 work items
+    assert plan(64, 64 * 100, 4)[0] == "pipelined_scan"            # 256 work items
+    assert plan(65, 65 * 100, 4)[0] == "scan"                      # 260 work items
+    assert plan(16, 16 * 100, 4, cus=128)[0] == "prepared_scan"    # 64 work items, 2 CUs each
+    assert plan(64, 64 * 100, 4, cus=128)[0] == "scan"             # fewer CUs
+    assert plan(8, 800, 4, dt=F32)[0] == "scan"                    # fp32 q/k/v
+    assert plan(8, 800, 4, ck=True)[0] == "scan"                   # checkpoints
+    assert plan(0, 0, 4) == ("prepared_scan", 0)                   # empty batch: no work items
+    assert plan(0, 100000, 4) == ("prepared_scan", 0)              # no sequences: never split
 
 
 @pytest.mark.parametrize("args", [(-1, 0, 4), (1, -1, 4), (1, 64, 0)])
