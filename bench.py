@@ -19,9 +19,16 @@ sequences (Hqk 16, Hv 32, bf16, fp32 state updated in place) and prints its
 own JSON line; it reads and writes the whole state once, so its roofline is
 HBM: bytes/step = state (2 Hv d^2 4B per sequence) + q, k, v, out, g, beta.
 
+Every configuration: ``--all`` prints one JSON line per workload (the five
+recipes of gdn_workloads.py) and batch_invariant mode, each with its host plan,
+the fp32 oracle's timing and the timed run's error against it; ``--table FILE``
+renders such lines as a markdown table.
+
 Other modes (used to produce the committed rocprofv3 summaries):
   --copy-calibration   a plain device copy of known size (for PMC scaling)
-  --summarize-pmc DIR  turn rocprofv3 --pmc outputs (rocpd .db) into profiles/*.txt
+  --summarize-plan DIR OUT  one call's kernels (trace, traffic, SQ counters) from
+                       the rocprofv3 output dirs DIR/{trace,fetch,write,sq1,sq2}
+  --summarize-pmc DIR  (with --decode) the decode kernel's traffic summary
   --summarize-trace DIR OUT  kernel-trace statistics (rocpd .db) into a text summary
 """
 import argparse
@@ -40,10 +47,6 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 D, C = 128, 64
 KERNEL = "fused_scan_kernel"
-# sources of the scan kernel: traffic counters count only while these are unchanged
-KERNEL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_prefill_amd", "csrc", f)
-               for f in ("gdn_scan.hip", "gdn_device.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_scan_large_batch.txt")
 DECODE_KERNEL = "decode_kernel"
 DECODE_SRCS = [os.path.join(ROOT, "chunked_gated_delta_prefill_amd", "csrc", "gdn_decode.hip")]
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_kernel_decode_batch.txt")
@@ -74,14 +77,14 @@ def scan_kernels(w, batch_invariant, cus, checkpoints=False, noalloc=False):
             "split": "split: plan_kernel, fused_scan_kernel (maps N, M), fixup_kernel, fused_scan_kernel"}[kind]
 
 
-def kernel_source_sha(srcs=None):
+def kernel_source_sha(srcs):
     h = hashlib.sha256()
-    for f in srcs or KERNEL_SRCS:
+    for f in srcs:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(path=TRAFFIC_FILE, srcs=None):
+def read_traffic(path, srcs):
     """HBM bytes per launch measured by rocprofv3 PMC runs, if they were taken
     on the current kernel source; else None."""
     if not os.path.exists(path):
@@ -263,35 +266,11 @@ def summarize_trace(base, out_path, command, last=0, kernel=KERNEL):
     print("\n".join(lines))
 
 
-def summarize_counters(dirs, out_path, commands):
-    """Median per-dispatch value of every counter found for the scan kernel in
-    the rocprofv3 --pmc output directories `dirs`; writes a text summary."""
-    import sqlite3
-    vals = {}
-    for d in dirs:
-        for f in _db_files(d):
-            con = sqlite3.connect(f)
-            for disp, kname, cname, v in con.execute(
-                    "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
-                if KERNEL in kname and "kScan" not in cname:
-                    vals.setdefault(cname, {}).setdefault((f, disp), 0.0)
-                    vals[cname][(f, disp)] += float(v)
-            con.close()
-    lines = ["# rocprofv3 --pmc counters of fused_scan_kernel (median over dispatches, summed over the device)"]
-    lines += [f"# command: {c}" for c in commands]
-    for cname in sorted(vals):
-        lines.append(f"{cname} = {statistics.median(vals[cname].values()):.0f}")
-    open(out_path, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines))
-
-
-SCAN_TRAFFIC_TITLE = "# HBM traffic of fused_scan_kernel, large_batch workload (32 x 8192 tokens, Hqk 16, Hv 32, bf16)"
 DECODE_TRAFFIC_TITLE = ("# HBM traffic of decode_kernel, decode_batch workload (256 one-token sequences, Hqk 16, Hv 32, "
                         "fp32 state updated in place)")
 
 
-def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes, kernel=KERNEL, out_path=TRAFFIC_FILE,
-                  srcs=None, title=SCAN_TRAFFIC_TITLE):
+def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes, kernel, out_path, srcs, title):
     """Reads four rocprofv3 --pmc output dirs (kernel FETCH_SIZE, WRITE_SIZE;
     copy FETCH_SIZE, WRITE_SIZE) and writes the traffic summary file."""
     kf = _pmc_values(os.path.join(base, "pmc_fetch"), kernel, "FETCH_SIZE")
@@ -330,6 +309,198 @@ def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes, 
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+# Kernels one gdn_chunk_prefill call launches, in launch order, per host plan
+# (gdn_prefill_plan); the fused scan kernel runs in several modes.
+PLAN_SEQUENCE = {
+    "scan": ["fused_scan_kernel"],
+    "pipelined_scan": ["piped_scan_kernel"],
+    "prepared_scan": ["plan_kernel", "fused_scan_kernel (preparation)", "prepared_scan_kernel"],
+    "split": ["plan_kernel", "fused_scan_kernel (map N)", "fused_scan_kernel (map M)", "fixup_kernel",
+              "fused_scan_kernel (segment scan)"],
+}
+GDN_KERNELS = ("fused_scan_kernel", "piped_scan_kernel", "prepared_scan_kernel", "plan_kernel", "fixup_kernel",
+               "decode_kernel")
+ALL_SRCS = [os.path.join(ROOT, "chunked_gated_delta_prefill_amd", "csrc", f)
+            for f in ("gdn_api.hip", "gdn_scan.hip", "gdn_scan_piped.hip", "gdn_scan_prepared.hip", "gdn_split.hip",
+                      "gdn_device.h", "gdn_internal.h")]
+SQ_PASSES = (
+    "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM SQ_WAVE_CYCLES SQ_BUSY_CYCLES",
+    "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS "
+    "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAIT_ANY SQ_INSTS_SMEM",
+)
+
+
+def _gdn_base(name):
+    for k in GDN_KERNELS:
+        if k in str(name):
+            return k
+    return None
+
+
+def _group_calls(names, seq):
+    """Splits the launch-ordered gdn kernel names of a run into calls of the
+    plan's kernel sequence; returns the call index of every dispatch."""
+    bases = [s.split(" (")[0] for s in seq]
+    if len(names) % len(seq):
+        raise ValueError(f"{len(names)} gdn dispatches are not whole calls of {seq}")
+    for i, n in enumerate(names):
+        if _gdn_base(n) != bases[i % len(seq)]:
+            raise ValueError(f"dispatch {i} is {n}, expected {bases[i % len(seq)]}")
+    return [i // len(seq) for i in range(len(names))]
+
+
+def _trace_calls(d, seq):
+    """Per-position durations (us) of the gdn dispatches in the trace under d,
+    grouped into calls: list over positions of lists over calls."""
+    import sqlite3
+    rows = []
+    for f in _db_files(d):
+        con = sqlite3.connect(f)
+        cur = con.execute("select * from kernels")
+        cols = [c[0] for c in cur.description]
+        ni, si, ei = cols.index("name"), cols.index("start"), cols.index("end")
+        rows += [(r[si], r[ei], r[ni]) for r in cur.fetchall() if _gdn_base(r[ni])]
+        con.close()
+    rows.sort()
+    _group_calls([r[2] for r in rows], seq)
+    per = [[] for _ in seq]
+    for i, (s0, e0, _) in enumerate(rows):
+        per[i % len(seq)].append((e0 - s0) / 1e3)
+    return per
+
+
+def _pmc_calls(d, seq):
+    """{counter: per-position lists over calls} of the gdn dispatches under d."""
+    import sqlite3
+    disp = {}
+    for f in _db_files(d):
+        con = sqlite3.connect(f)
+        for did, kname, cname, v in con.execute(
+                "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+            if _gdn_base(kname):
+                e = disp.setdefault((f, did), [kname, {}])
+                e[1][cname] = e[1].get(cname, 0.0) + float(v)
+        con.close()
+    order = sorted(disp)
+    _group_calls([disp[k][0] for k in order], seq)
+    out = {}
+    for i, k in enumerate(order):
+        for cname, v in disp[k][1].items():
+            out.setdefault(cname, [[] for _ in seq])[i % len(seq)].append(v)
+    return out
+
+
+def summarize_plan(base, out_path, w, bi, plan, commands, alg_bytes, timed_calls):
+    """One summary file per (workload, batch_invariant): every kernel the call
+    launches with its trace duration, HBM traffic (FETCH_SIZE / WRITE_SIZE
+    scaled by a plain copy's counters) and SQ counters.  base holds the
+    rocprofv3 output dirs trace, fetch, write, sq1, sq2 and, one level up,
+    copy_fetch, copy_write."""
+    seq = PLAN_SEQUENCE[plan]
+    med = statistics.median
+    tr = _trace_calls(os.path.join(base, "trace"), seq)
+    fe = _pmc_calls(os.path.join(base, "fetch"), seq)["FETCH_SIZE"]
+    wr = _pmc_calls(os.path.join(base, "write"), seq)["WRITE_SIZE"]
+    sq = {**_pmc_calls(os.path.join(base, "sq1"), seq), **_pmc_calls(os.path.join(base, "sq2"), seq)}
+    up = os.path.dirname(base.rstrip("/"))
+    cf = _pmc_values(os.path.join(up, "copy_fetch"), "copyBuffer", "FETCH_SIZE")
+    cw = _pmc_values(os.path.join(up, "copy_write"), "copyBuffer", "WRITE_SIZE")
+    f_fac = float(1 << 30) / (med(cf) * 1024.0)
+    w_fac = float(1 << 30) / (med(cw) * 1024.0)
+    lines = [f"# Kernels of one gdn_chunk_prefill call: {plan} plan, workload {w.name} ({w.N} sequences, {w.T} "
+             f"tokens, Hqk {w.Hqk}, Hv {w.Hv}, {str(w.q.dtype).replace('torch.', '')}), batch_invariant {bi}",
+             "# durations: rocprofv3 --kernel-trace, the last timed calls (warmup excluded);",
+             "# traffic: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch, median over calls), each",
+             "#   scaled by the same counter read for a plain 1 GiB device-to-device copy;",
+             "# SQ counters: median per dispatch, summed over the device.  Derived: per_wave = INSTS / SQ_WAVES;",
+             "#   mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (SQ_BUSY_CYCLES / 32 shader engines);",
+             "#   lds_conflict_ratio = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS"]
+    lines += [f"# {k} command: {c}" for k, c in commands.items()]
+    lines += [f"kernel_source_sha = {kernel_source_sha(ALL_SRCS)}",
+              f"fetch_scale = {f_fac:.4f}", f"write_scale = {w_fac:.4f}"]
+    tot_us, tot_bytes = 0.0, 0.0
+    for i, name in enumerate(seq):
+        durs = tr[i][-timed_calls:]
+        fb = med(fe[i]) * 1024.0 * f_fac
+        wb = med(wr[i]) * 1024.0 * w_fac
+        tot_us += statistics.fmean(durs)
+        tot_bytes += fb + wb
+        lines += ["", f"[{name}]", f"timed_dispatches = {len(durs)}",
+                  f"average_us = {statistics.fmean(durs):.3f}", f"median_us = {med(durs):.3f}",
+                  f"fetch_bytes = {fb:.0f}", f"write_bytes = {wb:.0f}",
+                  f"hbm_gbs = {(fb + wb) / (statistics.fmean(durs) * 1e3):.1f}"]
+        vals = {c: med(v[i]) for c, v in sq.items() if v[i]}
+        lines += [f"{c} = {vals[c]:.0f}" for c in sorted(vals)]
+        waves = vals.get("SQ_WAVES", 0.0)
+        if waves:
+            for c in ("VALU", "MFMA", "LDS", "SALU", "VMEM"):
+                if f"SQ_INSTS_{c}" in vals:
+                    lines.append(f"{c.lower()}_per_wave = {vals[f'SQ_INSTS_{c}'] / waves:.1f}")
+        if vals.get("SQ_BUSY_CYCLES") and "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            lines.append(f"mfma_busy = {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (vals['SQ_BUSY_CYCLES'] / 32):.3f}")
+        if vals.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in vals:
+            lines.append(f"lds_conflict_ratio = {vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_ACTIVE_INST_LDS']:.3f}")
+    lines[9:9] = [f"call_average_us = {tot_us:.3f}", f"hbm_bytes_per_call = {tot_bytes:.0f}",
+                  f"algorithmic_bytes_per_call = {alg_bytes:.0f}",
+                  f"traffic_over_algorithmic = {tot_bytes / alg_bytes:.3f}"]
+    os.makedirs(os.path.dirname(out_path) or ".", exist_ok=True)
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def plan_profile_path(workload, bi, plan):
+    return os.path.join(ROOT, "profiles", f"plan_{plan}_{workload}_bi{int(bi)}.txt")
+
+
+def read_plan_traffic(path):
+    """HBM bytes per call from a per-plan summary taken on the current sources."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if line.startswith("["):
+            break
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha(ALL_SRCS):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+TABLE_HEAD = ("| Workload | batch_invariant | plan | call (ms) | tokens/s | TFLOP/s (% bf16 peak) | "
+              "algorithmic GB/s (% of 8 TB/s) | measured traffic / algorithmic | max_norm_err out, state |\n"
+              "|---|---|---|---|---|---|---|---|---|")
+
+
+def render_table(path):
+    """Markdown table of the JSON lines in `path` (bench.py --all output)."""
+    rows = [TABLE_HEAD]
+    for line in open(path):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        r = json.loads(line)
+        cfg, rf, e = r["config"], r["roofline"], r.get("max_norm_err") or {}
+        tr = rf.get("traffic")
+        if tr is None:   # the plan's committed summary, when it was taken on the current sources
+            for b in dict.fromkeys((int(cfg["batch_invariant"]), 0)):
+                path = plan_profile_path(cfg["workload"], b, r.get("plan", "?"))
+                if os.path.exists(path):
+                    tr = read_plan_traffic(path)
+                    break
+        err = (f"{e['out']:.1e}, " + ("-" if e.get("state") is None else f"{e['state']:.1e}")) if e else "-"
+        ratio = "-" if tr is None else f"{tr / rf['algorithmic_bytes']:.2f}"
+        rows.append(f"| {cfg['workload']} | {int(cfg['batch_invariant'])} | {r.get('plan', '?')} | "
+                    f"{r['kernel_ms']:.3f} | {r['value'] / 1e6:.1f} M | {r['tflops']:.0f} ({100 * r['mfma_frac']:.1f}%) | "
+                    f"{rf['achieved']:.0f} ({100 * rf['frac']:.1f}%) | "
+                    f"{ratio} | {err} |")
+    return "\n".join(rows)
 
 
 def decode_bytes(w):
@@ -410,6 +581,112 @@ def bench_decode(args, gdn, W):
     print(json.dumps(res), flush=True)
 
 
+def bench_prefill(args, gdn, w, bi, peaks, oracle_ref):
+    """Times gdn_chunk_prefill on workload w (already on the device) and returns
+    the result record; oracle_ref is cpu_baseline()'s return value or None."""
+    import torch
+    flops, byts = algorithmic(w)
+
+    out = torch.empty(w.T, w.Hv, D, dtype=w.q.dtype, device="cuda")
+    fin = None if w.state_dtype is None else torch.empty(w.N, w.Hv, D, D, dtype=w.state_dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    ck_every = args.checkpoint_interval
+    if ck_every:
+        per_seq = max(1, max(w.lengths()) // ck_every)
+        ck = torch.empty(w.N * per_seq, w.Hv, D, D, dtype=torch.float32, device="cuda")
+        byts += sum(L // ck_every for L in w.lengths()) * w.Hv * D * D * 4   # checkpoint writes
+
+    if args.pooled:
+        pool = w.initial_state.clone()
+        pidx = torch.arange(w.N - 1, -1, -1, dtype=torch.int32, device="cuda")
+
+    def step():
+        if args.pooled:
+            gdn.gdn_chunk_prefill_pooled(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, pool, pidx,
+                                         w.use_qk_l2norm, bool(bi), out, stream)
+        elif ck_every:
+            gdn.gdn_chunk_prefill_checkpointed(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state,
+                                               fin, w.use_qk_l2norm, bool(bi), ck, per_seq,
+                                               ck_every, out, stream)
+        else:
+            fn = gdn.gdn_chunk_prefill_noalloc if args.noalloc else gdn.gdn_chunk_prefill
+            fn(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin, w.use_qk_l2norm,
+               bool(bi), out, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch durations with events on the launch stream (one kernel per call)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = statistics.mean(launch_ms)
+    value = w.T / (ms_step / 1e3)
+    achieved = byts / (kern_ms / 1e3) / 1e9
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan, _ = gdn.prefill_plan(w.N, w.T, w.Hv, w.q.dtype, bool(ck_every), bool(bi), cus)
+    if args.noalloc and plan == "prepared_scan":
+        plan = "pipelined_scan"
+    # measured traffic of the whole call, from the plan's committed summary when it
+    # was taken on the current sources for this workload (plain entry point only)
+    traffic = None
+    if args.variant is None and not (ck_every or args.pooled or args.noalloc):
+        for b in dict.fromkeys((int(bi), 0)):
+            path = plan_profile_path(w.name, b, plan)
+            if os.path.exists(path):
+                traffic = read_plan_traffic(path)
+                break
+    res = {
+        "metric": "GDN prefill tokens/s and TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.q.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "sequences": w.N, "tokens": w.T, "hqk": w.Hqk, "hv": w.Hv,
+                   "head_dim": D, "state": str(w.initial_state.dtype).replace("torch.", "")
+                   if w.initial_state is not None else None, "l2norm": w.use_qk_l2norm,
+                   "batch_invariant": bool(bi),
+                   **({"checkpoint_interval": ck_every} if ck_every else {}),
+                   **({"entry": "gdn_chunk_prefill_noalloc"} if args.noalloc else {}),
+                   **({"pooled": True} if args.pooled else {})},
+        "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
+        "mfma_frac": round(flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": round(kern_ms, 4),
+        "kernel_ms_p20_p80": [round(sorted(launch_ms)[int(0.2 * (len(launch_ms) - 1))], 4),
+                              round(sorted(launch_ms)[int(0.8 * (len(launch_ms) - 1))], 4)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": scan_kernels(w, bi, cus, bool(ck_every), args.noalloc),
+                     "algorithmic_bytes": byts, "algorithmic_flops": flops},
+        "cpu_baseline": None,
+        # the realised sequence boundaries of the seeded workload
+        "cu_seqlens": [int(x) for x in w.cu_seqlens.cpu().tolist()],
+    }
+    res["plan"] = plan
+    res["achievable"] = {**peaks, "mfma_frac_of_mm": round(flops / (ms_step / 1e3) / 1e12 / peaks["bf16_mm_tflops"], 4),
+                         "hbm_frac_of_copy": round(achieved / peaks["copy_gbs"], 4)}
+    if oracle_ref is not None:
+        rec, (ro, rf), take, end = oracle_ref
+        res["cpu_baseline"] = rec
+        # the timed run's own output and final state against the oracle (same sample)
+        if args.pooled:   # the pool is updated in place by every step: no fixed reference
+            res["max_norm_err"] = None
+        else:
+            res["max_norm_err"] = {"out": max_norm_err(out[:end], ro),
+                                   "state": None if fin is None else max_norm_err(fin[:take], rf),
+                                   "reference": "fp32 oracle", "sample": rec["sample"].split(" (")[0]}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,8 +701,6 @@ def main():
     ap.add_argument("--summarize-pmc", default=None)
     ap.add_argument("--pmc-commands", default="{}")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"), default=None)
-    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
-                    help="rocprofv3 --pmc output dirs; the last argument is the output file")
     ap.add_argument("--decode", action="store_true", help="time the decode step instead of the prefill")
     ap.add_argument("--noalloc", action="store_true",
                     help="time gdn_chunk_prefill_noalloc (no workspace: the pipelined scan where the allocating "
@@ -434,6 +709,13 @@ def main():
                     help="states in an indexed pool (gdn_chunk_prefill_pooled, reversed index order)")
     ap.add_argument("--checkpoint-interval", type=int, default=0,
                     help="tokens between state checkpoints (gdn_chunk_prefill_checkpointed); 0 = plain scan")
+    ap.add_argument("--all", action="store_true",
+                    help="one JSON line per configuration (all five) and batch_invariant mode")
+    ap.add_argument("--table", default=None, metavar="FILE",
+                    help="markdown table of the JSON lines in FILE (the output of --all)")
+    ap.add_argument("--summarize-plan", nargs=2, metavar=("DIR", "OUT"), default=None,
+                    help="per-kernel summary of a plan's rocprofv3 runs under DIR (trace, fetch, write, sq1, sq2)")
+    ap.add_argument("--cus", type=int, default=256, help="with --summarize-plan: compute units the plan assumed")
     ap.add_argument("--trace-command", default="?")
     ap.add_argument("--trace-kernel", default=KERNEL, help="with --summarize-trace: kernel name to average")
     ap.add_argument("--trace-last", type=int, default=0,
@@ -447,10 +729,6 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
-        return
-    if args.summarize_counters:
-        summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1],
-                           json.loads(args.pmc_commands).get("commands", []))
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_command, args.trace_last,
@@ -473,105 +751,30 @@ def main():
             return
         bench_decode(args, gdn, W)
         return
-    w = W.make(args.workload, device="cuda", variant=args.variant)
-    flops, byts = algorithmic(w)
-    if args.summarize_pmc:
-        cmds = json.loads(args.pmc_commands)
-        summarize_pmc(args.summarize_pmc, cmds.get("fetch", "?"), cmds.get("write", "?"),
-                      cmds.get("copy_fetch", "?"), cmds.get("copy_write", "?"), byts)
+    if args.table:
+        print(render_table(args.table))
         return
-
-    out = torch.empty(w.T, w.Hv, D, dtype=w.q.dtype, device="cuda")
-    fin = None if w.state_dtype is None else torch.empty(w.N, w.Hv, D, D, dtype=w.state_dtype, device="cuda")
-    stream = torch.cuda.current_stream()
-    ck_every = args.checkpoint_interval
-    if ck_every:
-        per_seq = max(1, max(w.lengths()) // ck_every)
-        ck = torch.empty(w.N * per_seq, w.Hv, D, D, dtype=torch.float32, device="cuda")
-        byts += sum(L // ck_every for L in w.lengths()) * w.Hv * D * D * 4   # checkpoint writes
-
-    if args.pooled:
-        pool = w.initial_state.clone()
-        pidx = torch.arange(w.N - 1, -1, -1, dtype=torch.int32, device="cuda")
-
-    def step():
-        if args.pooled:
-            gdn.gdn_chunk_prefill_pooled(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, pool, pidx,
-                                         w.use_qk_l2norm, bool(args.batch_invariant), out, stream)
-        elif ck_every:
-            gdn.gdn_chunk_prefill_checkpointed(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state,
-                                               fin, w.use_qk_l2norm, bool(args.batch_invariant), ck, per_seq,
-                                               ck_every, out, stream)
-        else:
-            fn = gdn.gdn_chunk_prefill_noalloc if args.noalloc else gdn.gdn_chunk_prefill
-            fn(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin, w.use_qk_l2norm,
-               bool(args.batch_invariant), out, stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # per-launch durations with events on the launch stream (one kernel per call)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in evs:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_step = wall * 1e3 / args.steps
-    kern_ms = statistics.mean(launch_ms)
-    value = w.T / (ms_step / 1e3)
-    achieved = byts / (kern_ms / 1e3) / 1e9
-    # the counters were taken on the unsplit 32 x 8192 batch: no other workload carries them
-    profiled = (args.workload == "large_batch" and args.variant is None and not (ck_every or args.pooled)
-                and not args.noalloc)
-    traffic = read_traffic() if profiled else None
-    res = {
-        "metric": "GDN prefill tokens/s and TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU",
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.q.dtype == torch.bfloat16 else "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "sequences": w.N, "tokens": w.T, "hqk": w.Hqk, "hv": w.Hv,
-                   "head_dim": D, "state": str(w.initial_state.dtype).replace("torch.", "")
-                   if w.initial_state is not None else None, "l2norm": w.use_qk_l2norm,
-                   "batch_invariant": bool(args.batch_invariant),
-                   **({"checkpoint_interval": ck_every} if ck_every else {}),
-                   **({"entry": "gdn_chunk_prefill_noalloc"} if args.noalloc else {}),
-                   **({"pooled": True} if args.pooled else {})},
-        "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
-        "mfma_frac": round(flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "kernel_ms": round(kern_ms, 4),
-        "kernel_ms_p20_p80": [round(sorted(launch_ms)[int(0.2 * (len(launch_ms) - 1))], 4),
-                              round(sorted(launch_ms)[int(0.8 * (len(launch_ms) - 1))], 4)],
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": scan_kernels(w, args.batch_invariant,
-                                            torch.cuda.get_device_properties(0).multi_processor_count,
-                                            bool(ck_every), args.noalloc),
-                     "algorithmic_bytes": byts, "algorithmic_flops": flops},
-        "cpu_baseline": None,
-        # the realised sequence boundaries of the seeded workload
-        "cu_seqlens": [int(x) for x in w.cu_seqlens.cpu().tolist()],
-    }
+    if args.summarize_plan:
+        import torch
+        w = W.make(args.workload, device="cpu", variant=args.variant)
+        plan, _ = gdn.prefill_plan(w.N, w.T, w.Hv, w.q.dtype, False, bool(args.batch_invariant), args.cus)
+        summarize_plan(args.summarize_plan[0], args.summarize_plan[1], w, args.batch_invariant, plan,
+                       json.loads(args.pmc_commands), algorithmic(w)[1], args.trace_last or 20)
+        return
     peaks = achievable_peaks()
-    res["achievable"] = {**peaks, "mfma_frac_of_mm": round(flops / (ms_step / 1e3) / 1e12 / peaks["bf16_mm_tflops"], 4),
-                         "hbm_frac_of_copy": round(achieved / peaks["copy_gbs"], 4)}
-    if not args.no_cpu_baseline:
-        rec, (ro, rf), take, end = cpu_baseline(w, args.cpu_sample_seqs)
-        res["cpu_baseline"] = rec
-        # the timed run's own output and final state against the oracle (same sample)
-        if args.pooled:   # the pool is updated in place by every step: no fixed reference
-            res["max_norm_err"] = None
-        else:
-            res["max_norm_err"] = {"out": max_norm_err(out[:end], ro),
-                                   "state": None if fin is None else max_norm_err(fin[:take], rf),
-                                   "reference": "fp32 oracle", "sample": rec["sample"].split(" (")[0]}
-        del ro, rf
+    if args.all:
+        # one line per configuration and batch_invariant mode; the oracle runs once per workload
+        for name in W.CONFIG_NAMES:
+            w = W.make(name, device="cuda", variant=args.variant)
+            ref = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_seqs)
+            for bi in (0, 1):
+                print(json.dumps(bench_prefill(args, gdn, w, bi, peaks, ref)), flush=True)
+            del w, ref
+            torch.cuda.empty_cache()
+        return
+    w = W.make(args.workload, device="cuda", variant=args.variant)
+    ref = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_seqs)
+    res = bench_prefill(args, gdn, w, args.batch_invariant, peaks, ref)
     print(json.dumps(res), flush=True)
 
 

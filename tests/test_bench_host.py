@@ -64,3 +64,85 @@ def test_max_norm_err_on_host_tensors():
     got = torch.tensor([[1.0, -3.9], [2.2, 0.5]])
     assert abs(bench.max_norm_err(got, ref) - 0.2 / 4.0) < 1e-6
     assert bench.max_norm_err(got[:0], ref[:0]) == 0.0
+
+
+def _fake_rocpd(path, trace=None, counters=None):
+    """A database with the two rocpd views bench.py reads: kernels (name,
+    start, end in ns) and counters_collection (dispatch_id, kernel_name,
+    counter_name, value)."""
+    import sqlite3
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    con = sqlite3.connect(path)
+    con.execute("create table kernels (name text, start integer, end integer)")
+    con.execute("create table counters_collection (dispatch_id integer, kernel_name text, counter_name text, "
+                "value real)")
+    for row in trace or []:
+        con.execute("insert into kernels values (?, ?, ?)", row)
+    for row in counters or []:
+        con.execute("insert into counters_collection values (?, ?, ?, ?)", row)
+    con.commit()
+    con.close()
+
+
+def test_plan_summary_groups_dispatches_into_calls(tmp_path):
+    """bench.summarize_plan: gdn dispatches are grouped into calls of the plan's
+    kernel sequence (other kernels ignored), durations averaged per position,
+    traffic scaled by the copy's counters, per-wave counts derived."""
+    seq = bench.PLAN_SEQUENCE["split"]
+    names = ["_ZN3gdn12_GLOBAL__N_111plan_kernelEv", "_ZN3gdn12_GLOBAL__N_117fused_scan_kernelILi1E",
+             "_ZN3gdn12_GLOBAL__N_117fused_scan_kernelILi2E", "gdn::anon::fixup_kernel",
+             "_ZN3gdn12_GLOBAL__N_117fused_scan_kernelILi0E"]
+    base = tmp_path / "case"
+    trace, t = [], 0
+    for call in range(3):
+        trace.append(("at::native::copy_kernel", t, t + 999))   # not a gdn kernel
+        for i, n in enumerate(names):
+            trace.append((n, t, t + 1000 * (i + 1) + call))      # position i lasts ~(i + 1) us
+            t += 10000
+    _fake_rocpd(str(base / "trace" / "a.db"), trace=trace)
+    disp = [(len(names) * call + i, n) for call in range(3) for i, n in enumerate(names)]   # launch order
+    for sub, cnt in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        _fake_rocpd(str(base / sub / "a.db"), counters=[(d, n, cnt, 2.0) for d, n in disp])
+    _fake_rocpd(str(base / "sq1" / "a.db"),
+                counters=[(d, n, c, v) for d, n in disp for c, v in (("SQ_WAVES", 4.0), ("SQ_INSTS_VALU", 400.0))])
+    _fake_rocpd(str(base / "sq2" / "a.db"),
+                counters=[(d, n, c, v) for d, n in disp
+                          for c, v in (("SQ_LDS_BANK_CONFLICT", 1.0), ("SQ_ACTIVE_INST_LDS", 4.0))])
+    _fake_rocpd(str(tmp_path / "copy_fetch" / "a.db"), counters=[(1, "copyBuffer", "FETCH_SIZE", 524288.0)])
+    _fake_rocpd(str(tmp_path / "copy_write" / "a.db"), counters=[(1, "copyBuffer", "WRITE_SIZE", 1048576.0)])
+    w = SimpleNamespace(name="long_single", N=1, T=65536, Hqk=16, Hv=32, q=torch.empty(0, dtype=torch.bfloat16))
+    out = tmp_path / "summary.txt"
+    bench.summarize_plan(str(base), str(out), w, 0, "split", {"trace": "cmd"}, 1000.0, 2)
+    kv, block = {}, "head"
+    for line in out.read_text().splitlines():
+        if line.startswith("["):
+            block = line.strip("[]")
+        elif "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[(block, a.strip())] = b.strip()
+    assert [b for b in dict.fromkeys(k[0] for k in kv) if b != "head"] == seq
+    # the last 2 calls: position i lasts (i + 1) us + call index (1, 2) ns
+    for i, name in enumerate(seq):
+        assert abs(float(kv[(name, "average_us")]) - (i + 1 + 0.0015)) < 1e-3
+        assert float(kv[(name, "fetch_bytes")]) == 2.0 * 1024 * 2.0   # 2 KiB, fetch scale 2
+        assert float(kv[(name, "write_bytes")]) == 2.0 * 1024 * 1.0
+        assert float(kv[(name, "valu_per_wave")]) == 100.0
+        assert float(kv[(name, "lds_conflict_ratio")]) == 0.25
+    assert abs(float(kv[("head", "call_average_us")]) - (15 + 5 * 0.0015)) < 1e-3
+    assert float(kv[("head", "hbm_bytes_per_call")]) == 5 * 3 * 2048.0
+    # a run whose dispatches do not follow the plan's sequence is refused
+    import pytest
+    with pytest.raises(ValueError):
+        bench.summarize_plan(str(base), str(out), w, 0, "prepared_scan", {}, 1000.0, 2)
+
+
+def test_table_from_bench_lines(tmp_path):
+    line = {"config": {"workload": "large_batch", "batch_invariant": False}, "plan": "scan", "kernel_ms": 2.0,
+            "value": 1.25e8, "tflops": 520.0, "mfma_frac": 0.208,
+            "roofline": {"achieved": 3200.0, "frac": 0.4, "traffic": 7.2e9, "algorithmic_bytes": 6.64e9},
+            "max_norm_err": {"out": 7e-3, "state": 4e-3}}
+    f = tmp_path / "lines.txt"
+    f.write_text("noise\n" + __import__("json").dumps(line) + "\n")
+    t = bench.render_table(str(f)).splitlines()
+    assert len(t) == 3 and t[2].startswith("| large_batch | 0 | scan | 2.000 | 125.0 M | 520 (20.8%) | 3200 (40.0%)")
+    assert "| 1.08 |" in t[2] and "7.0e-03, 4.0e-03" in t[2]
