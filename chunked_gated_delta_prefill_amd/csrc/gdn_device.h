@@ -245,16 +245,20 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return x;
 }
 
-// bf16 K and Q tiles in LDS: rows of 128 values padded to kKqLd, row r stored at
-// row kq_row(r), which permutes each aligned group of 8 rows as 0 2 4 6 1 3 5 7.
-// With the 4-dword pad, 8 consecutive rows at one column (16-byte operand reads)
-// start in 8 different bank quads, and 4 consecutive rows at 32-byte spans
-// (transposing 8-byte reads) fall two quads apart, so both patterns, like the
-// 16-byte staging writes along a row, touch 32 distinct banks per group of lanes
-// the LDS serves together.  The permutation is a per-lane constant for every
-// access, so it costs no address arithmetic beyond the base.
+// bf16 K and Q tiles in LDS: rows of 128 values padded to kKqLd (272 bytes, 4
+// banks past a multiple of the 64 four-byte banks), row r stored at row
+// kq_row(r), which transposes each aligned group of 16 rows as a 4 x 4 block
+// (r = 4a + b goes to 4b + a).  A half-wave's 8-byte LDS reads finish in one
+// pass only when they touch 64 distinct banks.  The transposing K^T reads of the
+// state update take 4 consecutive tokens x 64 bytes per half-wave: after the
+// permutation those rows sit 16 banks apart, so the half-wave covers all 64
+// banks (with consecutive rows 4 banks apart they overlapped two-way).  16-byte
+// operand reads of 16 consecutive rows at one column still land on 16 distinct
+// bank quads, and the 16-byte staging writes run along one row, so neither
+// conflicts.  The permutation is a per-lane constant for every access, so it
+// costs no address arithmetic beyond the base.
 constexpr int kKqLd = 136;
-__device__ __forceinline__ int kq_row(int r) { return (r & ~7) | (2 * (r & 3) + ((r >> 2) & 1)); }
+__device__ __forceinline__ int kq_row(int r) { return (r & ~15) | (4 * (r & 3) + ((r >> 2) & 3)); }
 __device__ __forceinline__ int kq_off(int row, int col) { return kq_row(row) * kKqLd + col; }
 // 32x32 operand in natural order from a K or Q tile: step s covers columns
 // [16 s, 16 s + 16), half h holds the 8 consecutive columns 16 s + 8 h ..
@@ -281,8 +285,8 @@ __device__ __forceinline__ bf16x8 ld_acc_tr(const bf16 *Ks, int m0, int cb, int 
     const bf16 *p = Ks + kq_off(cb + 16 * s + 4 * h + (i >> 2), m0 + 16 * g16 + 4 * qs);
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    // 8 rows further down: kq_row(r + 8) = kq_row(r) + 8
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 8 * kKqLd));
+    // 8 tokens further down: kq_row(r + 8) = kq_row(r) + 2 for r % 16 < 8
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 2 * kKqLd));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
