@@ -271,6 +271,11 @@ struct Plan {
     int64_t lseg;   // segment length of the split path (0 without a split)
     int np;         // prepared scan: blocks of 32 state rows per workgroup (1 or 2)
 };
+// Largest prepared-chunk workspace (one slot per chunk and value head, ~208 bytes
+// per token and head) a call takes; beyond it the pipelined scan prepares each
+// chunk beside the state work instead.
+constexpr double kPrepBudget = 8.0 * (1ull << 30);
+
 Plan make_plan(int64_t N, int64_t T, int64_t Hv, bool bf, bool ck, bool batch_invariant, int cus) {
     // Split path (T precompute -> MN precompute -> state fix-up -> CP prefill) when
     // one work item per (sequence, head) leaves the GPU under-filled and the
@@ -314,6 +319,9 @@ Plan make_plan(int64_t N, int64_t T, int64_t Hv, bool bf, bool ck, bool batch_in
     // chunk c + 1 beside the state work of chunk c.  Both give bitwise the results
     // of the four-wave scan, so the choice keeps batch_invariant results
     // independent of the batch.
+    const double prep_bytes =
+        (double)(T / ((int64_t)gdn::kChunk * gdn::kPrepChunks) + N + 1) * gdn::kPrepChunks * Hv * gdn::kPrepSlot;
+    if (bf && !ck && N * Hv <= cus && prep_bytes > kPrepBudget) return {GDN_PLAN_PIPELINED_SCAN, 0, 0};
     if (bf && !ck && N * Hv <= cus) {
         if (N * Hv * 4 <= cus) return {GDN_PLAN_PREPARED_SCAN, 0, 1};
         if (N * Hv * 2 <= cus) return {GDN_PLAN_PREPARED_SCAN, 0, 2};

@@ -48,6 +48,20 @@ def test_prepared_scan_threshold_and_exclusions():
     assert plan(0, 100000, 4) == ("prepared_scan", 0)              # no sequences: never split
 
 
+def test_prepared_workspace_budget():
+    """The prepared chunks take ~208 bytes per token and value head; past 8 GiB the
+    plan keeps the preparation inside the pipelined scan."""
+    slot, per_seg = 13312, 8 * 64
+    def prep_bytes(N, T, Hv):
+        return (T // per_seg + N + 1) * 8 * Hv * slot
+    T_ok = 1 << 20                                   # one sequence of 2^20 tokens, 32 heads: ~6.5 GiB
+    assert prep_bytes(1, T_ok, 32) <= 8 << 30
+    assert plan(1, T_ok, 32, bi=True)[0] == "prepared_scan"
+    T_big = 3 << 19                                  # 1.5 x 2^20 tokens: ~9.8 GiB
+    assert prep_bytes(1, T_big, 32) > 8 << 30
+    assert plan(1, T_big, 32, bi=True)[0] == "pipelined_scan"
+
+
 @pytest.mark.parametrize("args", [(-1, 0, 4), (1, -1, 4), (1, 64, 0)])
 def test_invalid_sizes_are_rejected(args):
     with pytest.raises(RuntimeError):
