@@ -28,10 +28,14 @@
 // Per chunk, two barrier intervals:
 //
 //   interval  recurrence                 output              loaders
-//   1         X, Z', Vnew, ub (to LDS),  Y = S~ Q^T          loads of chunk c + 2
-//             V loads of chunk c + 1
+//   1         X, Z', Vnew, ub (to LDS),  Y = S~ Q^T; P and   loads of chunk c + 2
+//             V loads of chunk c + 1     FY read ahead
 //   2         renorm fold, update, S~    output products,    chunk c + 1 into LDS
 //             fragments (to LDS)         staging, stores
+//
+// A wave here has its SIMD to itself, so every LDS read waited on next to its
+// use costs its whole latency: each wave reads what a phase needs in one batch
+// (the recurrence wave after its X pass, the output wave a whole interval ahead).
 //
 // With one or two blocks of rows per CU, each CU reads K, K^T, Q and the
 // exchange tiles for 32 or 64 state rows instead of 128: the LDS traffic per
@@ -185,7 +189,10 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
             bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + ws0 * (C * 32);
 
             // ---- interval 1: X = K S~^T (the next step's K fragments read while the
-            // current step runs), Z', Vnew, ub
+            // current step runs), Z', Vnew, ub.  After the X pass everything Z', Vnew and ub
+            // read from LDS is read at once (the T' fragments, the FZ and FU rows, and V,
+            // staged through this wave's 4 KB and read back as 4 consecutive tokens of one
+            // column), so its latency is paid once.
             f32x16 X[2] = {zero16(), zero16()};
             {
                 frag fk[2][2];
@@ -202,10 +209,25 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
                     X[1] = M::run(fk[cur][1], sfr[k], X[1]);
                 }
             }
-            frag zb[2][S32];
+            frag tf[3][S32];   // T' blocks (0,0), (1,0), (1,1)
+            // (with NP = 2 the FU rows come later, while the Vnew products run: reading them
+            // here too would exceed that kernel's 256 registers)
+            f32x4 fz[2][4], fu[2][4];
+#pragma unroll
+            for (int s = 0; s < S32; ++s) {
+                tf[0][s] = ld_acc<bf16>(Ts, L::OLD, l32, 0, s, h32);
+                tf[1][s] = ld_acc<bf16>(Ts, L::OLD, 32 + l32, 0, s, h32);
+                tf[2][s] = ld_acc<bf16>(Ts, L::OLD, 32 + l32, 32, s, h32);
+            }
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    fz[ib][jj] = ld4(FZr + 32 * ib + 8 * jj + 4 * h32);
+                    if constexpr (NP == 1) fu[ib][jj] = ld4(FUr + 32 * ib + 8 * jj + 4 * h32);
+                }
+            bf16x4 vx[2][4];
             {
-                // V through this wave's 4 KB, back as 4 consecutive tokens of one column
-                float vv[2][16];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     *reinterpret_cast<i32x4 *>(Vw + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = vw.x[j];
@@ -216,34 +238,37 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const bf16 *src = Vw + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
-                        const bf16x4 xv =
+                        vx[ib][q] =
                             __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src));
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) vv[ib][4 * q + t] = (float)xv[t];
                     }
                 if (c + 1 < nchunks) issue_v(c + 1);   // the registers are free again
+            }
+            frag zb[2][S32];
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
+            for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const f32x4 fz = ld4(FZr + 32 * ib + 8 * jj + 4 * h32);
+                for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            const int rr = 4 * jj + t;
-                            X[ib][rr] = fmaf(-fz[t], X[ib][rr], vv[ib][rr]);
-                        }
+                    for (int t = 0; t < 4; ++t) {
+                        const int rr = 4 * jj + t;
+                        X[ib][rr] = fmaf(-fz[ib][jj][t], X[ib][rr], (float)vx[ib][jj][t]);
                     }
 #pragma unroll
-                    for (int st = 0; st < S32; ++st) zb[ib][st] = acc_frag<bf16>(X[ib], st);
-                }
+                for (int st = 0; st < S32; ++st) zb[ib][st] = acc_frag<bf16>(X[ib], st);
             }
             // Vnew = T' Z'   (T' lower block-triangular: the upper 32x32 block is zero)
             f32x16 Vn[2] = {zero16(), zero16()};
 #pragma unroll
             for (int s = 0; s < S32; ++s) {
-                Vn[0] = M::run(ld_acc<bf16>(Ts, L::OLD, l32, 0, s, h32), zb[0][s], Vn[0]);
-                Vn[1] = M::run(ld_acc<bf16>(Ts, L::OLD, 32 + l32, 0, s, h32), zb[0][s], Vn[1]);
-                Vn[1] = M::run(ld_acc<bf16>(Ts, L::OLD, 32 + l32, 32, s, h32), zb[1][s], Vn[1]);
+                Vn[0] = M::run(tf[0][s], zb[0][s], Vn[0]);
+                Vn[1] = M::run(tf[1][s], zb[0][s], Vn[1]);
+                Vn[1] = M::run(tf[2][s], zb[1][s], Vn[1]);
+            }
+            if constexpr (NP != 1) {
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) fu[ib][jj] = ld4(FUr + 32 * ib + 8 * jj + 4 * h32);
             }
             if (!fast) {   // the entry-wise output path takes Vnew itself
 #pragma unroll
@@ -256,11 +281,9 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const f32x4 fu = ld4(FUr + 32 * ib + 8 * jj + 4 * h32);
+                for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) Vn[ib][4 * jj + t] *= fu[t];
-                }
+                    for (int t = 0; t < 4; ++t) Vn[ib][4 * jj + t] *= fu[ib][jj][t];
 #pragma unroll
                 for (int s = 0; s < S32; ++s) {
                     ub[ib][s] = acc_frag<bf16>(Vn[ib], s);
@@ -329,7 +352,18 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
             const int Lc = ch.L;
 
             // ---- interval 1: Y = S~ Q^T (the state as the A operand gives its transpose:
-            // lane = token, registers = 4 consecutive v)
+            // lane = token, registers = 4 consecutive v); this chunk's P fragments and
+            // output row factors (staged in the previous interval) read here for interval 2
+            const bf16 *Ps = pbuf(c);
+            const float *FYr = fyr(c);
+            frag pfr[3][S32];   // P blocks (0,0), (1,0), (1,1)
+#pragma unroll
+            for (int s = 0; s < S32; ++s) {
+                pfr[0][s] = ld_acc<bf16>(Ps, L::OLD, l32, 0, s, h32);
+                pfr[1][s] = ld_acc<bf16>(Ps, L::OLD, 32 + l32, 0, s, h32);
+                pfr[2][s] = ld_acc<bf16>(Ps, L::OLD, 32 + l32, 32, s, h32);
+            }
+            const float fyv[2] = {FYr[l32], FYr[32 + l32]};
             f32x16 Y[2] = {zero16(), zero16()};
             {
                 frag fq[2][2];
@@ -349,9 +383,11 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
             }
             __syncthreads();
 
-            // ---- interval 2: the output rows of chunk c
-            const bf16 *Ps = pbuf(c);
-            const float *FYr = fyr(c);
+            // ---- interval 2: the output rows of chunk c (the recurrence wave's ub, or
+            // Vnew on the entry-wise path, read first)
+            frag uf[2 * S32];
+#pragma unroll
+            for (int f = 0; f < 2 * S32; ++f) uf[f] = *xfrag(fast ? L::UB_OFF : L::NB_OFF, 4, w, f, lane);
             if (fast) {   // O^T = FY_t [S~ Q^T + ub^T P^T] (renormalising: the state term as (S~ Q^T) sigma gamma_L)
                 if (renorm) {
 #pragma unroll
@@ -364,25 +400,19 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
 #pragma unroll
                     for (int jb = 0; jb <= ib; ++jb)
 #pragma unroll
-                        for (int s = 0; s < S32; ++s)
-                            Y[ib] = M::run(*xfrag(L::UB_OFF, 4, w, S32 * jb + s, lane),
-                                           ld_acc<bf16>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), Y[ib]);
-                    const float fy = FYr[32 * ib + l32];
+                        for (int s = 0; s < S32; ++s) Y[ib] = M::run(uf[S32 * jb + s], pfr[ib + jb][s], Y[ib]);
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
+                    for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fyv[ib];
                 }
             } else {      // FY_t (S~ Q^T) + Vnew^T P^T
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
-                    const float fy = FYr[32 * ib + l32];
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
+                    for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fyv[ib];
 #pragma unroll
                     for (int jb = 0; jb <= ib; ++jb)
 #pragma unroll
-                        for (int s = 0; s < S32; ++s)
-                            Y[ib] = M::run(*xfrag(L::NB_OFF, 4, w, S32 * jb + s, lane),
-                                           ld_acc<bf16>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), Y[ib]);
+                        for (int s = 0; s < S32; ++s) Y[ib] = M::run(uf[S32 * jb + s], pfr[ib + jb][s], Y[ib]);
                 }
             }
             // staged through this block's 4 KB (rows t of the 32 columns, 16-byte granules
