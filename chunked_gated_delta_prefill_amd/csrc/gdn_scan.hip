@@ -661,15 +661,19 @@ fused_scan_kernel(const ScanParams p) {
                         for (int t = 0; t < 4; ++t) vv[ib][4 * q + t] = (float)x[t];
                     }
             }
+            f32x4 fz[2][4];   // read as one batch (one wait instead of one per read)
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) fz[ib][jj] = ld4(rf(FZ_) + 32 * ib + 8 * jj + 4 * h32);
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const f32x4 fz = ld4(rf(FZ_) + 32 * ib + 8 * jj + 4 * h32);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const int rr = 4 * jj + t;
-                        X[ib][rr] = fmaf(-fz[t], X[ib][rr], BF && HASV ? vv[ib][rr] : vreg_at(vcur, 16 * ib + rr, BF));
+                        X[ib][rr] = fmaf(-fz[ib][jj][t], X[ib][rr], BF && HASV ? vv[ib][rr] : vreg_at(vcur, 16 * ib + rr, BF));
                     }
                 }
 #pragma unroll
@@ -677,12 +681,19 @@ fused_scan_kernel(const ScanParams p) {
             }
         }
         // Vnew = T' Z'   (T' lower block-triangular: skip the zero upper 32x32 block)
+        typename M::frag tf[3][S32];   // T' blocks (0,0), (1,0), (1,1), read as one batch
+#pragma unroll
+        for (int s = 0; s < S32; ++s) {
+            tf[0][s] = ld_acc<IO>(Ts, L::OLD, l32, 0, s, h32);
+            tf[1][s] = ld_acc<IO>(Ts, L::OLD, 32 + l32, 0, s, h32);
+            tf[2][s] = ld_acc<IO>(Ts, L::OLD, 32 + l32, 32, s, h32);
+        }
         f32x16 Vn[2] = {zero16(), zero16()};
 #pragma unroll
         for (int s = 0; s < S32; ++s) {
-            Vn[0] = M::run(ld_acc<IO>(Ts, L::OLD, l32, 0, s, h32), zb[0][s], Vn[0]);
-            Vn[1] = M::run(ld_acc<IO>(Ts, L::OLD, 32 + l32, 0, s, h32), zb[0][s], Vn[1]);
-            Vn[1] = M::run(ld_acc<IO>(Ts, L::OLD, 32 + l32, 32, s, h32), zb[1][s], Vn[1]);
+            Vn[0] = M::run(tf[0][s], zb[0][s], Vn[0]);
+            Vn[1] = M::run(tf[1][s], zb[0][s], Vn[1]);
+            Vn[1] = M::run(tf[2][s], zb[1][s], Vn[1]);
         }
         if constexpr (OUT) {
             if (!fast) {   // slow: FY_t (S~ Q^T) + Vnew^T P^T, with its own Vnew operand
@@ -707,17 +718,25 @@ fused_scan_kernel(const ScanParams p) {
         frag ub[2][S32];
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
+            f32x4 fu[4];   // one batch per block of 32 rows
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const f32x4 fu = ld4(rf(FU_) + 32 * ib + 8 * jj + 4 * h32);
+            for (int jj = 0; jj < 4; ++jj) fu[jj] = ld4(rf(FU_) + 32 * ib + 8 * jj + 4 * h32);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) Vn[ib][4 * jj + t] *= fu[t];
-            }
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) Vn[ib][4 * jj + t] *= fu[jj][t];
 #pragma unroll
             for (int s = 0; s < S32; ++s) ub[ib][s] = acc_frag<IO>(Vn[ib], s);
         }
         if constexpr (OUT) {
             if (fast) {
+                frag pfr[3][S32];   // P blocks (0,0), (1,0), (1,1), read as one batch
+#pragma unroll
+                for (int s = 0; s < S32; ++s) {
+                    pfr[0][s] = ld_acc<IO>(Ps, L::OLD, l32, 0, s, h32);
+                    pfr[1][s] = ld_acc<IO>(Ps, L::OLD, 32 + l32, 0, s, h32);
+                    pfr[2][s] = ld_acc<IO>(Ps, L::OLD, 32 + l32, 32, s, h32);
+                }
                 if (renorm) {   // sigma and gamma_L are both normal numbers; their product may not be
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib)
@@ -729,8 +748,7 @@ fused_scan_kernel(const ScanParams p) {
 #pragma unroll
                     for (int jb = 0; jb <= ib; ++jb)
 #pragma unroll
-                        for (int s = 0; s < S32; ++s)
-                            Y[ib] = M::run(ub[jb][s], ld_acc<IO>(Ps, L::OLD, 32 * ib + l32, 32 * jb, s, h32), Y[ib]);
+                        for (int s = 0; s < S32; ++s) Y[ib] = M::run(ub[jb][s], pfr[ib + jb][s], Y[ib]);
                     const float fy = rf(FY_)[32 * ib + l32];
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) Y[ib][rr] *= fy;
