@@ -260,8 +260,10 @@ int gdn_decode_step_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_t
  *   GDN_PLAN_SCAN            one launch of the four-wave fused scan
  *   GDN_PLAN_PIPELINED_SCAN  one launch of the eight-wave pipelined scan (bf16,
  *                            no checkpoints, more than half as many work items
- *                            as CUs and at most one per CU); bitwise the
- *                            results of GDN_PLAN_SCAN
+ *                            as CUs and at most one per CU, or fewer work items
+ *                            when the prepared chunks would take more than
+ *                            8 GiB, about 208 bytes per token and value head);
+ *                            bitwise the results of GDN_PLAN_SCAN
  *   GDN_PLAN_SPLIT           segment table, the two segment maps, the state
  *                            fix-up and the per-segment scan, with segments
  *                            of *segment_length tokens
