@@ -271,9 +271,9 @@ fused_scan_kernel(const ScanParams p) {
                 if constexpr (BF) return ld_kq(M, 32 * blk + l32, k, h32);
                 else return ld_acc<IO>(M, L::KLD, 32 * blk + l32, 32 * (k / S32), k % S32, h32);
             };
-            auto sq = [&](const frag &f) {
-                if constexpr (BF) return sumsq8_acc(f, 0.f);
-                else return f * f;
+            auto sq = [&](const frag &f, float acc) {   // acc + the squares of f's elements
+                if constexpr (BF) return sumsq8_acc(f, acc);
+                else return acc + f * f;
             };
             // 1 / |row| (or 1 without the norm); a K row's factor also goes into
             // its 1 / gamma entry, which only the A tiles read
@@ -315,18 +315,18 @@ fused_scan_kernel(const ScanParams p) {
                     }
                     if constexpr (R == 0) {
                         gt[cur] = M::run(k0, k0, gt[cur]);
-                        ssa += sq(k0);
-                        if constexpr (USEQ) ssb += sq(fq[cur][1]);
+                        ssa = sq(k0, ssa);
+                        if constexpr (USEQ) ssb = sq(fq[cur][1], ssb);
                     } else if constexpr (R == 1) {
                         gt[0] = M::run(k0, k1, gt[0]);
-                        ssa += sq(k1);
+                        ssa = sq(k1, ssa);
                         if constexpr (USEQ) gt[1] = M::run(k1, fq[cur][1], gt[1]);
                     } else if constexpr (R == 2) {
                         gt[cur] = M::run(k1, k1, gt[cur]);
                     } else if constexpr (USEQ) {
                         gt[0] = M::run(k0, fq[cur][0], gt[0]);
                         gt[1] = M::run(k0, fq[cur][1], gt[1]);
-                        ssb += sq(fq[cur][0]);
+                        ssb = sq(fq[cur][0], ssb);
                     }
                 }
                 if constexpr (R == 0) {

@@ -450,18 +450,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     if (k + 1 < NK) load(k + 1, cur ^ 1);
                     if constexpr (R == 0) {   // k0, q1
                         X[cur] = M::run(fa[cur][0], fa[cur][0], X[cur]);
-                        ssa += sumsq8_acc(fa[cur][0], 0.f);
-                        ssb += sumsq8_acc(fa[cur][1], 0.f);
+                        ssa = sumsq8_acc(fa[cur][0], ssa);
+                        ssb = sumsq8_acc(fa[cur][1], ssb);
                     } else if constexpr (R == 1) {   // k0, k1, q1
                         X[0] = M::run(fa[cur][0], fa[cur][1], X[0]);
-                        ssa += sumsq8_acc(fa[cur][1], 0.f);
+                        ssa = sumsq8_acc(fa[cur][1], ssa);
                         X[1] = M::run(fa[cur][1], fa[cur][2], X[1]);
                     } else if constexpr (R == 2) {   // k1
                         X[cur] = M::run(fa[cur][0], fa[cur][0], X[cur]);
                     } else {   // k0, q0, q1
                         X[0] = M::run(fa[cur][0], fa[cur][1], X[0]);
                         X[1] = M::run(fa[cur][0], fa[cur][2], X[1]);
-                        ssb += sumsq8_acc(fa[cur][1], 0.f);
+                        ssb = sumsq8_acc(fa[cur][1], ssb);
                     }
                 }
                 if constexpr (R == 0) {
