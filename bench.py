@@ -21,7 +21,10 @@ HBM: bytes/step = state (2 Hv d^2 4B per sequence) + q, k, v, out, g, beta.
 
 Every configuration: ``--all`` prints one JSON line per workload (the five
 recipes of gdn_workloads.py) and batch_invariant mode, each with its host plan,
-the fp32 oracle's timing and the timed run's error against it; ``--table FILE``
+the fp32 oracle's timing (all host threads, and one item on one thread) and the
+timed run's error against it, plus the varlen batch with cold caches (its inputs
+fit the 256 MiB last-level cache: ``--cold-cache`` writes 512 MiB before each
+timed call and takes the rate from the calls' own events); ``--table FILE``
 renders such lines as a markdown table.
 
 Other modes (used to produce the committed rocprofv3 summaries):
@@ -128,6 +131,20 @@ def cpu_baseline(w, max_seqs):
     rec = {"value": round(end / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
            "sample": f"{part} {w.N} sequences ({end} tokens, all {w.Hv} v-heads), fp32 token-by-token "
                      f"oracle, {dt:.1f} s wall"}
+    # one (sequence, v-head) item on one thread: the rate one core gives, as tokens/s
+    # of the whole head count (the first non-empty sequence, v-head 0 and its q/k head)
+    n0 = next((i for i in range(take) if int(cu[i + 1]) > int(cu[i])), None)
+    if n0 is not None:
+        b0, e0 = int(cu[n0]), int(cu[n0 + 1])
+        one = lambda x: None if x is None else x[b0:e0, :1]
+        t = time.perf_counter()
+        oracle.run(one(sub.q), one(sub.k), one(sub.v), one(sub.g), one(sub.beta), sub.scale, [0, e0 - b0],
+                   None if sub.initial_state is None else sub.initial_state[n0:n0 + 1, :1], sub.use_qk_l2norm,
+                   precision="f32", nthreads=1)
+        dt1 = time.perf_counter() - t
+        rec["per_core"] = {"value": round((e0 - b0) / dt1 / w.Hv, 1), "unit": "tokens/s",
+                           "sample": f"sequence {n0} ({e0 - b0} tokens), v-head 0, one thread, {dt1:.2f} s; "
+                                     f"divided by the {w.Hv} v-heads"}
     return rec, ref, take, end
 
 
@@ -496,7 +513,8 @@ def render_table(path):
                     break
         err = (f"{e['out']:.1e}, " + ("-" if e.get("state") is None else f"{e['state']:.1e}")) if e else "-"
         ratio = "-" if tr is None else f"{tr / rf['algorithmic_bytes']:.2f}"
-        rows.append(f"| {cfg['workload']} | {int(cfg['batch_invariant'])} | {r.get('plan', '?')} | "
+        name = cfg["workload"] + (" (cold caches)" if "cache" in cfg else "")
+        rows.append(f"| {name} | {int(cfg['batch_invariant'])} | {r.get('plan', '?')} | "
                     f"{r['kernel_ms']:.3f} | {r['value'] / 1e6:.1f} M | {r['tflops']:.0f} ({100 * r['mfma_frac']:.1f}%) | "
                     f"{rf['achieved']:.0f} ({100 * rf['frac']:.1f}%) | "
                     f"{ratio} | {err} |")
@@ -581,9 +599,10 @@ def bench_decode(args, gdn, W):
     print(json.dumps(res), flush=True)
 
 
-def bench_prefill(args, gdn, w, bi, peaks, oracle_ref):
+def bench_prefill(args, gdn, w, bi, peaks, oracle_ref, cold=False):
     """Times gdn_chunk_prefill on workload w (already on the device) and returns
-    the result record; oracle_ref is cpu_baseline()'s return value or None."""
+    the result record; oracle_ref is cpu_baseline()'s return value or None;
+    cold: L2 and last-level cache flushed before every timed call."""
     import torch
     flops, byts = algorithmic(w)
 
@@ -613,6 +632,9 @@ def bench_prefill(args, gdn, w, bi, peaks, oracle_ref):
             fn(w.q, w.k, w.v, w.g, w.beta, w.scale, w.cu_seqlens, w.initial_state, fin, w.use_qk_l2norm,
                bool(bi), out, stream)
 
+    # cold caches: a 512 MiB write (twice the 256 MiB last-level cache) before each
+    # timed call, outside its event pair; the rate then comes from the calls' events
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -621,14 +643,17 @@ def bench_prefill(args, gdn, w, bi, peaks, oracle_ref):
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
+        if cold:
+            flush.fill_(i & 255)
         a.record(stream)
         step()
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_step = wall * 1e3 / args.steps
+    ms_step = statistics.mean(launch_ms) if cold else wall * 1e3 / args.steps
+    del flush
     kern_ms = statistics.mean(launch_ms)
     value = w.T / (ms_step / 1e3)
     achieved = byts / (kern_ms / 1e3) / 1e9
@@ -657,7 +682,9 @@ def bench_prefill(args, gdn, w, bi, peaks, oracle_ref):
                    "batch_invariant": bool(bi),
                    **({"checkpoint_interval": ck_every} if ck_every else {}),
                    **({"entry": "gdn_chunk_prefill_noalloc"} if args.noalloc else {}),
-                   **({"pooled": True} if args.pooled else {})},
+                   **({"pooled": True} if args.pooled else {}),
+                   **({"cache": "cold (512 MiB write before each call; rate from the calls' events)"}
+                      if cold else {})},
         "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
         "mfma_frac": round(flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": round(kern_ms, 4),
@@ -709,8 +736,11 @@ def main():
                     help="states in an indexed pool (gdn_chunk_prefill_pooled, reversed index order)")
     ap.add_argument("--checkpoint-interval", type=int, default=0,
                     help="tokens between state checkpoints (gdn_chunk_prefill_checkpointed); 0 = plain scan")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="flush L2 and the last-level cache (512 MiB write) before each timed call")
     ap.add_argument("--all", action="store_true",
-                    help="one JSON line per configuration (all five) and batch_invariant mode")
+                    help="one JSON line per configuration (all five) and batch_invariant mode, and the varlen batch "
+                         "with cold caches")
     ap.add_argument("--table", default=None, metavar="FILE",
                     help="markdown table of the JSON lines in FILE (the output of --all)")
     ap.add_argument("--summarize-plan", nargs=2, metavar=("DIR", "OUT"), default=None,
@@ -769,12 +799,14 @@ def main():
             ref = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_seqs)
             for bi in (0, 1):
                 print(json.dumps(bench_prefill(args, gdn, w, bi, peaks, ref)), flush=True)
+            if name == "varlen_bf16":   # inputs smaller than the last-level cache: also cold
+                print(json.dumps(bench_prefill(args, gdn, w, 0, peaks, ref, cold=True)), flush=True)
             del w, ref
             torch.cuda.empty_cache()
         return
     w = W.make(args.workload, device="cuda", variant=args.variant)
     ref = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_seqs)
-    res = bench_prefill(args, gdn, w, args.batch_invariant, peaks, ref)
+    res = bench_prefill(args, gdn, w, args.batch_invariant, peaks, ref, cold=args.cold_cache)
     print(json.dumps(res), flush=True)
 
 
