@@ -3,8 +3,10 @@ lengths (empty ones included), head counts and GVA ratios, bf16 or fp32 q/k/v,
 fp32, bf16 or absent states, the three gate recipes with fp32 or bf16 gates
 and absent g or beta, in-kernel norm on or off, custom scales, both
 batch_invariant modes.  Small batches take the prepared plan, larger ones the
-pipelined or the four-wave scan, the last cases few long sequences (the split
-path where batch_invariant is off), so the sweep runs every plan; each case
+pipelined or the four-wave scan, a middle band batches of 16-64 short
+sequences on many heads (the four-wave scan with more workgroups than the GPU
+holds at once), the last cases few long sequences (the split path where
+batch_invariant is off), so the sweep runs every plan; each case
 prints the plan it took and compares out and the final state element by
 element with the fp64 oracle on the same inputs."""
 import numpy as np
@@ -16,7 +18,7 @@ from _harness import BF16_TOL, F32_TOL, check, say
 
 pytestmark = pytest.mark.gpu
 
-SHORT, LONG = 20, 4
+SHORT, MID, LONG = 20, 8, 4
 
 
 def random_case(seed):
@@ -28,6 +30,11 @@ def random_case(seed):
         if rng.random() < 0.3:
             lengths[int(rng.integers(0, N))] = 0          # an empty sequence
         Hqk, r = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 4]))
+        bi = bool(rng.random() < 0.5)
+    elif seed < SHORT + MID:                              # many short sequences, many heads
+        N = int(rng.integers(16, 65))
+        lengths = [int(x) for x in rng.integers(0, 300, size=N)]
+        Hqk, r = int(rng.choice([4, 8, 16])), int(rng.choice([2, 4]))
         bi = bool(rng.random() < 0.5)
     else:                                                 # few long sequences
         N = int(rng.integers(1, 3))
@@ -53,7 +60,7 @@ def tolerance(w):
     return F32_TOL if (w.q.dtype == torch.float32 and w.state_dtype != torch.bfloat16) else BF16_TOL
 
 
-@pytest.mark.parametrize("seed", range(SHORT + LONG))
+@pytest.mark.parametrize("seed", range(SHORT + MID + LONG))
 def test_random_shapes(gdn, seed):
     w, bi = random_case(seed)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
