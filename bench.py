@@ -590,11 +590,11 @@ def bench_decode(args, gdn, W):
         reps = 0
         while time.perf_counter() - t < 2.0:
             oracle.run(wc.q, wc.k, wc.v, wc.g, wc.beta, wc.scale, wc.cu_seqlens, wc.initial_state,
-                       wc.use_qk_l2norm, nthreads=threads)
+                       wc.use_qk_l2norm, precision="f32", nthreads=threads)
             reps += 1
         dt = (time.perf_counter() - t) / reps
         res["cpu_baseline"] = {"value": round(wc.N / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                               "sample": f"the whole batch ({wc.N} sequences x {wc.Hv} v-heads), fp64 oracle, "
+                               "sample": f"the whole batch ({wc.N} sequences x {wc.Hv} v-heads), fp32 oracle, "
                                          f"{reps} runs of {dt * 1e3:.0f} ms"}
     print(json.dumps(res), flush=True)
 
