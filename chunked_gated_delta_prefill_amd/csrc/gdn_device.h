@@ -403,6 +403,44 @@ __device__ __forceinline__ void issue_v_wide_part(VWide &vw, const ScanParams &p
     vw.x[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * j * p.v_st, 0, 0);
 }
 
+// A wave's 64 x 32 staging block in LDS (bf16 V in, bf16 output out): kStageBytes
+// per wave.  V goes in as 64-byte rows (token t at 64 t).  Output goes in by
+// granule columns: granule g (columns 8 g .. 8 g + 7) of token t at g kStageCol
+// + 16 t, the column stride padded by 64 bytes.  Staged from the transposed
+// output tile (lane = token, registers 4 q .. 4 q + 3 = columns 8 q + 4 h32 +
+// 0..3), the two lane halves first trade 8-byte pieces (permlane32 swap) so that
+// every lane holds 8 consecutive columns, granule 2 p + h32: each half-wave then
+// writes 512 contiguous bytes with 16-byte stores, and a quarter-wave reading 4
+// tokens x 4 granules (the 64-byte output rows) touches 64 distinct banks.  An
+// LDS probe under SQ_LDS_BANK_CONFLICT measured both patterns conflict-free; the
+// earlier row-major block with rotated granules took 8-byte writes with ~4.5
+// conflict cycles each.
+constexpr int kStageCol = 64 * 16 + 64;
+constexpr int kStageBytes = 4 * kStageCol;
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, bf16x2{(bf16)a, (bf16)b});
+}
+// Output rows 32 ib .. 32 ib + 31 of accumulator tile Y into the staging block.
+__device__ __forceinline__ void stage_out_tile(char *st, const f32x16 &Y, int ib, int l32, int h32) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+        const int q0 = 2 * pp, q1 = 2 * pp + 1;
+        const unsigned a0 = pack_bf16(Y[4 * q0], Y[4 * q0 + 1]), a1 = pack_bf16(Y[4 * q0 + 2], Y[4 * q0 + 3]);
+        const unsigned b0 = pack_bf16(Y[4 * q1], Y[4 * q1 + 1]), b1 = pack_bf16(Y[4 * q1 + 2], Y[4 * q1 + 3]);
+        // lanes 0..31 keep a (granule q0, columns +0..3) and take the other half's a
+        // (columns +4..7); lanes 32..63 take the other half's b and keep their own
+        const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        *reinterpret_cast<i32x4 *>(st + (2 * pp + h32) * kStageCol + 16 * (32 * ib + l32)) =
+            i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+    }
+}
+// Granule g (16 bytes) of staged output token t.
+__device__ __forceinline__ i32x4 staged_out(const char *st, int t, int g) {
+    return *reinterpret_cast<const i32x4 *>(st + g * kStageCol + 16 * t);
+}
+
 __device__ __forceinline__ ChunkRef chunk_at(int64_t bos, int64_t eos, int c) {
     ChunkRef ch;
     ch.t0 = bos + (int64_t)c * C;

@@ -71,6 +71,7 @@ template <typename IO> struct Smem {
     static constexpr int ROW_OFF = NT_OFF + 4 * NTS * 4;
     static constexpr int BYTES = ROW_OFF + (kRowsTotal * C + 4) * 4;
     static_assert(!BF || BYTES <= 80 * 1024, "two workgroups per CU");
+    static_assert(!BF || 4 * kStageBytes <= C * FLD * 4, "four staging blocks in the A area");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(Q_OFF % 16 == 0 && AF_OFF % 16 == 0 && T_OFF % 16 == 0 &&
                   ROW_OFF % 16 == 0, "align");
@@ -644,7 +645,7 @@ fused_scan_kernel(const ScanParams p) {
             // consecutive tokens of one column: registers 4q .. 4q+3 of tile ib.
             float vv[2][16];
             if constexpr (BF && HASV) {
-                bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::AF_OFF) + ws * (C * 32);
+                bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::AF_OFF + ws * kStageBytes);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     *reinterpret_cast<i32x4 *>(Vw + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = vwide.x[j];
@@ -756,19 +757,11 @@ fused_scan_kernel(const ScanParams p) {
             }
             // store (rows past the chunk end fall outside the buffer range)
             if constexpr (BF) {
-                // through this wave's 4 KB of the A area (free again): rows t of its 32
-                // columns (64 B), the 16-byte granules of row t rotated by (t / 4) % 4 so
-                // that the 8-byte writes spread over the banks; then 16 rows of 64 B per
-                // store instruction instead of 32 rows of 16 B
-                bf16 *Ow = reinterpret_cast<bf16 *>(smem + L::AF_OFF) + ws * (C * 32);
+                // through this wave's staging block in the A area (free again), then 16
+                // rows of 64 B per store instruction instead of 32 rows of 16 B
+                char *st = smem + L::AF_OFF + ws * kStageBytes;
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const bf16x4 b4 = {(bf16)Y[ib][4 * q], (bf16)Y[ib][4 * q + 1], (bf16)Y[ib][4 * q + 2],
-                                           (bf16)Y[ib][4 * q + 3]};
-                        *reinterpret_cast<bf16x4 *>(Ow + (32 * ib + l32) * 32 + 8 * (q ^ ((l32 >> 2) & 3)) + 4 * h32) = b4;
-                    }
+                for (int ib = 0; ib < 2; ++ib) stage_out_tile(st, Y[ib], ib, l32, h32);
                 // (read back and stored one 16-row group per step of the state update)
             } else {
                 // lane = token 32 ib + l32, registers 4q..4q+3 = v 32 ws + 8q + 4 h32 + 0..3
@@ -812,10 +805,10 @@ fused_scan_kernel(const ScanParams p) {
                 const int cur = k & 1;
                 if (k + 1 < NU) load_kt(k + 1, kt[cur ^ 1]);
                 if constexpr (OUT && BF) {   // output rows 16k .. 16k+15 of this wave's columns
-                    const bf16 *Ow = reinterpret_cast<const bf16 *>(smem + L::AF_OFF) + ws * (C * 32);
+                    const char *st = smem + L::AF_OFF + ws * kStageBytes;
                     const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * 2);
                     const int gq = lane & 3, t = 16 * k + (lane >> 2);
-                    const i32x4 o16 = *reinterpret_cast<const i32x4 *>(Ow + t * 32 + 8 * (gq ^ ((t >> 2) & 3)));
+                    const i32x4 o16 = staged_out(st, t, gq);
                     __builtin_amdgcn_raw_buffer_store_b128(o16, ro, t * p.o_st + (32 * ws + 8 * gq) * 2, 0, 0);
                 }
 #pragma unroll

@@ -47,9 +47,9 @@ struct PipedSmem {
     static constexpr int P_OFF = Q_OFF + 2 * KB;      // [2]
     static constexpr int T_OFF = P_OFF + 2 * OB;      // [2]
     static constexpr int AF_OFF = T_OFF + 2 * OB;
-    static constexpr int VO_OFF = AF_OFF + C * FLD * 4;   // 4 KB per state wave: V in, output out
+    static constexpr int VO_OFF = AF_OFF + C * FLD * 4;   // a staging block per state wave: V in, output out
     static constexpr int NTS = 16 * 16 + 4;
-    static constexpr int NT_OFF = VO_OFF + 4 * C * 32 * 2;
+    static constexpr int NT_OFF = VO_OFF + 4 * kStageBytes;
     static constexpr int ROW_OFF = NT_OFF + 4 * NTS * 4;  // row factors, [2] sets by chunk parity
     static constexpr int BYTES = ROW_OFF + (2 * NROWF * C + 4) * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
@@ -197,7 +197,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const ChunkRef ch = chunk_at(bos, eos, c);
             const int Lc = ch.L;
             const bf16 *Ks = kbuf(c);
-            bf16 *Ow = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + ws * (C * 32);
+            char *st = smem + L::VO_OFF + ws * kStageBytes;
+            bf16 *Vw = reinterpret_cast<bf16 *>(st);
 
             // ---- interval 1: Z' = V - FZ o X, Vnew = T' Z', ub = FU o Vnew (slow
             // path: the output products with their own Vnew operand)
@@ -205,19 +206,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (on) {
                 frag zb[2][S32];
                 {
-                    // V through this wave's 4 KB, back as 4 consecutive tokens of one
+                    // V through this wave's staging block, back as 4 consecutive tokens of one
                     // column (transposing reads): registers 4q .. 4q+3 of tile ib
                     float vv[2][16];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        *reinterpret_cast<i32x4 *>(Ow + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = pf.kq[0][j];
+                        *reinterpret_cast<i32x4 *>(Vw + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = pf.kq[0][j];
                     const int i = lane & 15, g16 = (lane >> 4) & 1;
                     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
                     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const bf16 *src = Ow + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
+                            const bf16 *src = Vw + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
                             const bf16x4 xv =
                                 __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src));
 #pragma unroll
@@ -325,14 +326,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     }
                 }
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const bf16x4 b4 = {(bf16)Y[ib][4 * q], (bf16)Y[ib][4 * q + 1], (bf16)Y[ib][4 * q + 2],
-                                           (bf16)Y[ib][4 * q + 3]};
-                        *reinterpret_cast<bf16x4 *>(Ow + (32 * ib + l32) * 32 + 8 * (q ^ ((l32 >> 2) & 3)) + 4 * h32) =
-                            b4;
-                    }
+                for (int ib = 0; ib < 2; ++ib) stage_out_tile(st, Y[ib], ib, l32, h32);
             }
             __syncthreads();
 
@@ -359,7 +353,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     const int cur = k & 1;
                     if (k + 1 < NU) load_kt(k + 1, kt[cur ^ 1]);
                     const int gq = lane & 3, t = 16 * k + (lane >> 2);
-                    const i32x4 o16 = *reinterpret_cast<const i32x4 *>(Ow + t * 32 + 8 * (gq ^ ((t >> 2) & 3)));
+                    const i32x4 o16 = staged_out(st, t, gq);
                     __builtin_amdgcn_raw_buffer_store_b128(o16, ro, t * p.o_st + (32 * ws + 8 * gq) * 2, 0, 0);
 #pragma unroll
                     for (int bb = 0; bb < 4; ++bb) S[bb] = M::run(kt[cur][bb], ub[k / S32][k % S32], S[bb]);

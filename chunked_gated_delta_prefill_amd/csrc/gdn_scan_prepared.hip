@@ -68,8 +68,8 @@ template <int NP> struct PreparedSmem {
     static constexpr int SB_OFF = P_OFF + 2 * OB;              // S~ fragments [block][8 steps]
     static constexpr int UB_OFF = SB_OFF + NP * 8 * FRAG_BYTES;   // ub fragments [block][4]
     static constexpr int NB_OFF = UB_OFF + NP * 4 * FRAG_BYTES;   // Vnew fragments (entry-wise path)
-    static constexpr int VO_OFF = NB_OFF + NP * 4 * FRAG_BYTES;   // 4 KB per block: V in (1), output out (2)
-    static constexpr int ROW_OFF = VO_OFF + NP * C * 32 * 2;      // FZ, FU, FY [2][64] each; scalars [2][4]
+    static constexpr int VO_OFF = NB_OFF + NP * 4 * FRAG_BYTES;   // staging block per block: V in (1), output out (2)
+    static constexpr int ROW_OFF = VO_OFF + NP * kStageBytes;     // FZ, FU, FY [2][64] each; scalars [2][4]
     static constexpr int BYTES = ROW_OFF + (6 * C + 8) * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(Q_OFF % 16 == 0 && T_OFF % 16 == 0 && P_OFF % 16 == 0 && SB_OFF % 16 == 0 &&
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
             const bool fast = uniform(scal(c)[2]) > kFastDecay;
             const bf16 *Ks = kbuf(c);
             const float *FZr = fzr(c), *FUr = fur(c);
-            bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + ws0 * (C * 32);
+            bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::VO_OFF + ws0 * kStageBytes);
 
             // ---- interval 1: X = K S~^T (the next step's K fragments read while the
             // current step runs), Z', Vnew, ub.  After the X pass everything Z', Vnew and ub
@@ -415,23 +415,16 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
                         for (int s = 0; s < S32; ++s) Y[ib] = M::run(uf[S32 * jb + s], pfr[ib + jb][s], Y[ib]);
                 }
             }
-            // staged through this block's 4 KB (rows t of the 32 columns, 16-byte granules
-            // of row t rotated by (t / 4) % 4), then 16 rows of 64 bytes per store
-            bf16 *Ow = reinterpret_cast<bf16 *>(smem + L::VO_OFF) + w * (C * 32);
+            // staged through this block's staging block, then 16 rows of 64 bytes per store
+            char *st = smem + L::VO_OFF + w * kStageBytes;
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const bf16x4 b4 = {(bf16)Y[ib][4 * q], (bf16)Y[ib][4 * q + 1], (bf16)Y[ib][4 * q + 2],
-                                       (bf16)Y[ib][4 * q + 3]};
-                    *reinterpret_cast<bf16x4 *>(Ow + (32 * ib + l32) * 32 + 8 * (q ^ ((l32 >> 2) & 3)) + 4 * h32) = b4;
-                }
+            for (int ib = 0; ib < 2; ++ib) stage_out_tile(st, Y[ib], ib, l32, h32);
             const auto ro = rsrc(p.out + ch.t0 * p.o_st + h * p.o_sh, (Lc - 1) * p.o_st + D * 2);
             const int gq = lane & 3;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int t = 16 * k + (lane >> 2);
-                const i32x4 o16 = *reinterpret_cast<const i32x4 *>(Ow + t * 32 + 8 * (gq ^ ((t >> 2) & 3)));
+                const i32x4 o16 = staged_out(st, t, gq);
                 __builtin_amdgcn_raw_buffer_store_b128(o16, ro, t * p.o_st + (32 * vb + 8 * gq) * 2, 0, 0);
             }
             sigma = renorm ? 1.f : sig_next;
