@@ -3,7 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large_batch]
 
 One step = one gdn_chunk_prefill call over the whole synthetic batch (inputs
-already resident in HBM).  Prints one JSON line with the throughput
+already resident in HBM).  The call first repeats untimed for --settle-ms
+(300 ms) so the GPU's clocks settle, then runs W warmup calls, then K timed
+calls.  Prints one JSON line with the throughput
 (tokens/s), the roofline of the dominant kernel and the CPU oracle baseline.
 
 Default workload: 32 sequences x 8192 tokens, Hqk = 16, Hv = 32, d = 128, bf16
@@ -528,6 +530,20 @@ def decode_bytes(w):
     return w.N * (2 * w.Hqk * D * io + 2 * w.Hv * D * io + w.Hv * 8) + 2 * w.N * w.Hv * D * D * 4
 
 
+def settle(args, step):
+    """A GPU that has idled (input generation, the oracle of the previous
+    workload) takes tens of milliseconds of work to reach its steady clocks, so
+    the call is repeated for settle_ms of wall time before the W warmup calls
+    (measured on the 256-sequence batch after 3 s idle: the first 20 calls ran
+    23% slower than the steady state, the 32 x 8192 batch 3.5%)."""
+    import torch
+    t_end = time.perf_counter() + args.settle_ms / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+
+
 def bench_decode(args, gdn, W):
     """One decode step per timed step over decode_batch; one JSON line."""
     import torch
@@ -541,6 +557,7 @@ def bench_decode(args, gdn, W):
     def step():
         gdn.gdn_decode_step(w.q, w.k, w.v, w.g, w.beta, w.scale, state, state, w.use_qk_l2norm, out, stream)
 
+    settle(args, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -572,7 +589,8 @@ def bench_decode(args, gdn, W):
     res = {
         "metric": "GDN decode step tokens/s (one token per sequence), 1 GPU",
         "value": round(w.N / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "sequences": w.N, "hqk": w.Hqk, "hv": w.Hv, "head_dim": D,
                    "state": "float32", "in_place": True, "l2norm": w.use_qk_l2norm},
@@ -599,10 +617,10 @@ def bench_decode(args, gdn, W):
     print(json.dumps(res), flush=True)
 
 
-def bench_prefill(args, gdn, w, bi, peaks, oracle_ref, cold=False):
+def bench_prefill(args, gdn, w, bi, peaks, cold=False):
     """Times gdn_chunk_prefill on workload w (already on the device) and returns
-    the result record; oracle_ref is cpu_baseline()'s return value or None;
-    cold: L2 and last-level cache flushed before every timed call."""
+    the result record with the timed run's output and final state (for
+    with_oracle); cold: L2 and last-level cache flushed before every timed call."""
     import torch
     flops, byts = algorithmic(w)
 
@@ -635,6 +653,7 @@ def bench_prefill(args, gdn, w, bi, peaks, oracle_ref, cold=False):
     # cold caches: a 512 MiB write (twice the 256 MiB last-level cache) before each
     # timed call, outside its event pair; the rate then comes from the calls' events
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
+    settle(args, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -673,8 +692,8 @@ def bench_prefill(args, gdn, w, bi, peaks, oracle_ref, cold=False):
     res = {
         "metric": "GDN prefill tokens/s and TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.q.dtype == torch.bfloat16 else "f32",
+        "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.q.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "sequences": w.N, "tokens": w.T, "hqk": w.Hqk, "hv": w.Hv,
                    "head_dim": D, "state": str(w.initial_state.dtype).replace("torch.", "")
@@ -701,8 +720,16 @@ def bench_prefill(args, gdn, w, bi, peaks, oracle_ref, cold=False):
     res["plan"] = plan
     res["achievable"] = {**peaks, "mfma_frac_of_mm": round(flops / (ms_step / 1e3) / 1e12 / peaks["bf16_mm_tflops"], 4),
                          "hbm_frac_of_copy": round(achieved / peaks["copy_gbs"], 4)}
-    if oracle_ref is not None:
-        rec, (ro, rf), take, end = oracle_ref
+    return res, out, fin
+
+
+def with_oracle(args, timed, oracle_ref):
+    """Adds the oracle baseline (cpu_baseline()'s return value, timed after the
+    GPU runs) and each timed run's own error against it to the records of
+    bench_prefill; returns the records."""
+    rec, (ro, rf), take, end = oracle_ref
+    recs = []
+    for res, out, fin in timed:
         res["cpu_baseline"] = rec
         # the timed run's own output and final state against the oracle (same sample)
         if args.pooled:   # the pool is updated in place by every step: no fixed reference
@@ -711,7 +738,8 @@ def bench_prefill(args, gdn, w, bi, peaks, oracle_ref, cold=False):
             res["max_norm_err"] = {"out": max_norm_err(out[:end], ro),
                                    "state": None if fin is None else max_norm_err(fin[:take], rf),
                                    "reference": "fp32 oracle", "sample": rec["sample"].split(" (")[0]}
-    return res
+        recs.append(res)
+    return recs
 
 
 def main():
@@ -736,6 +764,8 @@ def main():
                     help="states in an indexed pool (gdn_chunk_prefill_pooled, reversed index order)")
     ap.add_argument("--checkpoint-interval", type=int, default=0,
                     help="tokens between state checkpoints (gdn_chunk_prefill_checkpointed); 0 = plain scan")
+    ap.add_argument("--settle-ms", type=int, default=300,
+                    help="untimed calls for this long before the warmup calls, so the clocks settle (0: none)")
     ap.add_argument("--cold-cache", action="store_true",
                     help="flush L2 and the last-level cache (512 MiB write) before each timed call")
     ap.add_argument("--all", action="store_true",
@@ -792,21 +822,26 @@ def main():
                        json.loads(args.pmc_commands), algorithmic(w)[1], args.trace_last or 20)
         return
     peaks = achievable_peaks()
+    # The oracle runs after a workload's GPU runs (the GPU is not left idle
+    # between its warmup and the timed calls), once per workload.
     if args.all:
-        # one line per configuration and batch_invariant mode; the oracle runs once per workload
+        # one line per configuration and batch_invariant mode
         for name in W.CONFIG_NAMES:
             w = W.make(name, device="cuda", variant=args.variant)
-            ref = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_seqs)
-            for bi in (0, 1):
-                print(json.dumps(bench_prefill(args, gdn, w, bi, peaks, ref)), flush=True)
-            if name == "varlen_bf16":   # inputs smaller than the last-level cache: also cold
-                print(json.dumps(bench_prefill(args, gdn, w, 0, peaks, ref, cold=True)), flush=True)
-            del w, ref
+            timed = [bench_prefill(args, gdn, w, bi, peaks) for bi in (0, 1)]
+            if name == "varlen_bf16":   # part of its inputs stays in the last-level cache: also cold
+                timed.append(bench_prefill(args, gdn, w, 0, peaks, cold=True))
+            recs = ([r for r, _, _ in timed] if args.no_cpu_baseline
+                    else with_oracle(args, timed, cpu_baseline(w, args.cpu_sample_seqs)))
+            for r in recs:
+                print(json.dumps(r), flush=True)
+            del w, timed
             torch.cuda.empty_cache()
         return
     w = W.make(args.workload, device="cuda", variant=args.variant)
-    ref = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_seqs)
-    res = bench_prefill(args, gdn, w, args.batch_invariant, peaks, ref, cold=args.cold_cache)
+    timed = [bench_prefill(args, gdn, w, args.batch_invariant, peaks, cold=args.cold_cache)]
+    res = (timed[0][0] if args.no_cpu_baseline
+           else with_oracle(args, timed, cpu_baseline(w, args.cpu_sample_seqs))[0])
     print(json.dumps(res), flush=True)
 
 
