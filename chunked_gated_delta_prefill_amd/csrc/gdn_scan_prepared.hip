@@ -104,8 +104,13 @@ struct LoaderSet {
     float gl, igl, G;   // gamma_L, 1 / gamma_L, G_L
 };
 
+// NP = 1 runs 256 threads, one wave per SIMD, for which the compiler would take up
+// to 512 registers per lane and then move values between the VGPRs and the
+// accumulation registers (~480 such moves per chunk on the recurrence chain).  The
+// declared bound of 512 threads (two waves per SIMD) holds it to 256 VGPRs, which it
+// fits without spills; the launch stays at 256 threads.
 template <int NP>
-__global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const ScanParams p) {
+__global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_kernel(const ScanParams p) {
     using L = PreparedSmem<NP>;
     using M = Mma<bf16>;
     using frag = M::frag;
@@ -156,10 +161,12 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
         }
         float sigma = 1.f;
         VWide vw;
-        auto issue_v = [&](int x) {
+        // (lane: the loop's opaque copy, so that the load offsets are recomputed per
+        // chunk instead of held in registers across the loop)
+        auto issue_v = [&](int x, int lane) {
             const ChunkRef ch = chunk_at(bos, eos, x);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) issue_v_wide_part(vw, p, ch, h, vb, threadIdx.x & 63, j);
+            for (int j = 0; j < 4; ++j) issue_v_wide_part(vw, p, ch, h, vb, lane, j);
         };
         // the state's bf16 operand fragments (natural order), kept for this wave's X
         // pass and written to LDS for its output wave
@@ -171,7 +178,7 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
                 *xfrag(L::SB_OFF, 8, ws0, k, lane) = sfr[k];
             }
         };
-        if (nchunks > 0) issue_v(0);
+        if (nchunks > 0) issue_v(0, threadIdx.x & 63);
         state_frags(threadIdx.x & 63);
         __syncthreads();   // chunk 0 staged by the loaders
 
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(128 * NP + 128) void prepared_scan_kernel(const Sca
                         vx[ib][q] =
                             __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src));
                     }
-                if (c + 1 < nchunks) issue_v(c + 1);   // the registers are free again
+                if (c + 1 < nchunks) issue_v(c + 1, lane);   // the registers are free again
             }
             frag zb[2][S32];
 #pragma unroll
