@@ -107,7 +107,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         gamma_l(x) = __expf(GL);
         igamma_l(x) = __expf(-GL);
     };
-    constexpr int kGateW = 4 + kGateWave;   // the preparation wave that forms the gate rows
+    // The preparation wave that loads the gates and forms the gate rows.  Its gate
+    // loads of chunk c + 3 go out in interval 5 after its K, Q loads of that chunk,
+    // where the wave's A(1,1) pass leaves time for them: queued behind the other
+    // waves' 16-byte loads for the memory unit's address processing, the two small
+    // loads hold the issuing wave ~500 cycles, and issued later (intervals 3, 4)
+    // they also became part of the wait before the K, Q staging of interval 4.
+    constexpr int kGateW = 4 + kGateWave;
 
     // State waves: S[b] holds S~^T rows k in natural operand order, column v0.
     // pf: the preparation waves' K, Q and gate prefetch; the state waves keep the
@@ -476,6 +482,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             else pass(std::integral_constant<int, 3>{});
         };
         if (nchunks > 0) gram(0, threadIdx.x & 63);
+        // gamma_L and the last log-gate cumsum of the chunk the next iteration
+        // prepares, read one interval early (with the LDS still free of the state
+        // waves' V staging that opens interval 1)
+        auto uniform_f = [](float v) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+        };
+        float gl_next = 1.f, glog_next = 0.f;
+        if (nchunks > 0) {
+            gl_next = uniform_f(gamma_l(0));
+            glog_next = uniform_f(rows(RG_, 0)[C - 1]);
+        }
         __syncthreads();
         for (int c = -1; c < nchunks; ++c) {
             int tid_o = threadIdx.x;
@@ -486,12 +503,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int x = c + 1;   // the chunk being prepared
             const bool on = x < nchunks, on2 = c + 2 < nchunks;
             auto rf = [&](int which) { return rows(which, x); };
-            const float gLc =
-                __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gamma_l(x))));
+            const float gLc = gl_next;
             const float sig_next = sigma * gLc;
             const bool renorm = !(sig_next >= kRenorm);
-            const bool fast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                                  int, rf(RG_)[C - 1]))) > kFastDecay;
+            const bool fast = glog_next > kFastDecay;
             bf16 *Ts = tbuf(x);
 
             // ---- interval 1: A (fp32) and P of chunk x from the Gram tiles, row
@@ -602,14 +617,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 float xs[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) xs[k] = rq + 4 * k == cc ? 1.f : 0.f;
-                f32x4 ncol[2];
-                ncol[0] = ld4(nt);
+                // all 15 columns in one batch: the chain then waits for the LDS once, not
+                // at each of its first steps (the state waves' output products keep the
+                // LDS busy during this interval)
+                f32x4 ncol[15];
+#pragma unroll
+                for (int m = 0; m < 15; ++m) ncol[m] = ld4(nt + m * 16);
 #pragma unroll
                 for (int m = 0; m < 15; ++m) {
-                    if (m + 1 < 15) ncol[(m + 1) & 1] = ld4(nt + (m + 1) * 16);
                     const float xm = quad_bcast(xs[m >> 2], m & 3);
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) xs[k] = fmaf(-ncol[m & 1][k], xm, xs[k]);
+                    for (int k = 0; k < 4; ++k) xs[k] = fmaf(-ncol[m][k], xm, xs[k]);
                 }
                 const float bcol = rf(FB_)[16 * pw + cc];
                 float *blk = Af + (16 * pw) * L::FLD + 16 * pw;
@@ -625,8 +643,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
             // ---- interval 3: 16 -> 32 merges (waves 4, 5): T'_{2x+1,2x} =
             // -D_{2x+1} A_{2x+1,2x} D_{2x}; the gate rows of chunk c + 2 (their row
-            // set was last read by the state work of chunk c) and the gate loads of
-            // chunk c + 3
+            // set was last read by the state work of chunk c)
             if (on && pw < 2) {
                 const int g = lane >> 4, nn = lane & 15;
                 const int lo = 32 * pw, hi = 32 * pw + 16;
@@ -643,17 +660,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     Ts[i * L::OLD + lo + nn] = (bf16)(-Tq[rr] * bcol);
                 }
             }
-            if (on2 && ws == kGateW) {
-                gate_rows(pf, chunk_at(bos, eos, c + 2).L, c + 2, lane);
-                if (c + 3 < nchunks) issue_gates(pf, p, chunk_at(bos, eos, c + 3), h, lane);
-            }
+            if (on2 && ws == kGateW) gate_rows(pf, chunk_at(bos, eos, c + 2).L, c + 2, lane);
             __syncthreads();
 
             // ---- interval 4: 32 -> 64 merge on the four waves, wave (r, cc) forming
             // block (r, cc) of T''_21 = -T'_22 A_21 T''_11 (T''_11 read as its
             // column-scaled copy with transposing loads); K and Q of chunk c + 2
             // staged (their buffers were last read by the state update of chunk c),
-            // half of the loads of chunk c + 3
+            // half of the K, Q loads of chunk c + 3
             if (on) {
                 const int rr2 = pw >> 1, cc = pw & 1;
                 const int g = lane >> 4, nn = lane & 15;
@@ -695,12 +709,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             __syncthreads();
 
-            // ---- interval 5: Gram tiles and norms of chunk c + 2; the other half of
-            // the loads of chunk c + 3
-            if (on2) gram(c + 2, lane);
+            // ---- interval 5: Gram tiles and norms of chunk c + 2 (its gamma_L and last
+            // log-gate cumsum for the next iteration); the other half of the K, Q loads
+            // and the gate loads of chunk c + 3
+            if (on2) {
+                gl_next = uniform_f(gamma_l(c + 2));
+                glog_next = uniform_f(rows(RG_, c + 2)[C - 1]);
+                gram(c + 2, lane);
+            }
             if (c + 3 < nchunks) {
                 issue_kq_part(pf, p, chunk_at(bos, eos, c + 3), hq, tp, 2);
                 issue_kq_part(pf, p, chunk_at(bos, eos, c + 3), hq, tp, 3);
+                if (ws == kGateW) issue_gates(pf, p, chunk_at(bos, eos, c + 3), h, lane);
             }
             __syncthreads();
             if (on) sigma = renorm ? 1.f : sig_next;
