@@ -21,15 +21,18 @@
 //   output waves (NP, the same rows):
 //     Y = S~ Q^T (the state's bf16 operand fragments, passed through LDS),
 //     O^T = FY [Y + ub^T P^T]  (or the entry-wise form), bf16 rows to `out`
-//   loader waves (2): every global load of the coming chunks (K, Q, T', P, the
-//     row factors and the decay scalars) and their LDS staging, two chunks in
-//     flight in registers, so the compute waves issue no such loads
+//   loader waves (2): every other global load of the coming chunks (K, Q, T', P,
+//     the row factors and the decay scalars) and their LDS staging, two chunks
+//     in flight in registers; the output waves load and stage V (one chunk in
+//     flight), so the recurrence waves issue no loads at all
 //
 // Per chunk, two barrier intervals:
 //
 //   interval  recurrence                 output              loaders
-//   1         X, Z', Vnew, ub (to LDS),  Y = S~ Q^T; P and   loads of chunk c + 2
-//             V loads of chunk c + 1     FY read ahead
+//   1         X, Z', Vnew, ub (to LDS)   Y = S~ Q^T; P and   loads of chunk c + 2
+//                                        FY read ahead; V
+//                                        of c + 1 into LDS,
+//                                        V loads of c + 2
 //   2         renorm fold, update, S~    output products,    chunk c + 1 into LDS
 //             fragments (to LDS)         staging, stores
 //
@@ -68,12 +71,14 @@ template <int NP> struct PreparedSmem {
     static constexpr int SB_OFF = P_OFF + 2 * OB;              // S~ fragments [block][8 steps]
     static constexpr int UB_OFF = SB_OFF + NP * 8 * FRAG_BYTES;   // ub fragments [block][4]
     static constexpr int NB_OFF = UB_OFF + NP * 4 * FRAG_BYTES;   // Vnew fragments (entry-wise path)
-    static constexpr int VO_OFF = NB_OFF + NP * 4 * FRAG_BYTES;   // staging block per block: V in (1), output out (2)
-    static constexpr int ROW_OFF = VO_OFF + NP * kStageBytes;     // FZ, FU, FY [2][64] each; scalars [2][4]
+    static constexpr int VO_OFF = NB_OFF + NP * 4 * FRAG_BYTES;   // output staging block per block
+    static constexpr int VB = C * 32 * 2;                         // V of one chunk and block: [64 tokens][32] bf16
+    static constexpr int V_OFF = VO_OFF + NP * kStageBytes;       // [2][NP] by chunk parity
+    static constexpr int ROW_OFF = V_OFF + 2 * NP * VB;           // FZ, FU, FY [2][64] each; scalars [2][4]
     static constexpr int BYTES = ROW_OFF + (6 * C + 8) * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(Q_OFF % 16 == 0 && T_OFF % 16 == 0 && P_OFF % 16 == 0 && SB_OFF % 16 == 0 &&
-                  VO_OFF % 16 == 0 && ROW_OFF % 16 == 0, "align");
+                  VO_OFF % 16 == 0 && V_OFF % 16 == 0 && ROW_OFF % 16 == 0, "align");
 };
 
 // Row and 16-byte piece of piece u of a prepared tile (rows 0..31: 4 pieces,
@@ -122,6 +127,8 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
     bf16 *Qs = reinterpret_cast<bf16 *>(smem + L::Q_OFF);
     bf16 *Ts = reinterpret_cast<bf16 *>(smem + L::T_OFF);
     auto pbuf = [&](int x) { return reinterpret_cast<bf16 *>(smem + L::P_OFF + (x & 1) * L::OB); };
+    // V of chunk x for the workgroup's block i, staged by the loader waves
+    auto vbuf = [&](int x, int i) { return reinterpret_cast<bf16 *>(smem + L::V_OFF + ((x & 1) * NP + i) * L::VB); };
     // operand fragment f of block i in one of the exchange areas (16 bytes per lane)
     auto xfrag = [&](int off, int nf, int i, int f, int lane) {
         return reinterpret_cast<bf16x8 *>(smem + off + ((i * nf + f) * 64 + lane) * 16);
@@ -160,14 +167,6 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
                 load_state<true>(S, p.s_in + srow * p.si_n + h * p.si_h, p.si_v, p.si_dt, v0, h32);
         }
         float sigma = 1.f;
-        VWide vw;
-        // (lane: the loop's opaque copy, so that the load offsets are recomputed per
-        // chunk instead of held in registers across the loop)
-        auto issue_v = [&](int x, int lane) {
-            const ChunkRef ch = chunk_at(bos, eos, x);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) issue_v_wide_part(vw, p, ch, h, vb, lane, j);
-        };
         // the state's bf16 operand fragments (natural order), kept for this wave's X
         // pass and written to LDS for its output wave
         frag sfr[4 * S32];
@@ -178,7 +177,6 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
                 *xfrag(L::SB_OFF, 8, ws0, k, lane) = sfr[k];
             }
         };
-        if (nchunks > 0) issue_v(0, threadIdx.x & 63);
         state_frags(threadIdx.x & 63);
         __syncthreads();   // chunk 0 staged by the loaders
 
@@ -193,13 +191,13 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
             const bool fast = uniform(scal(c)[2]) > kFastDecay;
             const bf16 *Ks = kbuf(c);
             const float *FZr = fzr(c), *FUr = fur(c);
-            bf16 *Vw = reinterpret_cast<bf16 *>(smem + L::VO_OFF + ws0 * kStageBytes);
+            const bf16 *Vb = vbuf(c, ws0);
 
             // ---- interval 1: X = K S~^T (the next step's K fragments read while the
             // current step runs), Z', Vnew, ub.  After the X pass everything Z', Vnew and ub
             // read from LDS is read at once (the T' fragments, the FZ and FU rows, and V,
-            // staged through this wave's 4 KB and read back as 4 consecutive tokens of one
-            // column), so its latency is paid once.
+            // staged by the loader waves and read as 4 consecutive tokens of one column), so
+            // its latency is paid once.
             f32x16 X[2] = {zero16(), zero16()};
             {
                 frag fk[2][2];
@@ -235,20 +233,16 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
                 }
             bf16x4 vx[2][4];
             {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<i32x4 *>(Vw + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = vw.x[j];
                 const int i = lane & 15, g16 = (lane >> 4) & 1;
                 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const bf16 *src = Vw + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
+                        const bf16 *src = Vb + (32 * ib + 8 * q + 4 * h32 + (i >> 2)) * 32 + 16 * g16 + 4 * (i & 3);
                         vx[ib][q] =
                             __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src));
                     }
-                if (c + 1 < nchunks) issue_v(c + 1, lane);   // the registers are free again
             }
             frag zb[2][S32];
 #pragma unroll
@@ -344,6 +338,26 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
         const int w = ws0 - NP;             // the block of rows (and the recurrence wave) this wave outputs
         const int vb = slice * NP + w;
         float sigma = 1.f;
+        // V of this block for the recurrence wave, one chunk in flight in registers and
+        // staged into LDS ([64 tokens][32] bf16) a chunk before it is used: the output
+        // wave waits through most of the first interval, the recurrence wave does not
+        VWide vw;
+        auto stage_v = [&](int x, int lane) {
+            bf16 *Vb = vbuf(x, w);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<i32x4 *>(Vb + (16 * j + (lane >> 2)) * 32 + 8 * (lane & 3)) = vw.x[j];
+        };
+        auto issue_v = [&](int x, int lane) {
+            const ChunkRef ch = chunk_at(bos, eos, x);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) issue_v_wide_part(vw, p, ch, h, vb, lane, j);
+        };
+        if (nchunks > 0) {
+            issue_v(0, threadIdx.x & 63);
+            stage_v(0, threadIdx.x & 63);
+            if (nchunks > 1) issue_v(1, threadIdx.x & 63);
+        }
         __syncthreads();   // chunk 0 staged by the loaders
 
         for (int c = 0; c < nchunks; ++c) {
@@ -388,6 +402,10 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
                     Y[1] = M::run(sf, fq[cur][1], Y[1]);
                 }
             }
+            // V of chunk c + 1 into its buffer (last read by the recurrence wave in the first
+            // interval of chunk c - 1), then the loads of chunk c + 2
+            if (c + 1 < nchunks) stage_v(c + 1, lane);
+            if (c + 2 < nchunks) issue_v(c + 2, lane);
             __syncthreads();
 
             // ---- interval 2: the output rows of chunk c (the recurrence wave's ub, or
