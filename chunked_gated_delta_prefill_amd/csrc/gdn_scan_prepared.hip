@@ -530,11 +530,12 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
         // (chunk c + 1, loaded an iteration earlier) is staged in interval 2.  The loop
         // runs two chunks per trip so that each set is a fixed group of registers.
         auto body = [&](LoaderSet &mine, LoaderSet &other, int c) {
-            // With two blocks per workgroup, chunk c + 1's loads (an iteration old) are
-            // waited for before chunk c + 2's are issued: the compiler cannot count the
-            // conditional row loads, so a wait after that issue (in interval 2) also
-            // waits for the new loads (4 x 8192 tokens: -3.4%; with one block: +2%)
-            if constexpr (NP != 1) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            // Chunk c + 1's loads (an iteration old) are waited for before chunk c + 2's
+            // are issued: the compiler cannot count the conditional row loads, so a wait
+            // after that issue (in interval 2) also waits for the new loads (4 x 8192
+            // tokens: -3.4%; one 65,536-token sequence, once the recurrence waves no
+            // longer load V and the loaders' staging bounds the second interval: -8%)
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             if (c + 2 < nchunks) issue(mine, c + 2);
             __syncthreads();
             if (c + 1 < nchunks) stage(other, c + 1);
