@@ -617,9 +617,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 float xs[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) xs[k] = rq + 4 * k == cc ? 1.f : 0.f;
-                // all 15 columns in one batch: the chain then waits for the LDS once, not
-                // at each of its first steps (the state waves' output products keep the
-                // LDS busy during this interval)
+                // all 15 columns in one batch, so that no step of the chain waits on the
+                // read of its column (one step ahead measured the same on its own)
                 f32x4 ncol[15];
 #pragma unroll
                 for (int m = 0; m < 15; ++m) ncol[m] = ld4(nt + m * 16);

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
     bf16 *Qs = reinterpret_cast<bf16 *>(smem + L::Q_OFF);
     bf16 *Ts = reinterpret_cast<bf16 *>(smem + L::T_OFF);
     auto pbuf = [&](int x) { return reinterpret_cast<bf16 *>(smem + L::P_OFF + (x & 1) * L::OB); };
-    // V of chunk x for the workgroup's block i, staged by the loader waves
+    // V of chunk x for the workgroup's block i, staged by that block's output wave
     auto vbuf = [&](int x, int i) { return reinterpret_cast<bf16 *>(smem + L::V_OFF + ((x & 1) * NP + i) * L::VB); };
     // operand fragment f of block i in one of the exchange areas (16 bytes per lane)
     auto xfrag = [&](int off, int nf, int i, int f, int lane) {
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
             // ---- interval 1: X = K S~^T (the next step's K fragments read while the
             // current step runs), Z', Vnew, ub.  After the X pass everything Z', Vnew and ub
             // read from LDS is read at once (the T' fragments, the FZ and FU rows, and V,
-            // staged by the loader waves and read as 4 consecutive tokens of one column), so
+            // staged by the output wave and read as 4 consecutive tokens of one column), so
             // its latency is paid once.
             f32x16 X[2] = {zero16(), zero16()};
             {
