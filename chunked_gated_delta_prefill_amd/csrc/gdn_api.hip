@@ -162,9 +162,19 @@ int check_device(std::string &msg, int *dev_out, int *cus_out) {
 // the stream is capturing (an allocation is not capturable): an eager call of
 // the largest shape on the stream sizes the workspace first.  Growth rounds up
 // by half again, so a run of slowly growing calls retires few buffers.
+//
+// The prepared plan of a long launch also keeps a side stream (non-blocking, so
+// it never waits on the legacy default stream by itself) and its events: the
+// preparation of later chunk ranges runs there while the caller's stream scans
+// the earlier ones (fork and join by events, so a captured graph holds both
+// branches).
+constexpr int kPhases = 4;                  // chunk ranges of a long prepared launch
+constexpr int64_t kPhaseMinChunks = 64;     // average chunks per sequence below which it runs as one range
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
+    hipStream_t side = nullptr;
+    hipEvent_t ev[kPhases] = {};            // ev[0]: range 0 prepared (fork); ev[i]: range i prepared
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
@@ -199,6 +209,43 @@ int get_workspace(int dev, hipStream_t st, size_t need, void **out, std::string 
         w.bytes = bytes;
     }
     *out = w.ptr;
+    return GDN_OK;
+}
+
+// The side stream and events of (dev, st), created on first use.  They are not
+// created while `st` is capturing (a graph then runs the launch as one range,
+// with bitwise the same results): *side stays nullptr.
+int get_side(int dev, hipStream_t st, hipStream_t *side, hipEvent_t **ev, std::string &msg) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace &w = g_ws[{dev, st}];
+    *side = nullptr;
+    if (!w.side) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+            (void)hipGetLastError();
+            msg = "hipStreamIsCapturing failed";
+            return GDN_ERR_HIP;
+        }
+        if (cs != hipStreamCaptureStatusNone) return GDN_OK;
+        hipStream_t s = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+            (void)hipGetLastError();
+            msg = "side stream creation failed";
+            return GDN_ERR_HIP;
+        }
+        for (int i = 0; i < kPhases; ++i) {
+            if (hipEventCreateWithFlags(&w.ev[i], hipEventDisableTiming) != hipSuccess) {
+                (void)hipGetLastError();
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(w.ev[j]);
+                (void)hipStreamDestroy(s);
+                msg = "event creation failed";
+                return GDN_ERR_HIP;
+            }
+        }
+        w.side = s;
+    }
+    *side = w.side;
+    *ev = w.ev;
     return GDN_OK;
 }
 
@@ -246,10 +293,16 @@ extern "C" void gdn_release_workspace(void) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     for (auto &kv : g_ws) {
-        if (kv.second.ptr) {
-            (void)hipSetDevice(kv.first.first);
+        Workspace &w = kv.second;
+        (void)hipSetDevice(kv.first.first);
+        if (w.side) {
+            (void)hipStreamSynchronize(w.side);
+            for (int i = 0; i < kPhases; ++i) (void)hipEventDestroy(w.ev[i]);
+            (void)hipStreamDestroy(w.side);
+        }
+        if (w.ptr) {
             (void)hipStreamSynchronize(kv.first.second);
-            (void)hipFree(kv.second.ptr);
+            (void)hipFree(w.ptr);
         }
     }
     for (auto &r : g_ws_retired) {   // their users were enqueued before the current buffers' users
@@ -538,14 +591,34 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     if (plan.kind == GDN_PLAN_PREPARED_SCAN) {
         // table of segments of kPrepChunks chunks (the split path's plan kernel), the
         // prepared chunks (one preparation work item per segment and head), then
-        // the scan over them
+        // the scan over them.  A long launch runs in kPhases ranges of chunks: the
+        // preparation of range 0 first, then the scan of each range on this stream
+        // while the side stream prepares the later ones (the scan takes only
+        // 2 or 4 CUs per work item, at most half the device).  The scan leaves S~
+        // and its scale between ranges as they are, so the results are bitwise
+        // those of one range.
         const int64_t lprep = (int64_t)gdn::kChunk * gdn::kPrepChunks;
         const int64_t cap = T / lprep + N + 1;
         const size_t seg_bytes = align_up((size_t)cap * sizeof(gdn::SegEntry), 256);
         const size_t first_bytes = align_up((size_t)(N + 2) * sizeof(int32_t), 256);
         const size_t prep_bytes = (size_t)cap * gdn::kPrepChunks * (size_t)Hv * gdn::kPrepSlot;
+        const int64_t avg_chunks = N > 0 ? ((T + N - 1) / N + gdn::kChunk - 1) / gdn::kChunk : 0;
+        int nph = avg_chunks >= kPhaseMinChunks ? kPhases : 1;
+        // range length: a whole number of preparation segments, so every segment
+        // falls in one range; the last range runs to the end of every sequence
+        const int64_t ph = ((avg_chunks + kPhases - 1) / kPhases + gdn::kPrepChunks - 1) / gdn::kPrepChunks *
+                           gdn::kPrepChunks;
+        const size_t resume_bytes = (size_t)N * Hv * 4 * gdn::kResumeFloats * sizeof(float);
+        hipStream_t side = nullptr;
+        hipEvent_t *ev = nullptr;
+        if (nph > 1) {
+            if ((rc = get_side(dev, hs, &side, &ev, msg))) return fail(rc, msg);
+            if (!side) nph = 1;
+        }
         void *wsp = nullptr;
-        if ((rc = get_workspace(dev, hs, seg_bytes + first_bytes + prep_bytes, &wsp, msg))) return fail(rc, msg);
+        if ((rc = get_workspace(dev, hs, seg_bytes + first_bytes + prep_bytes + (nph > 1 ? resume_bytes : 0), &wsp,
+                                msg)))
+            return fail(rc, msg);
         char *w = static_cast<char *>(wsp);
         gdn::SegEntry *segs = reinterpret_cast<gdn::SegEntry *>(w);
         int32_t *seg_first = reinterpret_cast<int32_t *>(w + seg_bytes);
@@ -560,10 +633,32 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
         ps.prep = pp.prep;
         ps.prep_cps = gdn::kPrepChunks;
         ps.seg_first = seg_first;
+        if (nph == 1) {
+            if ((e = gdn::launch_plan(p.cu, p.cu_i64, (int)N, lprep, segs, nsegs, seg_first, (int)cap, hs)) !=
+                    hipSuccess ||
+                (e = gdn::launch_prep(pp, hs)) != hipSuccess ||
+                (e = gdn::launch_prepared_scan(ps, plan.np, hs)) != hipSuccess)
+                return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+            return GDN_OK;
+        }
+        float *resume = reinterpret_cast<float *>(w + seg_bytes + first_bytes + prep_bytes);
+        auto range = [&](gdn::ScanParams q, int i) {
+            q.ph_c0 = (int32_t)(i * ph);
+            q.ph_len = i + 1 < nph ? (int32_t)ph : 0;
+            q.resume = resume;
+            return q;
+        };
         if ((e = gdn::launch_plan(p.cu, p.cu_i64, (int)N, lprep, segs, nsegs, seg_first, (int)cap, hs)) != hipSuccess ||
-            (e = gdn::launch_prep(pp, hs)) != hipSuccess ||
-            (e = gdn::launch_prepared_scan(ps, plan.np, hs)) != hipSuccess)
+            (e = gdn::launch_prep(range(pp, 0), hs)) != hipSuccess || (e = hipEventRecord(ev[0], hs)) != hipSuccess ||
+            (e = hipStreamWaitEvent(side, ev[0], 0)) != hipSuccess)
             return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        for (int i = 1; i < nph; ++i)
+            if ((e = gdn::launch_prep(range(pp, i), side)) != hipSuccess || (e = hipEventRecord(ev[i], side)) != hipSuccess)
+                return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        for (int i = 0; i < nph; ++i)
+            if ((i > 0 && (e = hipStreamWaitEvent(hs, ev[i], 0)) != hipSuccess) ||
+                (e = gdn::launch_prepared_scan(range(ps, i), plan.np, hs)) != hipSuccess)
+                return fail(GDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
         return GDN_OK;
     }
     if (lseg == 0) {

@@ -92,7 +92,16 @@ struct ScanParams {
     char *prep;
     const int32_t *seg_first;
     int32_t prep_cps;
+    // a range of chunks of every sequence (ph_len == 0: from ph_c0 to the end):
+    // kPrep prepares only the segments that start in it, the prepared scan runs
+    // only its chunks.  A range that does not end a sequence leaves the lazily
+    // scaled state S~ and its scale sigma in `resume` (kResumeFloats per
+    // (sequence, value head, 32-row block)), where the next range takes them up
+    // exactly.
+    int32_t ph_c0, ph_len;
+    float *resume;
 };
+constexpr int kResumeFloats = 64 * 64 + 64;   // S~ (64 accumulator registers x 64 lanes), then sigma
 
 // Fix-up of the split path: per (sequence, value head), serially over its
 // segments, S_in(i+1) = S_in(i) M_i + N_i.

@@ -129,6 +129,10 @@ fused_scan_kernel(const ScanParams p) {
         first = e.first != 0;
         last = e.last != 0;
         if ((MODE == kMapN || MODE == kMapM) && last) return;   // maps: all but the last segment
+        if constexpr (PREP) {   // a range of chunks: only the segments that start in it
+            const int sc0 = (int)((bos - load_cu(p.cu, n, p.cu_i64)) / C);
+            if (sc0 < p.ph_c0 || (p.ph_len > 0 && sc0 >= p.ph_c0 + p.ph_len)) return;
+        }
     } else {
         n = item;
         bos = load_cu(p.cu, n, p.cu_i64);

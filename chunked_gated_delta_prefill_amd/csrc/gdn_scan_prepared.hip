@@ -154,6 +154,21 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
     const int64_t srow = state_row(p.sidx, p.sidx_i64, p.pool_rows, n);
     const int nchunks = (int)((eos - bos + C - 1) / C);
     const int ws0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the chunks this launch runs: [c0, cend), all of them unless the host splits
+    // the scan into ranges so that the preparation of the next range overlaps it
+    const int c0 = p.ph_c0 & -kPrepChunks;   // a whole number of preparation segments (the host's ranges)
+    const int cend = p.ph_len > 0 && c0 + p.ph_len < nchunks ? c0 + p.ph_len : nchunks;
+    if (c0 > 0 && c0 >= nchunks) return;   // the sequence ended in an earlier range
+    const bool resumed = c0 > 0;
+    // S~ and sigma of 32-row block vb where the previous range left them: register
+    // group j (accumulator registers 4 j .. 4 j + 3) of lane l at 16 (64 j + l)
+    // bytes, sigma after the 64 groups
+    auto resume_rsrc = [&](int vb) {
+        return rsrc(p.resume + (((int64_t)n * p.Hv + h) * 4 + vb) * kResumeFloats, kResumeFloats * 4);
+    };
+    auto resume_sigma = [&](int vb) {
+        return uniform(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(resume_rsrc(vb), 64 * 64 * 4, 0, 0)));
+    };
 
     if (ws0 < NP) {
         // ================= recurrence waves =================
@@ -161,12 +176,22 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
         f32x16 S[4];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) S[bb] = zero16();
-        {
+        float sigma = 1.f;
+        if (resumed) {
+            const int lane = threadIdx.x & 63;
+            const auto rr = resume_rsrc(vb);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, 16 * (64 * j + lane), 0, 0));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[j >> 2][4 * (j & 3) + t] = x[t];
+            }
+            sigma = resume_sigma(vb);
+        } else {
             const int lane = threadIdx.x & 63, h32 = lane >> 5, v0 = 32 * vb + (lane & 31);
             if (p.s_in && srow >= 0)
                 load_state<true>(S, p.s_in + srow * p.si_n + h * p.si_h, p.si_v, p.si_dt, v0, h32);
         }
-        float sigma = 1.f;
         // the state's bf16 operand fragments (natural order), kept for this wave's X
         // pass and written to LDS for its output wave
         frag sfr[4 * S32];
@@ -178,9 +203,9 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
             }
         };
         state_frags(threadIdx.x & 63);
-        __syncthreads();   // chunk 0 staged by the loaders
+        __syncthreads();   // chunk c0 staged by the loaders
 
-        for (int c = 0; c < nchunks; ++c) {
+        for (int c = c0; c < cend; ++c) {
             int tid_o = threadIdx.x;
             asm volatile("" : "+v"(tid_o));
             const int lane = tid_o & 63;
@@ -318,12 +343,21 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
                 }
             }
             sigma = renorm ? 1.f : sig_next;
-            if (c + 1 < nchunks) state_frags(lane);
+            if (c + 1 < cend) state_frags(lane);
             __syncthreads();
         }
 
-        // ---- final state (each slice writes its own rows)
-        if (p.s_out && srow >= 0) {
+        if (cend < nchunks) {   // S~ and sigma as they are, for the next range
+            const int lane = threadIdx.x & 63;
+            const auto rr = resume_rsrc(vb);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const f32x4 x = {S[j >> 2][4 * (j & 3)], S[j >> 2][4 * (j & 3) + 1], S[j >> 2][4 * (j & 3) + 2],
+                                 S[j >> 2][4 * (j & 3) + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), rr, 16 * (64 * j + lane), 0, 0);
+            }
+            if (lane == 0) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, sigma), rr, 64 * 64 * 4, 0, 0);
+        } else if (p.s_out && srow >= 0) {   // ---- final state (each slice writes its own rows)
             if (sigma != 1.f) {
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb)
@@ -337,7 +371,7 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
         // ================= output waves =================
         const int w = ws0 - NP;             // the block of rows (and the recurrence wave) this wave outputs
         const int vb = slice * NP + w;
-        float sigma = 1.f;
+        float sigma = resumed ? resume_sigma(vb) : 1.f;
         // V of this block for the recurrence wave, one chunk in flight in registers and
         // staged into LDS ([64 tokens][32] bf16) a chunk before it is used: the output
         // wave waits through most of the first interval, the recurrence wave does not
@@ -353,14 +387,14 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
 #pragma unroll
             for (int j = 0; j < 4; ++j) issue_v_wide_part(vw, p, ch, h, vb, lane, j);
         };
-        if (nchunks > 0) {
-            issue_v(0, threadIdx.x & 63);
-            stage_v(0, threadIdx.x & 63);
-            if (nchunks > 1) issue_v(1, threadIdx.x & 63);
+        if (cend > c0) {
+            issue_v(c0, threadIdx.x & 63);
+            stage_v(c0, threadIdx.x & 63);
+            if (c0 + 1 < cend) issue_v(c0 + 1, threadIdx.x & 63);
         }
-        __syncthreads();   // chunk 0 staged by the loaders
+        __syncthreads();   // chunk c0 staged by the loaders
 
-        for (int c = 0; c < nchunks; ++c) {
+        for (int c = c0; c < cend; ++c) {
             int tid_o = threadIdx.x;
             asm volatile("" : "+v"(tid_o));
             const int lane = tid_o & 63;
@@ -404,8 +438,8 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
             }
             // V of chunk c + 1 into its buffer (last read by the recurrence wave in the first
             // interval of chunk c - 1), then the loads of chunk c + 2
-            if (c + 1 < nchunks) stage_v(c + 1, lane);
-            if (c + 2 < nchunks) issue_v(c + 2, lane);
+            if (c + 1 < cend) stage_v(c + 1, lane);
+            if (c + 2 < cend) issue_v(c + 2, lane);
             __syncthreads();
 
             // ---- interval 2: the output rows of chunk c (the recurrence wave's ub, or
@@ -461,7 +495,7 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
         const int64_t slot_stride = (int64_t)p.Hv * kPrepSlot;
         const char *slot0 =
             p.prep + ((int64_t)(nchunks > 0 ? p.seg_first[n] : 0) * p.prep_cps * p.Hv + h) * kPrepSlot;
-        float sigma = 1.f;   // the lazy scale at the start of the chunk being staged
+        float sigma = resumed ? resume_sigma(slice * NP) : 1.f;   // the lazy scale at the start of the chunk being staged
         LoaderSet set0, set1;
         auto issue = [&](LoaderSet &d, int x) {
             const ChunkRef ch = chunk_at(bos, eos, x);
@@ -520,10 +554,10 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
             }
             sigma = renorm ? 1.f : sig_next;
         };
-        if (nchunks > 0) {
-            issue(set0, 0);
-            if (nchunks > 1) issue(set1, 1);
-            stage(set0, 0);
+        if (cend > c0) {
+            issue(set0, c0);
+            if (c0 + 1 < cend) issue(set1, c0 + 1);
+            stage(set0, c0);
         }
         __syncthreads();
         // Chunk c's set holds chunk c + 2 after interval 1 of chunk c; the other set
@@ -536,14 +570,14 @@ __global__ __launch_bounds__(NP == 1 ? 512 : 128 * NP + 128) void prepared_scan_
             // tokens: -3.4%; one 65,536-token sequence, once the recurrence waves no
             // longer load V and the loaders' staging bounds the second interval: -8%)
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            if (c + 2 < nchunks) issue(mine, c + 2);
+            if (c + 2 < cend) issue(mine, c + 2);
             __syncthreads();
-            if (c + 1 < nchunks) stage(other, c + 1);
+            if (c + 1 < cend) stage(other, c + 1);
             __syncthreads();
         };
-        for (int c = 0; c < nchunks; c += 2) {
+        for (int c = c0; c < cend; c += 2) {
             body(set0, set1, c);
-            if (c + 1 < nchunks) body(set1, set0, c + 1);
+            if (c + 1 < cend) body(set1, set0, c + 1);
         }
     }
 }

@@ -110,7 +110,12 @@ typedef struct gdn_tensor {
  *                   out with q, k, v, g or beta is an unchecked precondition.
  *   stream          a hipStream_t (NULL = the default stream).  The call is
  *                   asynchronous: it validates on the host, enqueues on
- *                   `stream` and returns without synchronising.
+ *                   `stream` and returns without synchronising.  A long
+ *                   GDN_PLAN_PREPARED_SCAN call also enqueues part of its
+ *                   work on a side stream the library keeps for `stream`,
+ *                   forked from `stream` and joined back into it by events:
+ *                   to the caller the call is ordered on `stream` as any
+ *                   other.
  *
  * Ownership: every tensor is caller-owned device memory; the library writes
  * only `out`, `output_state` and its own workspace (cached per device and
@@ -122,7 +127,10 @@ typedef struct gdn_tensor {
  * GDN_ERR_UNSUPPORTED.  A captured graph keeps the capture stream's workspace
  * address: its replays share that memory with eager split calls on the
  * capture stream, so the two must not run at the same time, and growing the
- * workspace later keeps the old buffer alive for the graph.
+ * workspace later keeps the old buffer alive for the graph.  The side stream
+ * of a prepared call is created by the first eager call on `stream`; a
+ * captured prepared call without one runs on `stream` alone, with bitwise the
+ * same results.
  * Errors: validation happens before any enqueue; an invalid call writes
  * nothing and returns a gdn_status (no fallback path exists).
  */
@@ -271,8 +279,11 @@ int gdn_decode_step_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_t
  *                            in one parallel pass ("T precompute"), then the
  *                            scan that consumes it with each head's state rows
  *                            spread over two or four CUs (bf16, no checkpoints,
- *                            at most half as many work items as CUs); bitwise
- *                            the results of GDN_PLAN_SCAN.
+ *                            at most half as many work items as CUs); with 64
+ *                            or more chunks per sequence on average, in four
+ *                            ranges of chunks, the later ranges prepared on a
+ *                            side stream while the earlier ones are scanned;
+ *                            bitwise the results of GDN_PLAN_SCAN.
  *                            gdn_chunk_prefill_noalloc runs
  *                            GDN_PLAN_PIPELINED_SCAN instead (no workspace).
  */
@@ -300,9 +311,10 @@ const char *gdn_last_error(void);
 /* Frees every cached workspace, current and superseded, on all devices and
  * streams (the workspace the dispatcher caches with the shape-specific plan,
  * "flashinfer.gdn_prefill", Cake GDN CP context-parallel backend; nothing is
- * kept for the process lifetime unless the caller keeps calling).  The caller
- * must ensure that no enqueued gdn work is still running and that no graph
- * captured from a split-path call is replayed afterwards. */
+ * kept for the process lifetime unless the caller keeps calling), and the side
+ * streams and events of prepared calls.  The caller must ensure that no
+ * enqueued gdn work is still running and that no graph captured from a split
+ * or prepared call is replayed afterwards. */
 void gdn_release_workspace(void);
 
 #ifdef __cplusplus

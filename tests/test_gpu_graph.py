@@ -32,17 +32,22 @@ def _replays_match(call, outs, label, replays=3):
     say(f"[gpu] graph {label}: {replays} replays bitwise equal")
 
 
-@pytest.mark.parametrize("split", [False, True])
-def test_prefill_graph_replay(gdn, split):
-    if split:   # one long sequence on few heads: plan, maps, fix-up and scan kernels
+@pytest.mark.parametrize("case", ["scan", "split", "prepared"])
+def test_prefill_graph_replay(gdn, case):
+    if case == "split":      # one long sequence on few heads: plan, maps, fix-up and scan kernels
         w = W.build([8200, 100], 1, 4, torch.bfloat16, seed=51, gate="long").to(DEV)
+    elif case == "prepared":  # batch_invariant, few work items: the prepared plan in chunk ranges, the
+        # later ranges prepared on the side stream (fork and join captured)
+        w = W.build([16384, 5000], 2, 4, torch.bfloat16, seed=58).to(DEV)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        assert gdn.prefill_plan(w.N, w.T, w.Hv, w.q.dtype, False, True, cus)[0] == "prepared_scan"
     else:
         w = W.build([300, 64, 1, 129], 2, 4, torch.bfloat16, seed=52).to(DEV)
     out = torch.empty(w.T, w.Hv, 128, dtype=w.q.dtype, device=DEV)
     fin = torch.empty(w.N, w.Hv, 128, 128, dtype=torch.float32, device=DEV)
     call = lambda: gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, 0.0, w.cu_seqlens, w.initial_state, fin,
-                                         True, not split, out)
-    _replays_match(call, [out, fin], "prefill split" if split else "prefill")
+                                         True, case != "split", out)
+    _replays_match(call, [out, fin], "prefill " + case)
 
 
 def test_decode_graph_replay(gdn):
