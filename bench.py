@@ -332,6 +332,11 @@ def summarize_pmc(base, cmd_fetch, cmd_write, cmd_cf, cmd_cw, launch_alg_bytes, 
 
 # Kernels one gdn_chunk_prefill call launches, in launch order, per host plan
 # (gdn_prefill_plan); the fused scan kernel runs in several modes.
+# The kernels of one call of each plan, in launch order.  A call opens with the
+# first of them; a kernel named more than once is told apart by its occurrence
+# in the call.  The prepared plan of a long launch runs the preparation and the
+# scan once per chunk range (the later ranges' preparation on a side stream,
+# beside the scan), so each of its labels may cover several dispatches.
 PLAN_SEQUENCE = {
     "scan": ["fused_scan_kernel"],
     "pipelined_scan": ["piped_scan_kernel"],
@@ -359,20 +364,40 @@ def _gdn_base(name):
 
 
 def _group_calls(names, seq):
-    """Splits the launch-ordered gdn kernel names of a run into calls of the
-    plan's kernel sequence; returns the call index of every dispatch."""
+    """Splits the gdn kernel names of a run (in start or dispatch order) into
+    calls of the plan's kernels and labels them: returns (call index, label
+    index) of every dispatch.  Every call must hold every label, each the same
+    number of times as in the first call."""
     bases = [s.split(" (")[0] for s in seq]
-    if len(names) % len(seq):
-        raise ValueError(f"{len(names)} gdn dispatches are not whole calls of {seq}")
+    res, call, occ, counts = [], -1, {}, []
     for i, n in enumerate(names):
-        if _gdn_base(n) != bases[i % len(seq)]:
-            raise ValueError(f"dispatch {i} is {n}, expected {bases[i % len(seq)]}")
-    return [i // len(seq) for i in range(len(names))]
+        b = _gdn_base(n)
+        cands = [j for j, x in enumerate(bases) if x == b]
+        if not cands:
+            raise ValueError(f"dispatch {i} is {n}, not a kernel of {seq}")
+        if b == bases[0] and (call < 0 or occ.get(b, 0) >= bases.count(b)):
+            call, occ = call + 1, {}
+            counts.append([0] * len(seq))
+        if call < 0:
+            raise ValueError(f"dispatch {i} is {n}, before the first {bases[0]}")
+        k = occ.get(b, 0)
+        lab = cands[0] if len(cands) == 1 else (cands[k] if k < len(cands) else None)
+        if lab is None:
+            raise ValueError(f"dispatch {i}: {n} once too often in a call of {seq}")
+        occ[b] = k + 1
+        counts[call][lab] += 1
+        res.append((call, lab))
+    for c, cnt in enumerate(counts):
+        if 0 in cnt or cnt != counts[0]:
+            raise ValueError(f"call {c} launches {cnt} of {seq}, the first call {counts[0]}")
+    return res
 
 
 def _trace_calls(d, seq):
-    """Per-position durations (us) of the gdn dispatches in the trace under d,
-    grouped into calls: list over positions of lists over calls."""
+    """Durations (us) of the gdn dispatches in the trace under d, grouped into
+    calls: (per label: its dispatches' summed duration per call, per label:
+    dispatches per call, per call: span from the first start to the last
+    end, which counts overlapping kernels once)."""
     import sqlite3
     rows = []
     for f in _db_files(d):
@@ -383,11 +408,17 @@ def _trace_calls(d, seq):
         rows += [(r[si], r[ei], r[ni]) for r in cur.fetchall() if _gdn_base(r[ni])]
         con.close()
     rows.sort()
-    _group_calls([r[2] for r in rows], seq)
-    per = [[] for _ in seq]
-    for i, (s0, e0, _) in enumerate(rows):
-        per[i % len(seq)].append((e0 - s0) / 1e3)
-    return per
+    lab = _group_calls([r[2] for r in rows], seq)
+    ncalls = lab[-1][0] + 1 if lab else 0
+    per = [[0.0] * ncalls for _ in seq]
+    cnt = [0] * len(seq)
+    lo, hi = [None] * ncalls, [None] * ncalls
+    for (s0, e0, _), (c, j) in zip(rows, lab):
+        per[j][c] += (e0 - s0) / 1e3
+        cnt[j] += c == 0
+        lo[c] = s0 if lo[c] is None else min(lo[c], s0)
+        hi[c] = e0 if hi[c] is None else max(hi[c], e0)
+    return per, cnt, [(b - a) / 1e3 for a, b in zip(lo, hi)]
 
 
 def _pmc_calls(d, seq):
@@ -403,11 +434,12 @@ def _pmc_calls(d, seq):
                 e[1][cname] = e[1].get(cname, 0.0) + float(v)
         con.close()
     order = sorted(disp)
-    _group_calls([disp[k][0] for k in order], seq)
+    lab = _group_calls([disp[k][0] for k in order], seq)
+    ncalls = lab[-1][0] + 1 if lab else 0
     out = {}
-    for i, k in enumerate(order):
+    for k, (c, j) in zip(order, lab):
         for cname, v in disp[k][1].items():
-            out.setdefault(cname, [[] for _ in seq])[i % len(seq)].append(v)
+            out.setdefault(cname, [[0.0] * ncalls for _ in seq])[j][c] += v
     return out
 
 
@@ -419,7 +451,7 @@ def summarize_plan(base, out_path, w, bi, plan, commands, alg_bytes, timed_calls
     copy_fetch, copy_write."""
     seq = PLAN_SEQUENCE[plan]
     med = statistics.median
-    tr = _trace_calls(os.path.join(base, "trace"), seq)
+    tr, ndisp, spans = _trace_calls(os.path.join(base, "trace"), seq)
     fe = _pmc_calls(os.path.join(base, "fetch"), seq)["FETCH_SIZE"]
     wr = _pmc_calls(os.path.join(base, "write"), seq)["WRITE_SIZE"]
     sq = {**_pmc_calls(os.path.join(base, "sq1"), seq), **_pmc_calls(os.path.join(base, "sq2"), seq)}
@@ -431,9 +463,11 @@ def summarize_plan(base, out_path, w, bi, plan, commands, alg_bytes, timed_calls
     lines = [f"# Kernels of one gdn_chunk_prefill call: {plan} plan, workload {w.name} ({w.N} sequences, {w.T} "
              f"tokens, Hqk {w.Hqk}, Hv {w.Hv}, {str(w.q.dtype).replace('torch.', '')}), batch_invariant {bi}",
              "# durations: rocprofv3 --kernel-trace, the last timed calls (warmup excluded);",
-             "# traffic: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch, median over calls), each",
+             "#   a kernel's figures sum its dispatches in the call; call_average_us spans the call from its first",
+             "#   kernel's start to its last kernel's end (overlapping kernels counted once);",
+             "# traffic: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB, median over calls), each",
              "#   scaled by the same counter read for a plain 1 GiB device-to-device copy;",
-             "# SQ counters: median per dispatch, summed over the device.  Derived: per_wave = INSTS / SQ_WAVES;",
+             "# SQ counters: median per call, summed over the device.  Derived: per_wave = INSTS / SQ_WAVES;",
              "#   mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (SQ_BUSY_CYCLES / 32 shader engines);",
              "#   lds_conflict_ratio = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS"]
     lines += [f"# {k} command: {c}" for k, c in commands.items()]
@@ -446,7 +480,7 @@ def summarize_plan(base, out_path, w, bi, plan, commands, alg_bytes, timed_calls
         wb = med(wr[i]) * 1024.0 * w_fac
         tot_us += statistics.fmean(durs)
         tot_bytes += fb + wb
-        lines += ["", f"[{name}]", f"timed_dispatches = {len(durs)}",
+        lines += ["", f"[{name}]", f"timed_calls = {len(durs)}", f"dispatches_per_call = {ndisp[i]}",
                   f"average_us = {statistics.fmean(durs):.3f}", f"median_us = {med(durs):.3f}",
                   f"fetch_bytes = {fb:.0f}", f"write_bytes = {wb:.0f}",
                   f"hbm_gbs = {(fb + wb) / (statistics.fmean(durs) * 1e3):.1f}"]
@@ -461,9 +495,11 @@ def summarize_plan(base, out_path, w, bi, plan, commands, alg_bytes, timed_calls
             lines.append(f"mfma_busy = {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (vals['SQ_BUSY_CYCLES'] / 32):.3f}")
         if vals.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in vals:
             lines.append(f"lds_conflict_ratio = {vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_ACTIVE_INST_LDS']:.3f}")
-    lines[9:9] = [f"call_average_us = {tot_us:.3f}", f"hbm_bytes_per_call = {tot_bytes:.0f}",
-                  f"algorithmic_bytes_per_call = {alg_bytes:.0f}",
-                  f"traffic_over_algorithmic = {tot_bytes / alg_bytes:.3f}"]
+    call_us = statistics.fmean(spans[-timed_calls:])
+    at = next(i for i, x in enumerate(lines) if x.startswith("kernel_source_sha"))
+    lines[at:at] = [f"call_average_us = {call_us:.3f}", f"kernel_time_us = {tot_us:.3f}",
+                    f"hbm_bytes_per_call = {tot_bytes:.0f}", f"algorithmic_bytes_per_call = {alg_bytes:.0f}",
+                    f"traffic_over_algorithmic = {tot_bytes / alg_bytes:.3f}"]
     os.makedirs(os.path.dirname(out_path) or ".", exist_ok=True)
     open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))

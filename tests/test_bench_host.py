@@ -128,12 +128,62 @@ def test_plan_summary_groups_dispatches_into_calls(tmp_path):
         assert float(kv[(name, "write_bytes")]) == 2.0 * 1024 * 1.0
         assert float(kv[(name, "valu_per_wave")]) == 100.0
         assert float(kv[(name, "lds_conflict_ratio")]) == 0.25
-    assert abs(float(kv[("head", "call_average_us")]) - (15 + 5 * 0.0015)) < 1e-3
+    # the call spans 4 gaps of 10 us and the last kernel (5 us + call index ns); the kernels alone sum to 15 us
+    assert abs(float(kv[("head", "call_average_us")]) - (45 + 0.0015)) < 1e-3
+    assert abs(float(kv[("head", "kernel_time_us")]) - (15 + 5 * 0.0015)) < 1e-3
     assert float(kv[("head", "hbm_bytes_per_call")]) == 5 * 3 * 2048.0
     # a run whose dispatches do not follow the plan's sequence is refused
     import pytest
     with pytest.raises(ValueError):
         bench.summarize_plan(str(base), str(out), w, 0, "prepared_scan", {}, 1000.0, 2)
+
+
+def _kv(path):
+    kv, block = {}, "head"
+    for line in open(path).read().splitlines():
+        if line.startswith("["):
+            block = line.strip("[]")
+        elif "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[(block, a.strip())] = b.strip()
+    return kv
+
+
+def test_plan_summary_of_overlapping_ranges(tmp_path):
+    """A prepared call in four chunk ranges: the preparation of ranges 1-3
+    overlaps the scan of range 0 (started in either order), so a kernel's
+    figures sum its dispatches and the call time is the span of the call."""
+    plan_k, prep_k, scan_k = ("gdn::plan_kernel", "_ZN3gdn12_GLOBAL__N_117fused_scan_kernelILi3E",
+                              "_ZN3gdn12_GLOBAL__N_120prepared_scan_kernelILi1EEEv")
+    # (name, start us, duration us) within a call; prep 1 starts before scan 0
+    call = [(plan_k, 0, 1), (prep_k, 2, 10), (prep_k, 12.5, 10), (scan_k, 13, 20), (prep_k, 23, 10),
+            (prep_k, 33.5, 10), (scan_k, 34, 20), (scan_k, 55, 20), (scan_k, 76, 20)]
+    enq = [0, 1, 2, 4, 5, 3, 6, 7, 8]   # dispatch (enqueue) order: the side stream's preparations first
+    base = tmp_path / "case"
+    trace, disp = [], []
+    for c in range(3):
+        t0 = 1000.0 * c
+        trace += [(n, int((t0 + s0) * 1000), int((t0 + s0 + d) * 1000)) for n, s0, d in call]
+        disp += [(9 * c + i, call[j][0]) for i, j in enumerate(enq)]
+    _fake_rocpd(str(base / "trace" / "a.db"), trace=trace)
+    for sub, cnt in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        _fake_rocpd(str(base / sub / "a.db"), counters=[(d, n, cnt, 1.0) for d, n in disp])
+    for sub in ("sq1", "sq2"):
+        _fake_rocpd(str(base / sub / "a.db"), counters=[(d, n, "SQ_WAVES", 4.0) for d, n in disp])
+    _fake_rocpd(str(tmp_path / "copy_fetch" / "a.db"), counters=[(1, "copyBuffer", "FETCH_SIZE", 1048576.0)])
+    _fake_rocpd(str(tmp_path / "copy_write" / "a.db"), counters=[(1, "copyBuffer", "WRITE_SIZE", 1048576.0)])
+    w = SimpleNamespace(name="long_single", N=1, T=65536, Hqk=16, Hv=32, q=torch.empty(0, dtype=torch.bfloat16))
+    out = tmp_path / "summary.txt"
+    bench.summarize_plan(str(base), str(out), w, 1, "prepared_scan", {}, 1000.0, 2)
+    kv = _kv(out)
+    seq = bench.PLAN_SEQUENCE["prepared_scan"]
+    for name, n, us in zip(seq, (1, 4, 4), (1.0, 40.0, 80.0)):
+        assert int(kv[(name, "dispatches_per_call")]) == n
+        assert abs(float(kv[(name, "average_us")]) - us) < 1e-6
+        assert float(kv[(name, "fetch_bytes")]) == n * 1024.0
+    assert abs(float(kv[("head", "call_average_us")]) - 96.0) < 1e-6
+    assert abs(float(kv[("head", "kernel_time_us")]) - 121.0) < 1e-6
+    assert float(kv[("head", "hbm_bytes_per_call")]) == 2 * 9 * 1024.0
 
 
 def test_table_from_bench_lines(tmp_path):
