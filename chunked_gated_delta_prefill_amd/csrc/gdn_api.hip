@@ -591,19 +591,21 @@ int prefill_impl(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, 
     if (plan.kind == GDN_PLAN_PREPARED_SCAN) {
         // table of segments of kPrepChunks chunks (the split path's plan kernel), the
         // prepared chunks (one preparation work item per segment and head), then
-        // the scan over them.  A long launch runs in kPhases ranges of chunks: the
-        // preparation of range 0 first, then the scan of each range on this stream
-        // while the side stream prepares the later ones (the scan takes only
-        // 2 or 4 CUs per work item, at most half the device).  The scan leaves S~
-        // and its scale between ranges as they are, so the results are bitwise
-        // those of one range.
+        // the scan over them.  A long launch whose scan leaves at least half the
+        // CUs free runs in kPhases ranges of chunks: the preparation of range 0
+        // first, then the scan of each range on this stream while the side stream
+        // prepares the later ones on the free CUs.  The scan leaves S~ and its
+        // scale between ranges as they are, so the results are bitwise those of
+        // one range.  (Measured: one 65,536-token sequence on 32 heads, 128 scan
+        // workgroups, -7%; 2 x 32,768 tokens, 256 scan workgroups, +6%.)
         const int64_t lprep = (int64_t)gdn::kChunk * gdn::kPrepChunks;
         const int64_t cap = T / lprep + N + 1;
         const size_t seg_bytes = align_up((size_t)cap * sizeof(gdn::SegEntry), 256);
         const size_t first_bytes = align_up((size_t)(N + 2) * sizeof(int32_t), 256);
         const size_t prep_bytes = (size_t)cap * gdn::kPrepChunks * (size_t)Hv * gdn::kPrepSlot;
         const int64_t avg_chunks = N > 0 ? ((T + N - 1) / N + gdn::kChunk - 1) / gdn::kChunk : 0;
-        int nph = avg_chunks >= kPhaseMinChunks ? kPhases : 1;
+        const int64_t scan_wgs = N * Hv * (4 / plan.np);
+        int nph = avg_chunks >= kPhaseMinChunks && 2 * scan_wgs <= cus ? kPhases : 1;
         // range length: a whole number of preparation segments, so every segment
         // falls in one range; the last range runs to the end of every sequence
         const int64_t ph = ((avg_chunks + kPhases - 1) / kPhases + gdn::kPrepChunks - 1) / gdn::kPrepChunks *

@@ -279,8 +279,9 @@ int gdn_decode_step_pooled(const gdn_tensor *q, const gdn_tensor *k, const gdn_t
  *                            in one parallel pass ("T precompute"), then the
  *                            scan that consumes it with each head's state rows
  *                            spread over two or four CUs (bf16, no checkpoints,
- *                            at most half as many work items as CUs); with 64
- *                            or more chunks per sequence on average, in four
+ *                            at most half as many work items as CUs); when
+ *                            the scan takes at most half the CUs and the
+ *                            sequences average 64 or more chunks, in four
  *                            ranges of chunks, the later ranges prepared on a
  *                            side stream while the earlier ones are scanned;
  *                            bitwise the results of GDN_PLAN_SCAN.

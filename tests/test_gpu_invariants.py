@@ -318,17 +318,18 @@ def test_split_path_bf16_states(gdn):
 def test_prepared_plan_equals_pipelined_scan(gdn, case):
     """The prepared plan (every chunk's preparation in parallel, then the scan
     over it with each head's state rows spread over 4 CUs for the 65,536-token
-    sequence, over 2 CUs for 4 x 8192 tokens or three uneven sequences on 32
-    heads; these launches run in four chunk ranges, the later ranges prepared
-    beside the scan of the earlier ones, and the uneven sequences end in
-    different ranges) and the pipelined scan (the no-allocation entry point's
-    plan for the same launch) give bitwise the same output and final state."""
+    sequence on 32 heads and four uneven sequences on 8 heads, over 2 CUs for
+    4 x 8192 tokens on 32 heads; the first two leave half the CUs free and run
+    in four chunk ranges, the later ranges prepared beside the scan of the
+    earlier ones, and the uneven sequences end in different ranges) and the
+    pipelined scan (the no-allocation entry point's plan for the same launch)
+    give bitwise the same output and final state."""
     if case == "long_single":
         w = W.make(2, device="cuda")
     elif case == "four_8192":
         w = W.build([8192] * 4, 16, 32, torch.bfloat16, seed=64, device="cuda", name="four_8192")
     else:
-        w = W.build([20000, 3000, 2373], 16, 32, torch.bfloat16, seed=65, device="cuda", name="uneven")
+        w = W.build([20000, 3000, 2373, 9000], 4, 8, torch.bfloat16, seed=65, device="cuda", name="uneven")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert gdn.prefill_plan(w.N, w.T, w.Hv, w.q.dtype, False, True, cus)[0] == "prepared_scan"
     res = []
