@@ -119,7 +119,11 @@ typedef struct gdn_tensor {
  *
  * Ownership: every tensor is caller-owned device memory; the library writes
  * only `out`, `output_state` and its own workspace (cached per device and
- * stream, grown on demand; see gdn_release_workspace).
+ * stream, grown on demand; see gdn_release_workspace).  Calls on different
+ * streams may be made from different threads at once; calls on one stream
+ * must come from one thread at a time (they share that stream's workspace,
+ * side stream and events, and each call's kernels must stay together in the
+ * stream's order).
  * Graph capture: a call whose plan (gdn_prefill_plan) is GDN_PLAN_SPLIT or
  * GDN_PLAN_PREPARED_SCAN uses the workspace of its stream; after one eager call of the largest shape on
  * that stream, calls enqueue kernels only and can be captured.  A call that
