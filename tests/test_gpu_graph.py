@@ -152,3 +152,22 @@ def test_growth_during_capture_is_refused(gdn):
     assert code == 2, code
     assert torch.equal(out, torch.ones_like(out)) and torch.equal(fin, torch.zeros_like(fin))
     say("[gpu] workspace growth during capture: refused")
+
+
+def test_release_and_reuse(gdn):
+    """gdn_release_workspace frees the cached workspaces and destroys the side
+    streams and events of prepared calls in chunk ranges; the next calls on the
+    same stream create them again and give bitwise the same results."""
+    cases = [(W.build([8200, 100], 1, 4, torch.bfloat16, seed=59, gate="long").to(DEV), False, "split"),
+             (W.build([16384, 5000], 2, 4, torch.bfloat16, seed=60).to(DEV), True, "prepared")]
+    for w, bi, label in cases:
+        res = []
+        for _ in range(2):
+            out = torch.full((w.T, w.Hv, 128), float("nan"), dtype=w.q.dtype, device=DEV)
+            fin = torch.full((w.N, w.Hv, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+            gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, 0.0, w.cu_seqlens, w.initial_state, fin, True, bi, out)
+            torch.cuda.synchronize()
+            res.append((out, fin))
+            gdn.release_workspace()
+        assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), label
+        say(f"[gpu] release and reuse, {label}: bitwise equal")
